@@ -1,0 +1,130 @@
+"""Draw the seeded arrays of one cycle.
+
+Every tensor is drawn from its own numpy ``default_rng([seed, tensor_id, slab])``
+stream, where ``slab`` is the request index for per-request tensors and 0 for
+shared ones, so that any request's rows can be regenerated on their own.
+
+Tensor ids: 1 Z, 2 target noise, 3 E, 4 Wt, 5 h, 6 w_c, 7 tau, 8 anchor,
+10 the extra base-logit row behind the bonus position (row K+1 of the target).
+
+bf16 arrays are returned as their raw 16-bit patterns (``np.uint16``), rounded
+from float32 with round-to-nearest-even; float32 arrays as ``np.float32``.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from .configs import Config
+
+TID_Z, TID_NOISE, TID_E, TID_WT, TID_H, TID_WC, TID_TAU, TID_ANCHOR, TID_ZBONUS = 1, 2, 3, 4, 5, 6, 7, 8, 10
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return the bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def _bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _rng(cfg: Config, tid: int, slab: int = 0) -> np.random.Generator:
+    return np.random.default_rng([cfg.seed, tid, slab])
+
+
+def _store(x32: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_bits_from_f32(x32) if dtype == "bf16" else np.ascontiguousarray(x32, np.float32)
+
+
+def _as_f32(stored: np.ndarray, dtype: str) -> np.ndarray:
+    return _bf16_bits_to_f32(stored) if dtype == "bf16" else stored
+
+
+def _base_rows(cfg: Config, rng: np.random.Generator, n: int, positions) -> np.ndarray:
+    """n base-logit rows (float32) for the given 1-based positions."""
+    V = cfg.V
+    out = np.empty((n, V), np.float32)
+    if cfg.z_kind == "zipf":
+        ranked = (cfg.zipf_top - cfg.zipf_slope * np.log1p(np.arange(V, dtype=np.float64))).astype(np.float32)
+        for i in range(n):
+            perm = rng.permutation(V)
+            out[i, perm] = ranked
+            out[i] += rng.standard_normal(V, dtype=np.float32) * np.float32(cfg.zipf_noise)
+    elif cfg.z_kind == "normal":
+        rng.standard_normal(out=out, dtype=np.float32)
+        out *= np.float32(cfg.z_std)
+    else:
+        raise ValueError(cfg.z_kind)
+    if cfg.flatten_after is not None:
+        for i, pos in enumerate(positions):
+            if pos > cfg.flatten_after:
+                out[i] *= np.float32(cfg.flatten_scale)
+    return out
+
+
+def T_table(cfg: Config) -> np.ndarray:
+    """Step time T[N] for N = 0 .. B*(K+1) verified positions (float32)."""
+    N = np.arange(cfg.n_max + 1, dtype=np.float64)
+    kind = cfg.ttable[0]
+    if kind == "linear":
+        _, a, b = cfg.ttable
+        t = a + b * N
+    elif kind == "knee":
+        _, flat, knee, slope = cfg.ttable
+        t = flat + slope * np.maximum(N - knee, 0.0)
+    elif kind == "table":
+        t = np.asarray(cfg.ttable[1], np.float64)
+        assert t.shape == N.shape
+    else:
+        raise ValueError(kind)
+    return t.astype(np.float32)
+
+
+def make_inputs(cfg: Config, threads: int | None = None) -> dict:
+    """All arrays of one cycle for ``cfg`` (see the module docstring for the layout)."""
+    B, K, V, r, d = cfg.B, cfg.K, cfg.V, cfg.r, cfg.d
+    ldt = cfg.logits_dtype
+    zdtype = np.uint16 if ldt == "bf16" else np.float32
+    Z = np.empty((B, K, V), zdtype)
+    Zt = np.empty((B, K + 1, V), zdtype)
+
+    def slab(b: int) -> None:
+        z32 = _base_rows(cfg, _rng(cfg, TID_Z, b), K, range(1, K + 1))
+        zs = _store(z32, ldt)
+        Z[b] = zs
+        zb32 = _base_rows(cfg, _rng(cfg, TID_ZBONUS, b), 1, [K + 1])
+        zbs = _store(zb32, ldt)
+        base = np.concatenate([_as_f32(zs, ldt), _as_f32(zbs, ldt)], axis=0)
+        noise = _rng(cfg, TID_NOISE, b).standard_normal((K + 1, V), dtype=np.float32)
+        Zt[b] = _store(base + noise * np.float32(cfg.target_noise), ldt)
+
+    nthreads = threads or min(16, os.cpu_count() or 1)
+    if B == 1 or nthreads == 1:
+        for b in range(B):
+            slab(b)
+    else:
+        with ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(slab, range(B)))
+
+    E32 = _rng(cfg, TID_E).standard_normal((V, r), dtype=np.float32) * np.float32(cfg.ew_std)
+    W32 = _rng(cfg, TID_WT).standard_normal((V, r), dtype=np.float32) * np.float32(cfg.ew_std)
+    hdt = cfg.hidden_dtype
+    h = np.empty((B, K, d), np.uint16 if hdt == "bf16" else np.float32)
+    for b in range(B):
+        h[b] = _store(_rng(cfg, TID_H, b).standard_normal((K, d), dtype=np.float32) * np.float32(cfg.h_std), hdt)
+    w_c = (_rng(cfg, TID_WC).standard_normal(d + r, dtype=np.float32) * np.float32(cfg.wc_std)).astype(np.float32)
+    lo, hi = cfg.tau_range
+    tau = _rng(cfg, TID_TAU).uniform(lo, hi, K).astype(np.float32)
+    anchor = _rng(cfg, TID_ANCHOR).integers(0, V, B).astype(np.int32)
+    return {
+        "cfg": cfg,
+        "Z": Z, "Zt": Zt,
+        "E": _store(E32, cfg.weight_dtype), "Wt": _store(W32, cfg.weight_dtype),
+        "h": h, "w_c": w_c, "b_c": float(cfg.b_c), "tau": tau,
+        "anchor": anchor, "T": T_table(cfg),
+    }
