@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Throughput of the per-cycle draft -> schedule -> verify step on one MI355X.
+
+One step = dspark_draft + dspark_schedule + dspark_verify over one batch of
+synthetic input (the high-concurrency workload by default: B=256 requests,
+K=16 draft positions, V=151,936, rank 256, d=4096, bf16), with the inputs
+resident in HBM.  Three input sets (the generated one and two copies rolled
+along the vocabulary) rotate so that consecutive steps do not find their
+logits in the 256 MB Infinity Cache.
+
+Prints one JSON line: positions/s (B*K per step), the cycle's algorithmic HBM
+bandwidth, a roofline entry for the dominant kernel (the vocabulary-stream
+kernel of the draft steps, timed with HIP events recorded on the library's
+stream), and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "draft+verify positions/sec and achieved HBM GB/s (% peak), B=256 K=16 V=152k"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["draft_sampling_verification_markov_amd/csrc/k_stream.hip",
+                  "draft_sampling_verification_markov_amd/csrc/dspark_device.hpp",
+                  "draft_sampling_verification_markov_amd/csrc/dspark_internal.hpp"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def element_size(dt: str) -> int:
+    return 2 if dt == "bf16" else 4
+
+
+def cycle_bytes(cfg, N: int, R: int) -> float:
+    """Algorithmic HBM bytes of one cycle: Z once, Wt once, E gathers, h, the N
+    verified target rows, and the Z rows re-read at the R rejections."""
+    sz, sw, sh = element_size(cfg.logits_dtype), element_size(cfg.weight_dtype), element_size(cfg.hidden_dtype)
+    B, K, V, r, d = cfg.B, cfg.K, cfg.V, cfg.r, cfg.d
+    return (B * K * V * sz + r * V * sw + 2 * B * K * r * sw + B * K * d * sh + N * V * sz + R * V * sz)
+
+
+def stream_launch_bytes(cfg, G: int) -> float:
+    """Algorithmic bytes of one draft-step stream launch: the step's Z slab, Wt
+    (the launch forms the whole [B x r] . [r x V] product), the gathered E rows,
+    and the per-(row, workgroup) partials written."""
+    sz, sw = element_size(cfg.logits_dtype), element_size(cfg.weight_dtype)
+    return cfg.B * cfg.V * sz + cfg.V * cfg.r * sw + cfg.B * cfg.r * sw + cfg.B * G * 16
+
+
+class Hip:
+    """Raw HIP events through the runtime library (events recorded on the library's stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n: int):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.lib.hipEventCreate(ctypes.byref(h)) == 0
+            arr[i] = h
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, arr) -> None:
+        for h in arr:
+            self.lib.hipEventDestroy(h)
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per stream launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, f"k_stream_draft_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return float(rec["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(cfg, inp, gpu, n_req: int):
+    """The oracle, as it stands, on a bounded sample: all K draft steps, the
+    confidence head and verification for n_req requests, and the scheduler over
+    the whole batch (on the GPU's survivals)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import conf as oconf
+    from oracle import draft as odraft
+    from oracle import sched as osched
+    from oracle import verify as overify
+
+    reqs = np.arange(n_req)
+    t0 = time.perf_counter()
+    d = odraft.draft(inp["Z"], inp["E"], inp["Wt"], inp["anchor"], cfg.T_s, cfg.seed, requests=reqs)
+    oconf.confidence(inp["h"][reqs], inp["E"], inp["w_c"], inp["b_c"], inp["tau"], inp["anchor"][reqs], d["x"])
+    sc = osched.schedule(gpu["surv"].astype(np.float64), inp["T"])
+    x = gpu["tok"].astype(np.int64).copy()
+    x[reqs] = d["x"]
+    overify.verify(inp["Zt"], inp["Z"], inp["E"], inp["Wt"], inp["anchor"], x, sc["n"], cfg.T_s, cfg.seed,
+                   requests=reqs)
+    t = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": n_req * cfg.K / t, "unit": "positions/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_req} of {cfg.B} requests x all {cfg.K} positions (draft, confidence, verify) "
+                      f"+ full-batch schedule; {t:.1f} s wall; host {platform.processor() or platform.machine()}, "
+                      f"{os.cpu_count()} logical CPUs"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="high_concurrency")
+    ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this step has no multi-GPU path; "
+              "each GPU would run its own batch, table and scheduler independently.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    from draft_sampling_verification_markov_amd import dspark, runner
+
+    if not os.path.exists(dspark.LIB_PATH):
+        from draft_sampling_verification_markov_amd import build as _b
+        _b.build()
+    dspark.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = synth.get_config(args.config)
+    P = dspark.Problem.from_config(cfg)
+    log(f"workload {cfg.name}: B={cfg.B} K={cfg.K} V={cfg.V} r={cfg.r} d={cfg.d} {cfg.logits_dtype}")
+    t0 = time.time()
+    inp = synth.make_inputs(cfg)
+    log(f"inputs generated in {time.time() - t0:.1f} s")
+    x0 = runner.CycleInputs.upload(inp, dev)
+    sets = [x0]
+    for shift in (cfg.V // 3, 2 * cfg.V // 3):
+        xs = runner.CycleInputs(**vars(x0))
+        xs.Z = torch.roll(x0.Z, shift, dims=-1).contiguous()
+        xs.Zt = torch.roll(x0.Zt, shift, dims=-1).contiguous()
+        sets.append(xs)
+    o = runner.CycleOutputs(P, dev)
+    torch.cuda.synchronize()
+    log("inputs resident on the GPU (3 rotating sets)")
+
+    for i in range(args.warmup):
+        runner.run_cycle(P, sets[i % 3], o)
+    torch.cuda.synchronize()
+    log(f"{args.warmup} warm-up steps done")
+
+    # timed region: exactly `steps` whole steps
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        runner.run_cycle(P, sets[i % 3], o)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    log(f"{args.steps} timed steps: {ms_step:.3f} ms/step")
+
+    # per-call split (a separate pass over the same steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    split = np.zeros(3)
+    for i in range(args.steps):
+        xs = sets[i % 3]
+        ev[0].record()
+        runner.draft(P, xs, o)
+        ev[1].record()
+        runner.schedule(P, xs, o)
+        ev[2].record()
+        runner.verify(P, xs, o)
+        ev[3].record()
+        torch.cuda.synchronize()
+        split += [ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]), ev[2].elapsed_time(ev[3])]
+    split /= args.steps
+
+    # dominant kernel: the draft-step stream kernel, timed by events the library
+    # records around each of its launches on the same stream
+    hip = Hip()
+    n_ev = 2 * cfg.K
+    kernel_ms = []
+    for i in range(args.steps):
+        xs = sets[i % 3]
+        evs = hip.events(n_ev)
+        dspark.draft_timed(P, xs.Z, xs.E, xs.Wt, xs.h, xs.w_c, xs.b_c, xs.tau, xs.anchor,
+                           o.tok, o.logq, o.lse, o.conf, o.surv, o.workspace, evs)
+        torch.cuda.synchronize()
+        kernel_ms += [hip.elapsed_ms(evs[2 * k], evs[2 * k + 1]) for k in range(cfg.K)]
+        hip.destroy(evs)
+    k_ms = float(np.mean(kernel_ms))
+
+    # final outputs of one step on set 0 for the realised schedule
+    runner.run_cycle(P, sets[0], o)
+    torch.cuda.synchronize()
+    g = o.host()
+    N = int(g["n_total"][0])
+    R = int((~np.isnan(g["resid_mass"])).sum())
+    positions = cfg.B * cfg.K
+    value = positions / (ms_step / 1e3)
+    alg_bytes = cycle_bytes(cfg, N, R)
+    G = min((cfg.V + 127) // 128, 256)
+    launch_bytes = stream_launch_bytes(cfg, G)
+    achieved = launch_bytes / (k_ms / 1e3) / 1e9
+    traffic = traffic_from_profile(cfg.name)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.logits_dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "K": cfg.K, "V": cfg.V, "r": cfg.r, "d": cfg.d,
+                   "logits": cfg.logits_dtype, "factors": cfg.weight_dtype, "T_s": cfg.T_s, "seed": cfg.seed},
+        "hbm_gbs_algorithmic": alg_bytes / (ms_step / 1e3) / 1e9,
+        "hbm_frac_algorithmic": alg_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes_per_step": alg_bytes,
+        "logits_per_s": (positions + N) * cfg.V / (ms_step / 1e3),
+        "ms_split": {"draft": split[0], "schedule": split[1], "verify": split[2]},
+        "scheduled_N": N,
+        "mean_accepted": float(g["n_acc"].mean()),
+        "roofline": {
+            "kernel": "k_stream (draft step)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "avg_launch_ms": k_ms,
+            "bytes_per_launch": launch_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_requests} requests")
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, g, args.cpu_requests)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,278 @@
+// C ABI of the dspark library: argument validation, workspace layout and the
+// kernel sequence of each call.  See include/dspark.h for the contract.
+#include <math.h>
+
+#include "dspark_internal.hpp"
+
+namespace dspark {
+
+static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Layout make_layout(const dspark_problem& P) {
+  Layout L{};
+  const size_t B = (size_t)P.B, K = (size_t)P.K;
+  L.G = stream_grid(P.V);
+  L.nseg = vlse_segments(P.V);
+  size_t off = 0;
+  L.part = off;   off = align_up(off + B * L.G * sizeof(float4));
+  L.vlse = off;   off = align_up(off + B * K * L.nseg * sizeof(float2));
+  L.lsep = off;   off = align_up(off + B * K * sizeof(float));
+  L.job = off;    off = align_up(off + B * sizeof(int32_t));
+  L.rows = off;   off = align_up(off + B * K * sizeof(int32_t));
+  L.nrows = off;  off = align_up(off + sizeof(int32_t));
+  L.sorted = off; off = align_up(off + B * K * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static dspark_status check_problem(const dspark_problem* P) {
+  if (!P) return DSPARK_E_POINTER;
+  if (P->B < 1 || P->B > 65536 || P->K < 1 || P->K > 64) return DSPARK_E_INVALID;
+  if (P->V < 8 || P->V % 8 != 0) return DSPARK_E_INVALID;
+  if (P->d < 1 || P->d % 8 != 0 || P->r < 1) return DSPARK_E_INVALID;
+  if ((long long)P->B * P->K > (1LL << 20)) return DSPARK_E_INVALID;
+  if (!(P->sampling_temp > 0.0f) || !isfinite(P->sampling_temp)) return DSPARK_E_INVALID;
+  for (int32_t t : {P->logits_dtype, P->weight_dtype, P->hidden_dtype})
+    if (t != DSPARK_F32 && t != DSPARK_BF16) return DSPARK_E_DTYPE;
+  const int r = P->r;
+  if (P->weight_dtype == DSPARK_BF16) {
+    if (r != 16 && r != 32 && r != 64 && r != 128 && r != 256) return DSPARK_E_UNSUPPORTED;
+  } else {
+    if (r != 16 && r != 32 && r != 64) return DSPARK_E_UNSUPPORTED;
+  }
+  return DSPARK_OK;
+}
+
+static dspark_status check_workspace(const dspark_problem& P, void* ws, size_t bytes) {
+  if (!ws || !aligned(ws, 256)) return DSPARK_E_WORKSPACE;
+  if (bytes < make_layout(P).total) return DSPARK_E_WORKSPACE;
+  return DSPARK_OK;
+}
+
+template <typename T>
+static T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+static Key host_key(uint64_t seed) { return Key{(uint32_t)seed, (uint32_t)(seed >> 32)}; }
+
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" size_t dspark_workspace_bytes(const dspark_problem* P) {
+  if (check_problem(P) != DSPARK_OK) return 0;
+  return make_layout(*P).total;
+}
+
+extern "C" const char* dspark_status_string(int status) {
+  switch (status) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_E_INVALID: return "invalid problem size or scalar argument";
+    case DSPARK_E_DTYPE: return "unknown dtype code";
+    case DSPARK_E_UNSUPPORTED: return "unsupported configuration (no kernel built for it)";
+    case DSPARK_E_WORKSPACE: return "workspace null, misaligned or too small";
+    case DSPARK_E_POINTER: return "null or misaligned pointer argument";
+    case DSPARK_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+static dspark_status draft_impl(const dspark_problem* P, const void* Z, const void* E, const void* Wt,
+                                const void* h, const float* w_conf, float b_conf, const float* tau,
+                                const int32_t* anchor, int32_t* draft_tok, float* draft_logq, float* draft_lse,
+                                float* conf, float* surv, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream, hipEvent_t* events) {
+  dspark_status st = check_problem(P);
+  if (st != DSPARK_OK) return st;
+  const dspark_problem& p = *P;
+  if (!Z || !E || !Wt || !h || !w_conf || !tau || !anchor || !draft_tok || !draft_logq || !draft_lse || !conf ||
+      !surv)
+    return DSPARK_E_POINTER;
+  for (const void* q : {Z, E, Wt, h, (const void*)w_conf})
+    if (!aligned(q, 16)) return DSPARK_E_POINTER;
+  for (const void* q : {(const void*)tau, (const void*)anchor, (const void*)draft_tok, (const void*)draft_logq,
+                        (const void*)draft_lse, (const void*)conf, (const void*)surv})
+    if (!aligned(q, 4)) return DSPARK_E_POINTER;
+  st = check_workspace(p, workspace, workspace_bytes);
+  if (st != DSPARK_OK) return st;
+  (void)hipGetLastError();
+
+  const Layout L = make_layout(p);
+  float4* part = at<float4>(workspace, L.part);
+  StreamArgs sa{};
+  sa.Z = Z;
+  sa.E = E;
+  sa.Wt = Wt;
+  sa.anchor = anchor;
+  sa.tok = draft_tok;
+  sa.part = part;
+  sa.B = p.B;
+  sa.K = p.K;
+  sa.V = p.V;
+  sa.nchunks = n_chunks(p.V);
+  sa.scale2 = kLog2e / p.sampling_temp;
+  sa.key = host_key(p.seed);
+
+  SelectArgs se{};
+  se.Z = Z;
+  se.E = E;
+  se.Wt = Wt;
+  se.anchor = anchor;
+  se.tok = draft_tok;
+  se.logq = draft_logq;
+  se.lse = draft_lse;
+  se.part = part;
+  se.B = p.B;
+  se.K = p.K;
+  se.V = p.V;
+  se.r = p.r;
+  se.G = L.G;
+  se.inv_T = 1.0f / p.sampling_temp;
+  se.key = sa.key;
+
+  for (int k = 1; k <= p.K; ++k) {
+    sa.k = k;
+    se.k = k;
+    if (events && hipEventRecord(events[2 * (k - 1)], stream) != hipSuccess) return DSPARK_E_LAUNCH;
+    if (launch_stream_draft(p, sa, L.G, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+    if (events && hipEventRecord(events[2 * (k - 1) + 1], stream) != hipSuccess) return DSPARK_E_LAUNCH;
+    if (launch_select(p, se, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+  }
+
+  ConfArgs ca{};
+  ca.h = h;
+  ca.E = E;
+  ca.w_c = w_conf;
+  ca.b_c = b_conf;
+  ca.tau = tau;
+  ca.anchor = anchor;
+  ca.tok = draft_tok;
+  ca.conf = conf;
+  ca.surv = surv;
+  ca.B = p.B;
+  ca.K = p.K;
+  ca.V = p.V;
+  ca.d = p.d;
+  ca.r = p.r;
+  if (launch_conf(p, ca, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status dspark_draft(const dspark_problem* P, const void* Z, const void* E, const void* Wt,
+                                      const void* h, const float* w_conf, float b_conf, const float* tau,
+                                      const int32_t* anchor, int32_t* draft_tok, float* draft_logq,
+                                      float* draft_lse, float* conf, float* surv, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return draft_impl(P, Z, E, Wt, h, w_conf, b_conf, tau, anchor, draft_tok, draft_logq, draft_lse, conf, surv,
+                    workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" dspark_status dspark_draft_timed(const dspark_problem* P, const void* Z, const void* E, const void* Wt,
+                                            const void* h, const float* w_conf, float b_conf, const float* tau,
+                                            const int32_t* anchor, int32_t* draft_tok, float* draft_logq,
+                                            float* draft_lse, float* conf, float* surv, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+  if (!events) return DSPARK_E_POINTER;
+  return draft_impl(P, Z, E, Wt, h, w_conf, b_conf, tau, anchor, draft_tok, draft_logq, draft_lse, conf, surv,
+                    workspace, workspace_bytes, stream, events);
+}
+
+extern "C" dspark_status dspark_schedule(const dspark_problem* P, const float* surv, const float* T_table,
+                                         int32_t* n_sched, int32_t* n_total, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  dspark_status st = check_problem(P);
+  if (st != DSPARK_OK) return st;
+  if (!surv || !T_table || !n_sched || !n_total) return DSPARK_E_POINTER;
+  for (const void* q : {(const void*)surv, (const void*)T_table, (const void*)n_sched, (const void*)n_total})
+    if (!aligned(q, 4)) return DSPARK_E_POINTER;
+  st = check_workspace(*P, workspace, workspace_bytes);
+  if (st != DSPARK_OK) return st;
+  (void)hipGetLastError();
+  const Layout L = make_layout(*P);
+  if (launch_schedule(*P, surv, T_table, n_sched, n_total, at<int32_t>(workspace, L.sorted), stream) != hipSuccess)
+    return DSPARK_E_LAUNCH;
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status dspark_verify(const dspark_problem* P, const void* target, const void* Z, const void* E,
+                                       const void* Wt, const int32_t* anchor, const int32_t* draft_tok,
+                                       const float* draft_logq, const float* draft_lse, const int32_t* n_sched,
+                                       int32_t* out_tok, int32_t* n_accepted, int32_t* next_anchor, float* logp,
+                                       float* resid_mass, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  dspark_status st = check_problem(P);
+  if (st != DSPARK_OK) return st;
+  const dspark_problem& p = *P;
+  if (!target || !Z || !E || !Wt || !anchor || !draft_tok || !draft_logq || !draft_lse || !n_sched || !out_tok ||
+      !n_accepted || !next_anchor || !logp || !resid_mass)
+    return DSPARK_E_POINTER;
+  for (const void* q : {target, Z, E, Wt})
+    if (!aligned(q, 16)) return DSPARK_E_POINTER;
+  for (const void* q : {(const void*)anchor, (const void*)draft_tok, (const void*)draft_logq,
+                        (const void*)draft_lse, (const void*)n_sched, (const void*)out_tok,
+                        (const void*)n_accepted, (const void*)next_anchor, (const void*)logp,
+                        (const void*)resid_mass})
+    if (!aligned(q, 4)) return DSPARK_E_POINTER;
+  st = check_workspace(p, workspace, workspace_bytes);
+  if (st != DSPARK_OK) return st;
+  (void)hipGetLastError();
+
+  const Layout L = make_layout(p);
+  VerifyArgs va{};
+  va.Zt = target;
+  va.Z = Z;
+  va.E = E;
+  va.Wt = Wt;
+  va.anchor = anchor;
+  va.tok = draft_tok;
+  va.logq = draft_logq;
+  va.lse_q = draft_lse;
+  va.n_sched = n_sched;
+  va.out_tok = out_tok;
+  va.n_acc = n_accepted;
+  va.next_anchor = next_anchor;
+  va.logp = logp;
+  va.resid_mass = resid_mass;
+  va.vlse = at<float2>(workspace, L.vlse);
+  va.lse_p = at<float>(workspace, L.lsep);
+  va.job = at<int32_t>(workspace, L.job);
+  va.rows = at<int32_t>(workspace, L.rows);
+  va.nrows = at<int32_t>(workspace, L.nrows);
+  va.part = at<float4>(workspace, L.part);
+  va.B = p.B;
+  va.K = p.K;
+  va.V = p.V;
+  va.r = p.r;
+  va.G = L.G;
+  va.nseg = L.nseg;
+  va.inv_T = 1.0f / p.sampling_temp;
+  va.scale2 = kLog2e / p.sampling_temp;
+  va.key = host_key(p.seed);
+  if (launch_verify_pre(p, va, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+
+  StreamArgs sa{};
+  sa.Z = Z;
+  sa.Zt = target;
+  sa.E = E;
+  sa.Wt = Wt;
+  sa.anchor = anchor;
+  sa.tok = draft_tok;
+  sa.lse_q = draft_lse;
+  sa.lse_p = va.lse_p;
+  sa.job = va.job;
+  sa.n_sched = n_sched;
+  sa.part = at<float4>(workspace, L.part);
+  sa.B = p.B;
+  sa.K = p.K;
+  sa.V = p.V;
+  sa.k = 0;
+  sa.nchunks = n_chunks(p.V);
+  sa.scale2 = va.scale2;
+  sa.key = va.key;
+  if (launch_stream_verify(p, sa, L.G, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+  if (launch_verify_finish(p, va, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+  return DSPARK_OK;
+}

@@ -1,0 +1,185 @@
+// Device helpers shared by the dspark kernels: Philox4x32-10, the uniform and
+// Gumbel transforms, bf16 unpacking, and wave/block reductions.  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+// Vocabulary chunk of the two-level Gumbel-max draw.
+constexpr int kChunk = 128;
+
+// Purposes of the random draws of one cycle (counter word 3).
+enum : uint32_t {
+  kDraftChunk = 1,
+  kDraftElem = 2,
+  kAccept = 3,
+  kResidChunk = 4,
+  kResidElem = 5,
+  kBonusChunk = 6,
+  kBonusElem = 7,
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct Words4 {
+  uint32_t w[4];
+};
+
+// Philox4x32 with ten rounds (Salmon, Moraes, Dror, Shaw, SC'11): counter words
+// 0 and 2 are multiplied by the two round multipliers into 64-bit products whose
+// halves are mixed with words 1, 3 and the key; the key advances by the two
+// Weyl increments between rounds.
+__device__ __forceinline__ Words4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  Words4 r;
+  r.w[0] = c0;
+  r.w[1] = c1;
+  r.w[2] = c2;
+  r.w[3] = c3;
+  return r;
+}
+
+struct Key {
+  uint32_t lo, hi;
+};
+
+__device__ __forceinline__ Key make_key(uint64_t seed) { return Key{(uint32_t)seed, (uint32_t)(seed >> 32)}; }
+
+// The four words of counter (idx >> 2, b, k, purpose); draw idx is word idx & 3.
+__device__ __forceinline__ Words4 draw_quad(Key key, uint32_t idx, uint32_t b, uint32_t k, uint32_t purpose) {
+  return philox4x32_10(idx >> 2, b, k, purpose, key.lo, key.hi);
+}
+
+__device__ __forceinline__ uint32_t draw_word(Key key, uint32_t idx, uint32_t b, uint32_t k, uint32_t purpose) {
+  const Words4 q = draw_quad(key, idx, b, k, purpose);
+  const uint32_t s = idx & 3u;
+  return s == 0 ? q.w[0] : s == 1 ? q.w[1] : s == 2 ? q.w[2] : q.w[3];
+}
+
+// Odd multiple of 2^-24 in (0, 1); the 24-bit integer converts exactly.
+__device__ __forceinline__ float uniform01(uint32_t w) { return (float)((w >> 8) | 1u) * 0x1p-24f; }
+
+// -ln(-ln u); for u >= 1/2, -ln u is taken as -log1p(-(1 - u)) with 1 - u exact,
+// which keeps the largest Gumbel values accurate.  Accurate libm calls, no
+// fast-math approximations.
+__device__ __forceinline__ float gumbel_from_word(uint32_t w) {
+  const float u = uniform01(w);
+  const float e = (u >= 0.5f) ? -log1pf(-(1.0f - u)) : -logf(u);
+  return -logf(e);
+}
+
+// bf16 halves of a packed 32-bit word -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Token id used as an index, clamped into [0, V) so that a corrupt id cannot
+// address outside the factor tables.
+__device__ __forceinline__ int clamp_id(int v, int V) { return v < 0 ? 0 : (v >= V ? V - 1 : v); }
+
+// Argmax with the smallest-index tie-break.
+__device__ __forceinline__ bool better(float s, int i, float best, int best_i) {
+  return s > best || (s == best && i < best_i);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ void wave_argmax(float& s, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float so = __shfl_xor(s, o);
+    const int io = __shfl_xor(i, o);
+    if (better(so, io, s, i)) {
+      s = so;
+      i = io;
+    }
+  }
+}
+
+// Combine two (max, sum of 2^(x - max)) pairs in base 2.
+__device__ __forceinline__ void lse2_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * exp2f(m - mn) + s2 * exp2f(m2 - mn);
+  m = mn;
+}
+
+
+// Logit at vocabulary id v of a row (bf16 bits or fp32).
+template <typename ZT>
+__device__ __forceinline__ float logit_at(const ZT* row, int v);
+template <>
+__device__ __forceinline__ float logit_at<uint16_t>(const uint16_t* row, int v) { return bf16_to_f32(row[v]); }
+template <>
+__device__ __forceinline__ float logit_at<float>(const float* row, int v) { return row[v]; }
+
+// Dot product of E[prev] with Wt[v] over a contiguous half of the rank.
+template <typename WT>
+__device__ __forceinline__ float half_dot(const WT* E, const WT* Wt, int prev, int v, int r, int h);
+
+template <>
+__device__ __forceinline__ float half_dot<uint16_t>(const uint16_t* E, const uint16_t* Wt, int prev, int v, int r,
+                                                    int h) {
+  const int n = r >> 1;
+  const uint4* e = reinterpret_cast<const uint4*>(E + (size_t)prev * r + h * n);
+  const uint4* w = reinterpret_cast<const uint4*>(Wt + (size_t)v * r + h * n);
+  float acc = 0.f;
+  for (int j = 0; j < n / 8; ++j) {
+    const uint4 ev = e[j], wv = w[j];
+    acc = fmaf(bf16_lo(ev.x), bf16_lo(wv.x), acc);
+    acc = fmaf(bf16_hi(ev.x), bf16_hi(wv.x), acc);
+    acc = fmaf(bf16_lo(ev.y), bf16_lo(wv.y), acc);
+    acc = fmaf(bf16_hi(ev.y), bf16_hi(wv.y), acc);
+    acc = fmaf(bf16_lo(ev.z), bf16_lo(wv.z), acc);
+    acc = fmaf(bf16_hi(ev.z), bf16_hi(wv.z), acc);
+    acc = fmaf(bf16_lo(ev.w), bf16_lo(wv.w), acc);
+    acc = fmaf(bf16_hi(ev.w), bf16_hi(wv.w), acc);
+  }
+  return acc;
+}
+
+template <>
+__device__ __forceinline__ float half_dot<float>(const float* E, const float* Wt, int prev, int v, int r, int h) {
+  const int n = r >> 1;
+  const float4* e = reinterpret_cast<const float4*>(E + (size_t)prev * r + h * n);
+  const float4* w = reinterpret_cast<const float4*>(Wt + (size_t)v * r + h * n);
+  float acc = 0.f;
+  for (int j = 0; j < n / 4; ++j) {
+    const float4 ev = e[j], wv = w[j];
+    acc = fmaf(ev.x, wv.x, acc);
+    acc = fmaf(ev.y, wv.y, acc);
+    acc = fmaf(ev.z, wv.z, acc);
+    acc = fmaf(ev.w, wv.w, acc);
+  }
+  return acc;
+}
+
+}  // namespace dspark

@@ -1,0 +1,386 @@
+// Rejection-sampling verification of the scheduled draft prefix.
+//
+// DSpark page, Overview and Background: the target scores all scheduled draft
+// positions in one pass, keeps the longest prefix consistent with its own
+// distribution, drops everything after the first rejection, and the
+// rejection-sampling rule keeps the output distributed exactly as the target.
+// The rule (speculative sampling): accept x_k iff u_k <= min(1, p_k(x_k) /
+// q_k(x_k)); at the first rejection draw from max(0, p - q) normalised; if all
+// scheduled positions pass, draw a bonus token from the next target row.
+//
+//   k_rowlist  one workgroup: compact list of the rows (b, k <= n_b) to test
+//   k_vlse     (row, 8192-entry segment) items: base-2 (max, sum) of target/T_s
+//   k_accept   one wave per request: log-partition of each tested row,
+//              log p_k(x_k), the accept draw, the first rejection
+//   (k_stream in verify mode: chunk scores of the residual or bonus row)
+//   k_finish   one workgroup per request: winning chunk, entry draw, emission
+#include "dspark_internal.hpp"
+
+namespace dspark {
+namespace {
+
+constexpr int kListThreads = 1024;
+
+__global__ __launch_bounds__(kListThreads) void k_rowlist(const int32_t* n_sched, int B, int K, int32_t* rows,
+                                                          int32_t* nrows) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int s_wsum[kListThreads / 64];
+  __shared__ int s_base;
+  if (tid == 0) s_base = 0;
+  __syncthreads();
+  for (int base = 0; base < B; base += kListThreads) {
+    const int b = base + tid;
+    int nb = b < B ? n_sched[b] : 0;
+    nb = nb < 0 ? 0 : (nb > K ? K : nb);
+    int incl = nb;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int off = s_base;
+    for (int w = 0; w < wave; ++w) off += s_wsum[w];
+    off += incl - nb;
+    for (int j = 0; j < nb; ++j) rows[off + j] = b * 64 + j;
+    __syncthreads();
+    if (tid == 0) {
+      int t = 0;
+      for (int w = 0; w < kListThreads / 64; ++w) t += s_wsum[w];
+      s_base += t;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) *nrows = s_base;
+}
+
+template <typename ZT>
+struct Vec16;  // one 16-byte load of logits
+template <>
+struct Vec16<uint16_t> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void load(const uint16_t* p, float* o) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    o[0] = bf16_lo(u.x);
+    o[1] = bf16_hi(u.x);
+    o[2] = bf16_lo(u.y);
+    o[3] = bf16_hi(u.y);
+    o[4] = bf16_lo(u.z);
+    o[5] = bf16_hi(u.z);
+    o[6] = bf16_lo(u.w);
+    o[7] = bf16_hi(u.w);
+  }
+};
+template <>
+struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void load(const float* p, float* o) {
+    const float4 f = *reinterpret_cast<const float4*>(p);
+    o[0] = f.x;
+    o[1] = f.y;
+    o[2] = f.z;
+    o[3] = f.w;
+  }
+};
+
+template <typename ZT>
+__global__ __launch_bounds__(256) void k_vlse(VerifyArgs a) {
+  using Vec = Vec16<ZT>;
+  constexpr int kPer = kVlseSeg / 256;  // entries per thread
+  constexpr int kLoads = kPer / Vec::N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float s_m[4], s_s[4];
+  const int M = *a.nrows;
+  const int items = M * a.nseg;
+  const ZT* Zt = static_cast<const ZT*>(a.Zt);
+  for (int w = blockIdx.x; w < items; w += gridDim.x) {
+    const int j = w / a.nseg, seg = w - j * a.nseg;
+    const int code = a.rows[j];
+    const int b = code >> 6, k0 = code & 63;
+    const ZT* row = Zt + ((size_t)b * (a.K + 1) + k0) * a.V;
+    const int lo = seg * kVlseSeg;
+    float x[kPer];
+    float m = -INFINITY;
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      const int v = lo + (l * 256 + tid) * Vec::N;
+      if (v < a.V) {
+        Vec::load(row + v, x + l * Vec::N);
+#pragma unroll
+        for (int i = 0; i < Vec::N; ++i) {
+          x[l * Vec::N + i] *= a.scale2;
+          m = fmaxf(m, x[l * Vec::N + i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < Vec::N; ++i) x[l * Vec::N + i] = -INFINITY;
+      }
+    }
+    m = wave_max(m);
+    if (lane == 0) s_m[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) s += exp2f(x[i] - m);
+    s = wave_sum(s);
+    if (lane == 0) s_s[wave] = s;
+    __syncthreads();
+    if (tid == 0) a.vlse[((size_t)b * a.K + k0) * a.nseg + seg] = make_float2(m, s_s[0] + s_s[1] + s_s[2] + s_s[3]);
+    __syncthreads();
+  }
+}
+
+template <typename ZT>
+__global__ __launch_bounds__(64) void k_accept(VerifyArgs a) {
+  const int b = blockIdx.x, k0 = threadIdx.x;
+  const int K = a.K;
+  int nb = a.n_sched[b];
+  nb = nb < 0 ? 0 : (nb > K ? K : nb);
+  const bool tested = k0 < nb;
+  float logp = __int_as_float(0x7fc00000);  // NaN where not verified
+  bool rej = false;
+  if (tested) {
+    float m = -INFINITY, s = 0.f;
+    const float2* part = a.vlse + ((size_t)b * K + k0) * a.nseg;
+    for (int i = 0; i < a.nseg; ++i) lse2_merge(m, s, part[i].x, part[i].y);
+    const float lse_p = (m + log2f(s)) * kLn2;
+    const int x = clamp_id(a.tok[(size_t)b * K + k0], a.V);
+    const ZT* row = static_cast<const ZT*>(a.Zt) + ((size_t)b * (K + 1) + k0) * a.V;
+    logp = logit_at<ZT>(row, x) * a.inv_T - lse_p;
+    a.lse_p[(size_t)b * K + k0] = lse_p;
+    const float u = uniform01(draw_word(a.key, 0u, (uint32_t)b, (uint32_t)(k0 + 1), kAccept));
+    const float ratio = expf(fminf(0.f, logp - a.logq[(size_t)b * K + k0]));
+    rej = !(u <= ratio);
+  }
+  if (k0 < K) a.logp[(size_t)b * K + k0] = logp;
+  const unsigned long long mask = __ballot(rej);
+  if (k0 == 0) a.job[b] = mask ? __ffsll((long long)mask) : 0;
+}
+
+// Two-level Gumbel-max over a whole row of x / T_s inside one workgroup (used
+// only when a residual has no mass left after rounding: the draw falls back to p).
+template <typename ZT>
+__device__ int full_row_draw(const ZT* row, int V, float inv_T, Key key, int b, int k, uint32_t pc, uint32_t pe,
+                             float* s_best, int* s_idx) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nc = (V + kChunk - 1) / kChunk;
+  float best = -INFINITY;
+  int bc = 0x7fffffff;
+  for (int c = wave; c < nc; c += 4) {
+    const int v0 = c * kChunk + lane, v1 = v0 + 64;
+    const float x0 = v0 < V ? logit_at<ZT>(row, v0) * inv_T : -INFINITY;
+    const float x1 = v1 < V ? logit_at<ZT>(row, v1) * inv_T : -INFINITY;
+    const float m = wave_max(fmaxf(x0, x1));
+    const float s = wave_sum(expf(x0 - m) + expf(x1 - m));
+    const float score = m + logf(s) + gumbel_from_word(draw_word(key, (uint32_t)c, (uint32_t)b, (uint32_t)k, pc));
+    if (better(score, c, best, bc)) {
+      best = score;
+      bc = c;
+    }
+  }
+  if (lane == 0) {
+    s_best[wave] = best;
+    s_idx[wave] = bc;
+  }
+  __syncthreads();
+  float B0 = s_best[0];
+  int C0 = s_idx[0];
+  for (int w = 1; w < 4; ++w)
+    if (better(s_best[w], s_idx[w], B0, C0)) {
+      B0 = s_best[w];
+      C0 = s_idx[w];
+    }
+  __syncthreads();
+  float sc = -INFINITY;
+  int idx = 0x7fffffff;
+  if (tid < kChunk) {
+    const int v = C0 * kChunk + tid;
+    if (v < V) {
+      sc = logit_at<ZT>(row, v) * inv_T + gumbel_from_word(draw_word(key, (uint32_t)v, (uint32_t)b, (uint32_t)k, pe));
+      idx = v;
+    }
+  }
+  wave_argmax(sc, idx);
+  if (lane == 0) {
+    s_best[wave] = sc;
+    s_idx[wave] = idx;
+  }
+  __syncthreads();
+  float B1 = s_best[0];
+  int X = s_idx[0];
+  for (int w = 1; w < 4; ++w)
+    if (better(s_best[w], s_idx[w], B1, X)) {
+      B1 = s_best[w];
+      X = s_idx[w];
+    }
+  __syncthreads();
+  return X;
+}
+
+template <typename ZT, typename WT>
+__global__ __launch_bounds__(256) void k_finish(VerifyArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, V = a.V;
+  __shared__ float s_f[4], s_best[4];
+  __shared__ int s_idx[4];
+  __shared__ int s_y;
+  __shared__ float s_mass;
+  __shared__ int s_cstar;
+
+  // merge the partials of the resample pass
+  float mass = 0.f, best = -INFINITY;
+  int bc = 0x7fffffff;
+  for (int i = tid; i < a.G; i += 256) {
+    const float4 p = a.part[(size_t)b * a.G + i];
+    mass += p.x;
+    const int pc = __float_as_int(p.w);
+    if (better(p.z, pc, best, bc)) {
+      best = p.z;
+      bc = pc;
+    }
+  }
+  mass = wave_sum(mass);
+  wave_argmax(best, bc);
+  if (lane == 0) {
+    s_f[wave] = mass;
+    s_best[wave] = best;
+    s_idx[wave] = bc;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float Bm = s_best[0];
+    int C0 = s_idx[0];
+    for (int w = 1; w < 4; ++w)
+      if (better(s_best[w], s_idx[w], Bm, C0)) {
+        Bm = s_best[w];
+        C0 = s_idx[w];
+      }
+    s_mass = s_f[0] + s_f[1] + s_f[2] + s_f[3];
+    s_cstar = (Bm == -INFINITY) ? -1 : C0;
+  }
+  __syncthreads();
+  const int cstar = s_cstar;
+  const int kstar = a.job[b];
+  int nb = a.n_sched[b];
+  nb = nb < 0 ? 0 : (nb > K ? K : nb);
+  const ZT* Zt = static_cast<const ZT*>(a.Zt);
+
+  int y = -1;
+  if (kstar > 0) {
+    const int k0 = kstar - 1;
+    const ZT* trow = Zt + ((size_t)b * (K + 1) + k0) * V;
+    if (s_mass > 0.f && cstar >= 0) {
+      const ZT* zrow = static_cast<const ZT*>(a.Z) + ((size_t)b * K + k0) * V;
+      const int prev = clamp_id(k0 == 0 ? a.anchor[b] : a.tok[(size_t)b * K + k0 - 1], V);
+      const int j = tid >> 1, h = tid & 1;
+      const int v = cstar * kChunk + j;
+      const bool inside = v < V;
+      float dot = inside ? half_dot<WT>(static_cast<const WT*>(a.E), static_cast<const WT*>(a.Wt), prev, v, a.r, h)
+                         : 0.f;
+      dot += __shfl_xor(dot, 1);
+      float sc = -INFINITY;
+      int idx = 0x7fffffff;
+      if (h == 0 && inside) {
+        const float q = expf((logit_at<ZT>(zrow, v) + dot) * a.inv_T - a.lse_q[(size_t)b * K + k0]);
+        const float p = expf(logit_at<ZT>(trow, v) * a.inv_T - a.lse_p[(size_t)b * K + k0]);
+        const float r = fmaxf(p - q, 0.f);
+        if (r > 0.f) {
+          sc = logf(r) + gumbel_from_word(draw_word(a.key, (uint32_t)v, (uint32_t)b, (uint32_t)kstar, kResidElem));
+          idx = v;
+        }
+      }
+      wave_argmax(sc, idx);
+      if (lane == 0) {
+        s_best[wave] = sc;
+        s_idx[wave] = idx;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        float B1 = s_best[0];
+        int X = s_idx[0];
+        for (int w = 1; w < 4; ++w)
+          if (better(s_best[w], s_idx[w], B1, X)) {
+            B1 = s_best[w];
+            X = s_idx[w];
+          }
+        s_y = (B1 == -INFINITY) ? -1 : X;
+      }
+      __syncthreads();
+      y = s_y;
+    }
+    if (y < 0) y = full_row_draw<ZT>(trow, V, a.inv_T, a.key, b, kstar, kResidChunk, kResidElem, s_best, s_idx);
+  } else {
+    const ZT* trow = Zt + ((size_t)b * (K + 1) + nb) * V;
+    float sc = -INFINITY;
+    int idx = 0x7fffffff;
+    if (tid < kChunk && cstar >= 0) {
+      const int v = cstar * kChunk + tid;
+      if (v < V) {
+        sc = logit_at<ZT>(trow, v) * a.inv_T +
+             gumbel_from_word(draw_word(a.key, (uint32_t)v, (uint32_t)b, (uint32_t)(nb + 1), kBonusElem));
+        idx = v;
+      }
+    }
+    wave_argmax(sc, idx);
+    if (lane == 0) {
+      s_best[wave] = sc;
+      s_idx[wave] = idx;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float B1 = s_best[0];
+      int X = s_idx[0];
+      for (int w = 1; w < 4; ++w)
+        if (better(s_best[w], s_idx[w], B1, X)) {
+          B1 = s_best[w];
+          X = s_idx[w];
+        }
+      s_y = (B1 == -INFINITY) ? -1 : X;
+    }
+    __syncthreads();
+    y = s_y;
+    if (y < 0) y = full_row_draw<ZT>(trow, V, a.inv_T, a.key, b, nb + 1, kBonusChunk, kBonusElem, s_best, s_idx);
+  }
+
+  const int acc = kstar > 0 ? kstar - 1 : nb;
+  for (int j = tid; j <= K; j += 256) {
+    int t = -1;
+    if (j < acc) t = a.tok[(size_t)b * K + j];
+    else if (j == acc) t = y;
+    a.out_tok[(size_t)b * (K + 1) + j] = t;
+  }
+  if (tid == 0) {
+    a.n_acc[b] = acc;
+    a.next_anchor[b] = y;
+    a.resid_mass[b] = kstar > 0 ? s_mass : __int_as_float(0x7fc00000);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_verify_pre(const dspark_problem& P, const VerifyArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_rowlist, 1, kListThreads, 0, s, a.n_sched, P.B, P.K, a.rows, a.nrows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool zb = P.logits_dtype == DSPARK_BF16;
+  if (zb) hipLaunchKernelGGL(k_vlse<uint16_t>, kVlseGrid, 256, 0, s, a);
+  else hipLaunchKernelGGL(k_vlse<float>, kVlseGrid, 256, 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (zb) hipLaunchKernelGGL(k_accept<uint16_t>, P.B, 64, 0, s, a);
+  else hipLaunchKernelGGL(k_accept<float>, P.B, 64, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_finish(const dspark_problem& P, const VerifyArgs& a, hipStream_t s) {
+  const bool zb = P.logits_dtype == DSPARK_BF16, wb = P.weight_dtype == DSPARK_BF16;
+  if (zb && wb) hipLaunchKernelGGL((k_finish<uint16_t, uint16_t>), P.B, 256, 0, s, a);
+  else if (zb) hipLaunchKernelGGL((k_finish<uint16_t, float>), P.B, 256, 0, s, a);
+  else if (wb) hipLaunchKernelGGL((k_finish<float, uint16_t>), P.B, 256, 0, s, a);
+  else hipLaunchKernelGGL((k_finish<float, float>), P.B, 256, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

@@ -1,0 +1,166 @@
+"""ctypes binding of libdspark.so: same entry points as include/dspark.h.
+
+This module only marshals arguments: torch tensors supply device pointers and
+torch supplies the current HIP stream.  Every step of the cycle runs in the
+library's HIP kernels; there is no other implementation behind these calls, and
+a missing library raises instead of falling back.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdspark.so")
+
+OK, E_INVALID, E_DTYPE, E_UNSUPPORTED, E_WORKSPACE, E_POINTER, E_LAUNCH = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+_DT = {"f32": F32, "bf16": BF16}
+_TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
+
+SYMBOLS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft", "dspark_draft_timed",
+           "dspark_schedule", "dspark_verify")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
+        ("r", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("logits_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32), ("hidden_dtype", ctypes.c_int32),
+        ("sampling_temp", ctypes.c_float), ("seed", ctypes.c_uint64),
+    ]
+
+    @classmethod
+    def make(cls, B, K, V, r, d, logits="bf16", weights="bf16", hidden="bf16", T_s=1.0, seed=0) -> "Problem":
+        return cls(B, K, V, r, d, _DT[logits], _DT[weights], _DT[hidden], float(T_s), int(seed))
+
+    @classmethod
+    def from_config(cls, cfg) -> "Problem":
+        return cls.make(cfg.B, cfg.K, cfg.V, cfg.r, cfg.d, cfg.logits_dtype, cfg.weight_dtype,
+                        cfg.hidden_dtype, cfg.T_s, cfg.seed)
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libdspark.so (built by draft_sampling_verification_markov_amd.build); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                                "or python -m draft_sampling_verification_markov_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Problem)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.dspark_workspace_bytes.argtypes = [P]
+    lib.dspark_workspace_bytes.restype = sz
+    lib.dspark_status_string.argtypes = [i32]
+    lib.dspark_status_string.restype = ctypes.c_char_p
+    lib.dspark_draft.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dspark_draft.restype = i32
+    lib.dspark_draft_timed.argtypes = lib.dspark_draft.argtypes + [vp]
+    lib.dspark_draft_timed.restype = i32
+    lib.dspark_schedule.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+    lib.dspark_schedule.restype = i32
+    lib.dspark_verify.argtypes = [P] + [vp] * 14 + [vp, sz, vp]
+    lib.dspark_verify.restype = i32
+    _lib = lib
+    return lib
+
+
+def workspace_bytes(P: Problem) -> int:
+    return int(load().dspark_workspace_bytes(ctypes.byref(P)))
+
+
+def status_string(status: int) -> str:
+    return load().dspark_status_string(int(status)).decode()
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    """Device pointer of a contiguous CUDA (HIP) tensor, checking its dtype; None passes NULL."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise DsparkError(fn, status)
+
+
+def draft(P: Problem, Z, E, Wt, h, w_conf, b_conf: float, tau, anchor,
+          draft_tok, draft_logq, draft_lse, conf, surv, workspace, stream=None) -> None:
+    lt, wt, ht = _TORCH_DT[P.logits_dtype], _TORCH_DT[P.weight_dtype], _TORCH_DT[P.hidden_dtype]
+    st = load().dspark_draft(
+        ctypes.byref(P), _ptr(Z, lt, "Z"), _ptr(E, wt, "E"), _ptr(Wt, wt, "Wt"), _ptr(h, ht, "h"),
+        _ptr(w_conf, torch.float32, "w_conf"), ctypes.c_float(b_conf), _ptr(tau, torch.float32, "tau"),
+        _ptr(anchor, torch.int32, "anchor"), _ptr(draft_tok, torch.int32, "draft_tok"),
+        _ptr(draft_logq, torch.float32, "draft_logq"), _ptr(draft_lse, torch.float32, "draft_lse"),
+        _ptr(conf, torch.float32, "conf"), _ptr(surv, torch.float32, "surv"),
+        _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+        _stream(stream))
+    _check("dspark_draft", st)
+
+
+def draft_timed(P: Problem, Z, E, Wt, h, w_conf, b_conf: float, tau, anchor,
+                draft_tok, draft_logq, draft_lse, conf, surv, workspace, events, stream=None) -> None:
+    """dspark_draft recording events[2i], events[2i+1] (raw hipEvent_t handles, a ctypes
+    array of 2K c_void_p) around the stream kernel of draft step i+1."""
+    lt, wt, ht = _TORCH_DT[P.logits_dtype], _TORCH_DT[P.weight_dtype], _TORCH_DT[P.hidden_dtype]
+    st = load().dspark_draft_timed(
+        ctypes.byref(P), _ptr(Z, lt, "Z"), _ptr(E, wt, "E"), _ptr(Wt, wt, "Wt"), _ptr(h, ht, "h"),
+        _ptr(w_conf, torch.float32, "w_conf"), ctypes.c_float(b_conf), _ptr(tau, torch.float32, "tau"),
+        _ptr(anchor, torch.int32, "anchor"), _ptr(draft_tok, torch.int32, "draft_tok"),
+        _ptr(draft_logq, torch.float32, "draft_logq"), _ptr(draft_lse, torch.float32, "draft_lse"),
+        _ptr(conf, torch.float32, "conf"), _ptr(surv, torch.float32, "surv"),
+        _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+        _stream(stream), ctypes.cast(events, ctypes.c_void_p))
+    _check("dspark_draft_timed", st)
+
+
+def schedule(P: Problem, surv, T_table, n_sched, n_total, workspace, stream=None) -> None:
+    st = load().dspark_schedule(
+        ctypes.byref(P), _ptr(surv, torch.float32, "surv"), _ptr(T_table, torch.float32, "T_table"),
+        _ptr(n_sched, torch.int32, "n_sched"), _ptr(n_total, torch.int32, "n_total"),
+        _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+        _stream(stream))
+    _check("dspark_schedule", st)
+
+
+def verify(P: Problem, target, Z, E, Wt, anchor, draft_tok, draft_logq, draft_lse, n_sched,
+           out_tok, n_accepted, next_anchor, logp, resid_mass, workspace, stream=None) -> None:
+    lt, wt = _TORCH_DT[P.logits_dtype], _TORCH_DT[P.weight_dtype]
+    st = load().dspark_verify(
+        ctypes.byref(P), _ptr(target, lt, "target"), _ptr(Z, lt, "Z"), _ptr(E, wt, "E"), _ptr(Wt, wt, "Wt"),
+        _ptr(anchor, torch.int32, "anchor"), _ptr(draft_tok, torch.int32, "draft_tok"),
+        _ptr(draft_logq, torch.float32, "draft_logq"), _ptr(draft_lse, torch.float32, "draft_lse"),
+        _ptr(n_sched, torch.int32, "n_sched"), _ptr(out_tok, torch.int32, "out_tok"),
+        _ptr(n_accepted, torch.int32, "n_accepted"), _ptr(next_anchor, torch.int32, "next_anchor"),
+        _ptr(logp, torch.float32, "logp"), _ptr(resid_mass, torch.float32, "resid_mass"),
+        _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+        _stream(stream))
+    _check("dspark_verify", st)

@@ -1,0 +1,197 @@
+/*
+ * dspark.h -- C ABI of the per-cycle draft -> schedule -> verify step of
+ * confidence-scheduled speculative decoding with a Markov draft head, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of the DSpark summary page ("DSpark: semi-autoregressive
+ * generation and confidence-scheduled verification", juhoplayground.github.io):
+ *
+ *   dspark_draft    -- Method > Semi-autoregressive generation (Markov head:
+ *                      rank-r transition bias added to the backbone's base
+ *                      logits, tokens sampled position after position) and
+ *                      Method > Confidence-scheduled verification (confidence
+ *                      head, Sequential Temperature Scaling, prefix survival);
+ *   dspark_schedule -- Method > Confidence-scheduled verification (hardware-aware
+ *                      prefix scheduler against a step-time table profiled once
+ *                      at start-up; greedy in survival order, stopping at the
+ *                      first drop in throughput so that it never looks ahead);
+ *   dspark_verify   -- Overview / Background (lossless rejection-sampling
+ *                      verification of the scheduled prefix, left to right).
+ *
+ * Notation: B requests, K draft positions (k = 1..K, 1-based in the text,
+ * 0-based in memory), V vocabulary entries, r Markov rank, d hidden size,
+ * T_s the sampling temperature.  Token x_0 of request b is anchor[b]; row k of
+ * Z predicts x_k.
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ * - All array arguments are DEVICE pointers on the current HIP device, dense
+ *   and row-major as documented per argument; the problem struct is a HOST
+ *   pointer.  The caller owns every buffer (inputs, outputs, workspace); the
+ *   library allocates, frees and synchronises nothing and keeps no state
+ *   between calls, so calls can be captured in a HIP graph.  Work is enqueued
+ *   on `stream` (NULL = the default stream) and is asynchronous.
+ * - Logit, weight and hidden arrays must be 16-byte aligned; int32/float
+ *   arrays 4-byte aligned.
+ * - Validation runs on the host before anything is enqueued and returns a
+ *   non-OK status without touching any buffer.  DSPARK_E_LAUNCH means a kernel
+ *   launch was rejected by the runtime; faults inside kernels surface at the
+ *   caller's next synchronisation.  Outputs are unspecified after a non-OK
+ *   status.
+ * - Randomness: Philox4x32-10 (Salmon et al., SC'11) with key
+ *   (seed & 0xffffffff, seed >> 32) and counter (idx >> 2, b, k, purpose),
+ *   taking output word idx & 3, where b is the 0-based request, k the 1-based
+ *   position and idx a chunk id, a vocabulary id, or 0.  A word w becomes the
+ *   uniform ((w >> 8) | 1) * 2^-24 and the Gumbel -ln(-ln u).  Purposes:
+ *   1/2 draft chunk/element, 3 accept, 4/5 residual chunk/element, 6/7 bonus
+ *   chunk/element.  Tokens are drawn by two-level Gumbel-max over chunks of
+ *   128 vocabulary entries: the chunk maximising (log chunk mass + chunk
+ *   Gumbel), then the entry of that chunk maximising (log weight + entry
+ *   Gumbel); ties go to the smallest id.  Results are therefore a pure
+ *   function of (inputs, seed).
+ * - Workspace: one buffer of at least dspark_workspace_bytes(P) bytes,
+ *   256-byte aligned, shared by the three calls of a cycle (its contents need
+ *   not be initialised and carry nothing between calls).
+ *
+ * Supported shapes: 1 <= B <= 65536, 1 <= K <= 64, 8 <= V < 2^31 with
+ * V % 8 == 0, d >= 1 with d % 8 == 0, r in {16, 32, 64, 128, 256} for bf16
+ * weights and {16, 32, 64} for fp32 weights; B*K <= 2^20.  Logits (Z and the
+ * target) and h may be fp32 or bf16, independently; weights (E, Wt) fp32 or
+ * bf16.  0 < T_s finite.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_E_INVALID = -1,      /* a size or scalar is out of range (B, K, V, d, T_s, ...) */
+  DSPARK_E_DTYPE = -2,        /* a dtype code is not a dspark_dtype */
+  DSPARK_E_UNSUPPORTED = -3,  /* valid, but no kernel is built for it (e.g. r = 48) */
+  DSPARK_E_WORKSPACE = -4,    /* workspace null, misaligned or smaller than required */
+  DSPARK_E_POINTER = -5,      /* a required pointer is null or misaligned */
+  DSPARK_E_LAUNCH = -6        /* the runtime rejected a kernel launch */
+} dspark_status;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+typedef struct {
+  int32_t B, K, V, r, d;
+  int32_t logits_dtype;   /* dspark_dtype of Z and of the target logits */
+  int32_t weight_dtype;   /* dspark_dtype of E and Wt */
+  int32_t hidden_dtype;   /* dspark_dtype of h */
+  float sampling_temp;    /* T_s: q = softmax((Z + bias) / T_s), p = softmax(target / T_s) */
+  uint64_t seed;          /* Philox key */
+} dspark_problem;
+
+/* Bytes of workspace the three calls need for problem P; 0 if P is invalid.
+ * Host-only: makes no HIP call. */
+size_t dspark_workspace_bytes(const dspark_problem* P);
+
+/* Static, NUL-terminated description of a status code. */
+const char* dspark_status_string(int status);
+
+/*
+ * dspark_draft -- sequential Markov-head sampling of K draft tokens per
+ * request, then the confidence head and prefix survival.
+ *
+ * For k = 1..K, with prev = x_{k-1} (the anchor for k = 1):
+ *   ell_v  = (Z[b][k-1][v] + sum_j E[prev][j] * Wt[v][j]) / T_s
+ *   x_k    = two-level Gumbel-max draw from softmax(ell) (purposes 1/2)
+ *   lse    = log sum_v exp(ell_v);  logq = ell_{x_k} - lse
+ * then z = w_conf[0:d] . h[b][k-1] + w_conf[d:d+r] . E[x_{k-1}] + b_conf,
+ *   conf = sigmoid(z / tau[k-1]),  surv[b][k-1] = prod_{j<=k} conf[b][j-1].
+ *
+ * Inputs:  Z [B][K][V] (logits_dtype); E [V][r], Wt [V][r] (weight_dtype;
+ *          Wt is the logit projection stored vocabulary-major);
+ *          h [B][K][d] (hidden_dtype); w_conf [d + r] fp32; tau [K] fp32 (> 0);
+ *          anchor [B] int32 in [0, V).
+ * Outputs: draft_tok [B][K] int32; draft_logq, draft_lse, conf, surv [B][K] fp32
+ *          (logq and lse in nats of ell).
+ * Token ids outside [0, V) in anchor are undefined behaviour.
+ */
+dspark_status dspark_draft(const dspark_problem* P,
+                           const void* Z, const void* E, const void* Wt, const void* h,
+                           const float* w_conf, float b_conf, const float* tau,
+                           const int32_t* anchor,
+                           int32_t* draft_tok, float* draft_logq, float* draft_lse,
+                           float* conf, float* surv,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_draft_timed -- dspark_draft, plus instrumentation: events[2i] and
+ * events[2i+1] (caller-created HIP events, 2*K of them) are recorded on
+ * `stream` immediately before and after the vocabulary-stream kernel of draft
+ * step i+1, so that the caller can read that kernel's duration with
+ * hipEventElapsedTime.  Same inputs, outputs and errors as dspark_draft;
+ * DSPARK_E_POINTER if events is NULL.
+ */
+dspark_status dspark_draft_timed(const dspark_problem* P,
+                                 const void* Z, const void* E, const void* Wt, const void* h,
+                                 const float* w_conf, float b_conf, const float* tau,
+                                 const int32_t* anchor,
+                                 int32_t* draft_tok, float* draft_logq, float* draft_lse,
+                                 float* conf, float* surv,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                 hipEvent_t* events);
+
+/*
+ * dspark_schedule -- choose n_b, the number of draft positions of request b to
+ * verify.  Candidates (s = surv[b][k-1], b, k) are taken in the order (s
+ * descending, b ascending, k ascending) starting from A = B expected tokens at
+ * N = B verified positions; a candidate is taken iff
+ *   (A + s) * T_table[N] >= A * T_table[N + 1]   (then A += s, N += 1),
+ * and the pass stops at the first candidate refused.
+ *
+ * Inputs:  surv [B][K] fp32, each row non-increasing (as written by
+ *          dspark_draft; other rows give unspecified but in-bounds results);
+ *          T_table [B*(K+1) + 1] fp32, the step time with N verified positions
+ *          (any positive unit; only ratios matter).
+ * Outputs: n_sched [B] int32 in [0, K]; n_total [1] int32 = B + sum_b n_sched[b].
+ */
+dspark_status dspark_schedule(const dspark_problem* P,
+                              const float* surv, const float* T_table,
+                              int32_t* n_sched, int32_t* n_total,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_verify -- lossless rejection-sampling verification.
+ *
+ * With p_k = softmax(target[b][k-1] / T_s) and q_k the draft distribution of
+ * position k (recomputed from Z, E, Wt and draft_lse), for k = 1..n_b in order:
+ * accept x_k iff u <= min(1, p_k(x_k) / q_k(x_k)) with u the accept draw
+ * (purpose 3).  At the first rejection k*, emit y drawn from max(0, p_k* - q_k*)
+ * (purposes 4/5 at position k*; from p_k* if that mass is exactly 0) and keep
+ * x_1..x_{k*-1}; if all n_b are accepted, emit y drawn from p_{n_b+1}
+ * (purposes 6/7 at position n_b + 1) and keep x_1..x_{n_b}.
+ *
+ * Inputs:  target [B][K+1][V] (logits_dtype); Z, E, Wt, anchor as for
+ *          dspark_draft; draft_tok, draft_logq, draft_lse [B][K] as written by
+ *          dspark_draft; n_sched [B] in [0, K].
+ * Outputs: out_tok [B][K+1] int32: x_1..x_a, y, then -1;
+ *          n_accepted [B] int32 (a); next_anchor [B] int32 (y);
+ *          logp [B][K] fp32: log p_k(x_k) for k <= n_b, NaN beyond;
+ *          resid_mass [B] fp32: sum_v max(0, p_k* - q_k*) at a rejection, NaN
+ *          when the bonus path was taken.
+ */
+dspark_status dspark_verify(const dspark_problem* P,
+                            const void* target, const void* Z, const void* E, const void* Wt,
+                            const int32_t* anchor, const int32_t* draft_tok,
+                            const float* draft_logq, const float* draft_lse,
+                            const int32_t* n_sched,
+                            int32_t* out_tok, int32_t* n_accepted, int32_t* next_anchor,
+                            float* logp, float* resid_mass,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

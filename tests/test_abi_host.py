@@ -1,0 +1,136 @@
+"""Host-side checks of the C ABI: loading, exported symbols, validation and
+workspace sizing.  Validation runs before anything is enqueued, so these
+calls need no GPU; no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+
+@pytest.fixture(scope="module")
+def ds():
+    from draft_sampling_verification_markov_amd import dspark
+    if not os.path.exists(dspark.LIB_PATH):
+        from draft_sampling_verification_markov_amd import build
+        build.build()
+    dspark.load()
+    return dspark
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(["dspark_draft", "dspark_draft_timed", "dspark_schedule", "dspark_verify",
+                                  "dspark_workspace_bytes", "dspark_status_string"])
+
+
+def test_library_exports_every_declared_symbol(ds):
+    out = subprocess.run(["nm", "-D", "--defined-only", ds.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\sT\s(dspark_\w+)", out.stdout))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(ds.load(), name)
+    assert set(ds.SYMBOLS) == set(_declared())
+
+
+def test_header_compiles_as_c():
+    src = '#include "dspark.h"\nint main(void){ dspark_problem p; (void)p; return (int)sizeof(dspark_problem); }\n'
+    r = subprocess.run(["gcc", "-x", "c", "-std=c99", "-fsyntax-only", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", "-"], input=src, text=True,
+                       capture_output=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_problem_struct_layout(ds):
+    assert ctypes.sizeof(ds.Problem) == 48
+    assert ds.Problem.seed.offset == 40
+
+
+def _P(ds, **kw):
+    base = dict(B=256, K=16, V=151936, r=256, d=4096)
+    base.update(kw)
+    return ds.Problem.make(base["B"], base["K"], base["V"], base["r"], base["d"],
+                           kw.get("logits", "bf16"), kw.get("weights", "bf16"), kw.get("hidden", "bf16"),
+                           kw.get("T_s", 1.0), 0)
+
+
+def test_workspace_bytes(ds):
+    P = _P(ds)
+    n = ds.workspace_bytes(P)
+    G = 256
+    nseg = (151936 + 8191) // 8192
+    assert n >= 256 * G * 16 + 256 * 16 * nseg * 8
+    assert n % 256 == 0
+    assert ds.workspace_bytes(_P(ds, B=1024, K=32)) > n
+    assert ds.workspace_bytes(_P(ds, V=100)) == 0          # V % 8 != 0
+    assert ds.workspace_bytes(_P(ds, r=48)) == 0           # unsupported rank
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -1), (dict(K=0), -1), (dict(K=65), -1), (dict(V=4), -1), (dict(V=1004), -1),
+    (dict(d=0), -1), (dict(d=12), -1), (dict(r=0), -1), (dict(B=65537), -1), (dict(B=32768, K=64), -1),
+    (dict(T_s=0.0), -1), (dict(T_s=float("inf")), -1), (dict(T_s=float("nan")), -1),
+    (dict(r=48), -3), (dict(r=512), -3), (dict(r=128, weights="f32"), -3),
+])
+def test_draft_rejects_bad_problems(ds, kw, code):
+    lib = ds.load()
+    P = _P(ds, **kw)
+    st = lib.dspark_draft(ctypes.byref(P), *([None] * 5), ctypes.c_float(0), *([None] * 8), 0, None)
+    assert st == code, ds.status_string(st)
+
+
+def test_bad_dtype_code(ds):
+    lib = ds.load()
+    P = _P(ds)
+    P.hidden_dtype = 7
+    st = lib.dspark_schedule(ctypes.byref(P), None, None, None, None, None, 0, None)
+    assert st == ds.E_DTYPE
+
+
+def test_null_and_misaligned_pointers(ds):
+    lib = ds.load()
+    P = _P(ds, B=4, K=2, V=1024, r=32, d=64)
+    fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(14)]
+    st = lib.dspark_draft(ctypes.byref(P), None, *fake[:4], ctypes.c_float(0), *fake[4:11], None, 0, None)
+    assert st == ds.E_POINTER
+    # misaligned logits (not 16-byte aligned)
+    st = lib.dspark_draft(ctypes.byref(P), ctypes.c_void_p(0x1004), *fake[:4], ctypes.c_float(0), *fake[4:11],
+                          ctypes.c_void_p(0x10000), 1 << 20, None)
+    assert st == ds.E_POINTER
+    st = lib.dspark_verify(ctypes.byref(P), *fake[:9], None, *fake[10:14], ctypes.c_void_p(0x10000), 1 << 20, None)
+    assert st == ds.E_POINTER
+    st = lib.dspark_schedule(ctypes.byref(P), None, fake[0], fake[1], fake[2], ctypes.c_void_p(0x10000), 1 << 20,
+                             None)
+    assert st == ds.E_POINTER
+
+
+def test_workspace_checks(ds):
+    lib = ds.load()
+    P = _P(ds, B=4, K=2, V=1024, r=32, d=64)
+    need = ds.workspace_bytes(P)
+    fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(4)]
+    for ws, nbytes in ((None, need), (ctypes.c_void_p(0x10080), need), (ctypes.c_void_p(0x10000), need - 1)):
+        st = lib.dspark_schedule(ctypes.byref(P), *fake, ws, nbytes, None)
+        assert st == ds.E_WORKSPACE
+
+
+def test_status_strings(ds):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert ds.status_string(code) and ds.status_string(code) != "unknown status"
+    assert ds.status_string(42) == "unknown status"
+
+
+def test_binding_refuses_host_tensors(ds):
+    torch = pytest.importorskip("torch")
+    P = _P(ds, B=1, K=1, V=8, r=16, d=8)
+    t = torch.zeros(8)
+    with pytest.raises(ValueError, match="device"):
+        ds.schedule(P, t, t, t, t, t)
