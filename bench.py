@@ -144,6 +144,8 @@ def main() -> int:
     ap.add_argument("--config", default="high_concurrency")
     ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (scale for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this step has no multi-GPU path; "
@@ -165,6 +167,15 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_dispatch": src.numel() * 4}), flush=True)
+        return 0
 
     cfg = synth.get_config(args.config)
     P = dspark.Problem.from_config(cfg)
