@@ -21,6 +21,8 @@ Layout make_layout(const dspark_problem& P) {
   L.rows = off;   off = align_up(off + B * K * sizeof(int32_t));
   L.nrows = off;  off = align_up(off + sizeof(int32_t));
   L.sorted = off; off = align_up(off + B * K * sizeof(int32_t));
+  L.ncpad = (n_chunks(P.V) + 3) & ~3;
+  L.gum = off;    off = align_up(off + B * K * (size_t)L.ncpad * sizeof(float));
   L.total = off;
   return L;
 }
@@ -115,6 +117,8 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
   sa.nchunks = n_chunks(p.V);
   sa.scale2 = kLog2e / p.sampling_temp;
   sa.key = host_key(p.seed);
+  sa.gum = at<float>(workspace, L.gum);
+  sa.ncpad = L.ncpad;
 
   SelectArgs se{};
   se.Z = Z;
@@ -133,6 +137,9 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
   se.inv_T = 1.0f / p.sampling_temp;
   se.key = sa.key;
 
+  if (draft_uses_gumbel_table(p) &&
+      launch_chunk_gumbels(p, at<float>(workspace, L.gum), L.ncpad, sa.key, stream) != hipSuccess)
+    return DSPARK_E_LAUNCH;
   for (int k = 1; k <= p.K; ++k) {
     sa.k = k;
     se.k = k;

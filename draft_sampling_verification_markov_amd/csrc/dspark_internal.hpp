@@ -33,6 +33,8 @@ struct Layout {
   size_t rows;  // int32 [B*K]: compact list of rows to verify, b * 64 + (k - 1)
   size_t nrows; // int32 [1]
   size_t sorted;// int32 [B*K]: candidates in schedule order
+  size_t gum;   // float [B*K][ncpad]: chunk Gumbels of the draft draws
+  int ncpad;    // chunks rounded up to a multiple of 4
   size_t total;
 };
 
@@ -51,6 +53,8 @@ struct StreamArgs {
   const int32_t* job;    // [B] (verify)
   const int32_t* n_sched;// [B] (verify)
   float4* part;          // [B][G]
+  const float* gum;      // [B*K][ncpad] chunk Gumbels (draft mode, bf16 logits and factors)
+  int ncpad;
   int B, K, V, k;        // k: 1-based draft position (draft mode)
   int nchunks;
   float scale2;          // log2(e) / T_s
@@ -113,6 +117,8 @@ struct VerifyArgs {
 
 // Launchers; each returns hipSuccess or the launch error.
 hipError_t launch_stream_draft(const dspark_problem& P, const StreamArgs& a, int G, hipStream_t s);
+hipError_t launch_chunk_gumbels(const dspark_problem& P, float* gum, int ncpad, Key key, hipStream_t s);
+bool draft_uses_gumbel_table(const dspark_problem& P);
 hipError_t launch_stream_verify(const dspark_problem& P, const StreamArgs& a, int G, hipStream_t s);
 hipError_t launch_select(const dspark_problem& P, const SelectArgs& a, hipStream_t s);
 hipError_t launch_conf(const dspark_problem& P, const ConfArgs& a, hipStream_t s);

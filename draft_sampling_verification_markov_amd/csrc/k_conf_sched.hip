@@ -89,32 +89,38 @@ __global__ __launch_bounds__(256) void k_conf(ConfArgs a) {
 
 // ---------------------------------------------------------------- scheduler
 // Rank of every candidate in the order (survival desc, request asc, position
-// asc).  Rows are non-increasing, so the candidates of row b' that precede
-// (s, b, k) form a prefix of that row, found by binary search.
-__global__ __launch_bounds__(256) void k_sched_rank(const float* surv, int B, int K, int32_t* sorted) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= B * K) return;
-  const int b = i / K, k = i - b * K;
-  const float s = surv[i];
-  int rank = k;
-  for (int bp = 0; bp < B; ++bp) {
-    if (bp == b) continue;
-    const float* row = surv + (size_t)bp * K;
-    int lo = 0, hi = K;
-    if (bp < b) {
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (row[mid] >= s) lo = mid + 1; else hi = mid;
-      }
-    } else {
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (row[mid] > s) lo = mid + 1; else hi = mid;
-      }
+// asc).  With candidate index i = b*K + (k-1), candidate j precedes i iff
+// s_j > s_i, or s_j == s_i and j < i.  Each workgroup ranks 64 candidates
+// against all n, streaming the survivals through LDS in 1024-entry tiles; its
+// four waves split every tile and their counts are summed at the end.
+constexpr int kRankCands = 64;
+constexpr int kRankTile = 1024;
+
+__global__ __launch_bounds__(256) void k_sched_rank(const float* surv, int n, int32_t* sorted) {
+  __shared__ float tile[kRankTile];
+  __shared__ int cnt[4][kRankCands];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = blockIdx.x * kRankCands + lane;
+  const float si = i < n ? surv[i] : 0.f;
+  int count = 0;
+  for (int t0 = 0; t0 < n; t0 += kRankTile) {
+    __syncthreads();
+    for (int j = tid; j < kRankTile; j += 256) tile[j] = t0 + j < n ? surv[t0 + j] : -INFINITY;
+    __syncthreads();
+    const int lo = wave * (kRankTile / 4);
+    const int hi = min(lo + kRankTile / 4, n - t0);
+    for (int jj = lo; jj < hi; ++jj) {
+      const float sj = tile[jj];
+      const int j = t0 + jj;
+      count += (sj > si) || (sj == si && j < i);
     }
-    rank += lo;
   }
-  if (rank < B * K) sorted[rank] = i;
+  cnt[wave][lane] = count;
+  __syncthreads();
+  if (wave == 0 && i < n) {
+    const int rank = cnt[0][lane] + cnt[1][lane] + cnt[2][lane] + cnt[3][lane];
+    if (rank >= 0 && rank < n) sorted[rank] = i;
+  }
 }
 
 constexpr int kScanThreads = 1024;
@@ -204,7 +210,7 @@ hipError_t launch_conf(const dspark_problem& P, const ConfArgs& a, hipStream_t s
 hipError_t launch_schedule(const dspark_problem& P, const float* surv, const float* T, int32_t* n_sched,
                            int32_t* n_total, int32_t* sorted, hipStream_t s) {
   const int n = P.B * P.K;
-  hipLaunchKernelGGL(k_sched_rank, (n + 255) / 256, 256, 0, s, surv, P.B, P.K, sorted);
+  hipLaunchKernelGGL(k_sched_rank, (n + kRankCands - 1) / kRankCands, 256, 0, s, surv, n, sorted);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_sched_scan, 1, kScanThreads, 0, s, surv, T, P.B, P.K, sorted, n_sched, n_total);

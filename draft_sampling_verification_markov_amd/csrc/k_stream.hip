@@ -40,6 +40,7 @@ constexpr int kRowsPerPass = kWaves * 32;
 
 enum { MODE_DRAFT = 0, MODE_VERIFY = 1 };
 
+
 // ---------------------------------------------------------------- Markov factor fragments
 // A-operand = Wt rows of the chunk (from LDS), B-operand = E[prev] of the lane's
 // request (registers, loaded once per pass).  32x32 MFMA accumulator layout:
@@ -168,9 +169,10 @@ __device__ __forceinline__ uint32_t quad_word(const Words4& q, int s) {
   return s == 0 ? q.w[0] : s == 1 ? q.w[1] : s == 2 ? q.w[2] : q.w[3];
 }
 
-// ---------------------------------------------------------------- stream kernel
+// ---------------------------------------------------------------- stream kernel (generic: fp32 factors)
+// Single LDS buffer, logits loaded per chunk.  Serves the fp32-factor path.
 template <typename ZT, typename WT, int R, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void k_stream(StreamArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void k_stream_generic(StreamArgs a) {
   using F = Frag<WT, R>;
   using L = Logits<ZT>;
   __shared__ __attribute__((aligned(16))) WT lds[F::kLdsElems];
@@ -330,6 +332,632 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(StreamArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- stream kernel (bf16 factors)
+// Two-stage LDS pipeline over vocabulary units (one unit = 128 bytes of every
+// request's logits row in draft mode: 64 bf16 / 32 fp32 entries; 64 bytes in
+// verify mode, where a third tile carries the target row of residual requests):
+//  * every tile (logits 256 requests x unit, target likewise, Wt unit x r) is
+//    brought in by LDS DMA with coalesced 1 KB wave instructions, unit u+1
+//    streaming in while unit u is multiplied;
+//  * 16-byte slots of every LDS row are XOR-swizzled by the row index, so the
+//    A-fragment reads (32 Wt rows, same slot) and the logits reads (32
+//    requests, same slot) fall on distinct banks;
+//  * MFMA row rho of an M-tile is bound to vocabulary entry
+//    16*((rho >> 2) & 1) + 4*(rho >> 3) + (rho & 3): in the 32x32 accumulator
+//    layout lane l then holds 16 consecutive entries (16*(l/32) ... +15) of its
+//    request, reads its logits with 16-byte LDS loads, and the accumulator
+//    starts from them (D = logits + bias);
+//  * draft epilogue per unit: max, one fma into base-2 units, raw v_exp_f32,
+//    add; units merge into the chunk's (max, sum), finished chunks into the
+//    row's running log-partition and best chunk score.
+template <typename ZT, int R, int MODE>
+struct Tiles {
+  static constexpr int kZRow = MODE == MODE_DRAFT ? 128 : 64;  // bytes of one request's unit
+  static constexpr int kZSlots = kZRow / 16;
+  static constexpr int kUnit = kZRow / (int)sizeof(ZT);        // vocabulary entries per unit
+  static constexpr int kMt = kUnit / 32;                       // M-tiles per unit
+  static constexpr int kUnitsPerChunk = kChunk / kUnit;
+  static constexpr int kZBytes = kRowsPerPass * kZRow;
+  static constexpr int kTBytes = MODE == MODE_DRAFT ? 0 : kZBytes;
+  static constexpr int kWSlots = R / 8;
+  static constexpr int kWRow = R * 2;
+  static constexpr int kWBytes = kUnit * kWRow;
+  static constexpr int kStage = kZBytes + kTBytes + kWBytes;
+  static constexpr int kSteps = R / 16;
+  static constexpr int kZRowsPerBlk = 1024 / kZRow;
+
+  __device__ __forceinline__ static int z_off(int row, int s) {
+    return row * kZRow + ((s ^ (row & (kZSlots - 1))) << 4);
+  }
+  __device__ __forceinline__ static int w_off(int row, int s) {
+    return kZBytes + kTBytes + row * kWRow + ((s ^ (row & (kWSlots - 1))) << 4);
+  }
+  // DMA of the unit starting at vocabulary entry v0.  zsrc/tsrc: the row
+  // pointers of the requests whose logits (target) this lane brings in, one per
+  // block it handles (block blk = wave + j * kWaves).
+  __device__ __forceinline__ static void stage(unsigned char* buf, const ZT* const* zsrc, const ZT* const* tsrc,
+                                               const uint16_t* Wt, int V, int v0, int wave, int lane) {
+    constexpr int kPer = 16 / (int)sizeof(ZT);
+#pragma unroll
+    for (int j = 0; j < kZBytes / 1024 / kWaves; ++j) {
+      const int blk = wave + j * kWaves;
+      const int row = blk * kZRowsPerBlk + lane / kZSlots;
+      const int s = (lane % kZSlots) ^ (row & (kZSlots - 1));
+      int v = v0 + s * kPer;
+      v = v < V ? v : V - kPer;
+      __builtin_amdgcn_global_load_lds(zsrc[j] + v, (__attribute__((address_space(3))) void*)(buf + blk * 1024), 16,
+                                       0, 0);
+      if (MODE == MODE_VERIFY)
+        __builtin_amdgcn_global_load_lds(tsrc[j] + v,
+                                         (__attribute__((address_space(3))) void*)(buf + kZBytes + blk * 1024), 16, 0,
+                                         0);
+    }
+#pragma unroll
+    for (int blk = wave; blk < kWBytes / 1024; blk += kWaves) {
+      const int row = blk * (1024 / kWRow) + lane / kWSlots;
+      const int s = (lane % kWSlots) ^ (row & (kWSlots - 1));
+      int v = v0 + row;
+      v = v < V ? v : V - 1;
+      __builtin_amdgcn_global_load_lds(Wt + (size_t)v * R + s * 8,
+                                       (__attribute__((address_space(3))) void*)(buf + kZBytes + kTBytes + blk * 1024),
+                                       16, 0, 0);
+    }
+  }
+};
+
+// waits until every vector-memory operation of this wave has completed
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Tiles of the draft step (bf16 logits): per stage a logits tile (256 requests
+// x 64 entries, 128-byte rows, 16-byte slots XOR-swizzled by the row) and a Wt
+// tile (64 vocabulary rows x r) whose rows are padded to 2r + 16 bytes and
+// stored at their MFMA row: Wt row of entry mt*32 + vmap(rho) sits at LDS row
+// mt*32 + rho, so lane rho's A fragment of K-step t is at
+// base(rho) + mt*32*stride + 32*t, and 16 consecutive lanes hit 16 different
+// bank groups.  Both tiles arrive by buffer DMA with per-lane offsets that are
+// constant over the kernel plus a uniform per-unit offset.
+template <int R>
+struct DraftTiles {
+  using ZT = uint16_t;
+  static constexpr int kUnit = 64;
+  static constexpr int kMt = 2;
+  static constexpr int kZRow = 128, kZSlots = 8;
+  static constexpr int kZBytes = kRowsPerPass * kZRow;            // 32 KB
+  static constexpr int kWRow = R * 2;                               // bytes of a Wt row
+  static constexpr int kWStride = kWRow + 16;                       // padded LDS row
+  static constexpr int kWSlots = R / 8;
+  static constexpr int kWBytes = kUnit * kWStride;
+  static constexpr int kWBlocks = (kWBytes + 1023) / 1024;
+  static constexpr int kStage = (kZBytes + kWBlocks * 1024 + 1023) / 1024 * 1024;
+  static constexpr int kSteps = R / 16;
+  static constexpr int kUnitsPerChunk = 2;
+  static constexpr int kZRowsPerBlk = 1024 / kZRow;
+
+  __device__ __forceinline__ static int z_off(int row, int s) { return row * kZRow + ((s ^ (row & 7)) << 4); }
+};
+
+// MFMA row rho -> vocabulary entry within its M-tile (see the layout notes above)
+__device__ __forceinline__ int mfma_row_entry(int rho) { return ((rho >> 2) & 1) * 16 + (rho >> 3) * 4 + (rho & 3); }
+
+// Per-lane constant byte offsets of the draft DMA (logits: 4 blocks, Wt: up to 5)
+template <int R>
+struct DraftDma {
+  using T = DraftTiles<R>;
+  static constexpr int kZPer = T::kZBytes / 1024 / kWaves;        // 4
+  static constexpr int kWPer = (T::kWBlocks + kWaves - 1) / kWaves;
+  uint32_t zoff[kZPer];
+  uint32_t woff[kWPer];
+
+  __device__ __forceinline__ void init(int wave, int lane, int rows_valid, uint32_t zrow_bytes) {
+#pragma unroll
+    for (int j = 0; j < kZPer; ++j) {
+      const int blk = wave + j * kWaves;
+      int row = blk * T::kZRowsPerBlk + lane / T::kZSlots;
+      const int s = (lane % T::kZSlots) ^ (row & (T::kZSlots - 1));
+      row = row < rows_valid ? row : rows_valid - 1;
+      zoff[j] = (uint32_t)row * zrow_bytes + (uint32_t)s * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) {
+      const int blk = wave + j * kWaves;
+      const int byte = blk * 1024 + lane * 16;
+      const int lrow = byte / T::kWStride, slot = (byte % T::kWStride) / 16;
+      const bool real = slot < T::kWSlots && lrow < T::kUnit;
+      const int entry = (lrow / 32) * 32 + mfma_row_entry(lrow % 32);
+      woff[j] = real ? (uint32_t)entry * T::kWRow + (uint32_t)slot * 16 : 0u;
+    }
+  }
+  // DMA of the unit starting at entry v0 into `buf`
+  __device__ __forceinline__ void stage(unsigned char* buf, __amdgpu_buffer_rsrc_t zr, __amdgpu_buffer_rsrc_t wr, int v0,
+                                        int wave) const {
+#pragma unroll
+    for (int j = 0; j < kZPer; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          zr, (__attribute__((address_space(3))) void*)(buf + (wave + j * kWaves) * 1024), 16, (int)zoff[j],
+          v0 * 2, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) {
+      const int blk = wave + j * kWaves;
+      if (blk < T::kWBlocks)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wr, (__attribute__((address_space(3))) void*)(buf + T::kZBytes + blk * 1024), 16, (int)woff[j],
+            v0 * T::kWRow, 0, 0);
+    }
+  }
+};
+
+// 128-bit buffer descriptor over [base, base + bytes) (raw; reads past the end return 0)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+
+// 16 consecutive logits of one request from a tile row (two or four 16-byte slots)
+template <typename ZT, typename TL>
+__device__ __forceinline__ void read16(const unsigned char* tile, int row, int s0, float* o);
+
+template <typename ZT, typename TL>
+__device__ __forceinline__ void read16(const unsigned char* tile, int row, int s0, float* o) {
+  if (sizeof(ZT) == 2) {
+    const uint4 a = *reinterpret_cast<const uint4*>(tile + TL::z_off(row, s0));
+    const uint4 b = *reinterpret_cast<const uint4*>(tile + TL::z_off(row, s0 + 1));
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o[2 * i] = bf16_lo(w[i]);
+      o[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = *reinterpret_cast<const float4*>(tile + TL::z_off(row, s0 + q));
+      o[4 * q] = f.x;
+      o[4 * q + 1] = f.y;
+      o[4 * q + 2] = f.z;
+      o[4 * q + 3] = f.w;
+    }
+  }
+}
+
+template <typename ZT, int R, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void k_stream(StreamArgs a) {
+  using T = Tiles<ZT, R, MODE>;
+  constexpr int kDmaPerWave = T::kZBytes / 1024 / kWaves;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * T::kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = gridDim.x, g = blockIdx.x;
+  const int c_begin = (int)(((long long)g * a.nchunks) / G);
+  const int c_end = (int)(((long long)(g + 1) * a.nchunks) / G);
+  const int nunits = (c_end - c_begin) * T::kUnitsPerChunk;
+  const ZT* Z = static_cast<const ZT*>(a.Z);
+  const ZT* Zt = static_cast<const ZT*>(a.Zt);
+  const uint16_t* Wt = static_cast<const uint16_t*>(a.Wt);
+  const int V = a.V, K = a.K, B = a.B;
+  const float scale2 = a.scale2;
+  const int h = lane >> 5;
+  const int wrow = mfma_row_entry(lane & 31);
+
+  for (int base = 0; base < B; base += kRowsPerPass) {
+    // rows this lane brings in by DMA: the logits row seeding the accumulator
+    // (draft row k; residual base row k*; bonus target row n_b + 1) and, in
+    // verify mode, the target row of a residual
+    const ZT* zsrc[kDmaPerWave];
+    const ZT* tsrc[kDmaPerWave];
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) {
+      const int row = (wave + j * kWaves) * T::kZRowsPerBlk + lane / T::kZSlots;
+      int bb = base + row;
+      bb = bb < B ? bb : B - 1;
+      if (MODE == MODE_DRAFT) {
+        zsrc[j] = Z + ((size_t)bb * K + (a.k - 1)) * V;
+        tsrc[j] = zsrc[j];
+      } else {
+        const int ks = a.job[bb];
+        int nb = a.n_sched[bb];
+        nb = nb < 0 ? 0 : (nb > K ? K : nb);
+        if (ks > 0) {
+          zsrc[j] = Z + ((size_t)bb * K + (ks - 1)) * V;
+          tsrc[j] = Zt + ((size_t)bb * (K + 1) + (ks - 1)) * V;
+        } else {
+          zsrc[j] = Zt + ((size_t)bb * (K + 1) + nb) * V;
+          tsrc[j] = zsrc[j];
+        }
+      }
+    }
+
+    const int prow = wave * 32 + (lane & 31);
+    const int b = base + prow;
+    const bool rv = b < B;
+    const bool wave_on = base + wave * 32 < B;
+    int prev = 0, kpos = a.k;
+    uint32_t purpose = kDraftChunk;
+    bool resid = false;
+    float lsq2 = 0.f, lsp2 = 0.f;
+    if (rv) {
+      if (MODE == MODE_DRAFT) {
+        prev = clamp_id(a.k == 1 ? a.anchor[b] : a.tok[(size_t)b * K + a.k - 2], V);
+      } else {
+        const int ks = a.job[b];
+        if (ks > 0) {
+          resid = true;
+          kpos = ks;
+          purpose = kResidChunk;
+          prev = clamp_id(ks == 1 ? a.anchor[b] : a.tok[(size_t)b * K + ks - 2], V);
+          lsq2 = a.lse_q[(size_t)b * K + ks - 1] * kLog2e;
+          lsp2 = a.lse_p[(size_t)b * K + ks - 1] * kLog2e;
+        } else {
+          int nb = a.n_sched[b];
+          nb = nb < 0 ? 0 : (nb > K ? K : nb);
+          kpos = nb + 1;
+          purpose = kBonusChunk;
+        }
+      }
+    }
+    bf16x8_t bfrag[T::kSteps];
+    {
+      const bool need = rv && (MODE == MODE_DRAFT || resid);
+      const uint16_t* src = static_cast<const uint16_t*>(a.E) + (size_t)prev * R + 8 * h;
+#pragma unroll
+      for (int t = 0; t < T::kSteps; ++t)
+        bfrag[t] = need ? *reinterpret_cast<const bf16x8_t*>(src + 16 * t) : bf16x8_t{};
+    }
+
+    float run_m = -INFINITY, run_s = 0.f, best = -INFINITY, mass = 0.f;
+    int best_c = 0x7fffffff;
+    float cm = -INFINITY, cs = 0.f;  // current chunk: (max, sum) base 2, or residual sum
+    int quad_id = -1;
+    Words4 quad = {};
+
+    if (nunits > 0) T::stage(lds, zsrc, tsrc, Wt, V, c_begin * kChunk, wave, lane);
+    for (int u = 0; u < nunits; ++u) {
+      const int c = c_begin + u / T::kUnitsPerChunk;
+      const int part = u % T::kUnitsPerChunk;
+      const int v0 = c * kChunk + part * T::kUnit;
+      unsigned char* cur = lds + (u & 1) * T::kStage;
+      wait_vmem();      // this wave's DMA for unit u has landed
+      __syncthreads();  // every wave's; the other stage buffer is free again
+      if (u + 1 < nunits) {
+        const int u1 = u + 1;
+        const int v1 = (c_begin + u1 / T::kUnitsPerChunk) * kChunk + (u1 % T::kUnitsPerChunk) * T::kUnit;
+        T::stage(lds + (u1 & 1) * T::kStage, zsrc, tsrc, Wt, V, v1, wave, lane);
+      }
+      if (!wave_on) continue;
+
+      f32x16_t acc[T::kMt];
+#pragma unroll
+      for (int mt = 0; mt < T::kMt; ++mt) {
+        float z[16];
+        read16<ZT, T>(cur, prow, (mt * 32 + 16 * h) * (int)sizeof(ZT) / 16, z);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mt][i] = z[i];
+      }
+#pragma unroll
+      for (int t = 0; t < T::kSteps; ++t) {
+#pragma unroll
+        for (int mt = 0; mt < T::kMt; ++mt) {
+          const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(cur + T::w_off(mt * 32 + wrow, 2 * t + h));
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bfrag[t], acc[mt], 0, 0, 0);
+        }
+      }
+      if (!rv) continue;
+      const bool ragged = v0 + T::kUnit > V;
+
+      if (MODE == MODE_VERIFY && resid) {
+        // residual max(0, p - q) of the rejected position; q from the same tiles as the draft
+        float rs = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < T::kMt; ++mt) {
+          float tz[16];
+          read16<ZT, T>(cur + T::kZBytes, prow, (mt * 32 + 16 * h) * (int)sizeof(ZT) / 16, tz);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(tz[i], scale2, -lsp2));
+            const float q = __builtin_amdgcn_exp2f(fmaf(acc[mt][i], scale2, -lsq2));
+            const float d = fmaxf(p - q, 0.f);
+            rs += (!ragged || v0 + mt * 32 + 16 * h + i < V) ? d : 0.f;
+          }
+        }
+        cs += rs;
+      } else {
+        if (ragged) {
+#pragma unroll
+          for (int mt = 0; mt < T::kMt; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (v0 + mt * 32 + 16 * h + i >= V) acc[mt][i] = -INFINITY;
+        }
+        float m = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < T::kMt; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[mt][i]);
+        m = fmaxf(m, __shfl_xor(m, 32));
+        float s = 0.f;
+        if (m != -INFINITY) {
+          const float off = -m * scale2;
+#pragma unroll
+          for (int mt = 0; mt < T::kMt; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s += __builtin_amdgcn_exp2f(fmaf(acc[mt][i], scale2, off));
+        }
+        s += __shfl_xor(s, 32);
+        lse2_merge(cm, cs, m * scale2, s);
+      }
+      if (part == T::kUnitsPerChunk - 1) {  // chunk finished
+        if (c >> 2 != quad_id) {
+          quad = draw_quad(a.key, (uint32_t)c, (uint32_t)b, (uint32_t)kpos, purpose);
+          quad_id = c >> 2;
+        }
+        const float gum = gumbel_from_word(quad_word(quad, c & 3));
+        float score;
+        if (MODE == MODE_VERIFY && resid) {
+          const float rc = cs + __shfl_xor(cs, 32);
+          mass += rc;
+          score = rc > 0.f ? logf(rc) + gum : -INFINITY;
+        } else {
+          score = cs > 0.f ? (cm + log2f(cs)) * kLn2 + gum : -INFINITY;
+          if (MODE == MODE_DRAFT) lse2_merge(run_m, run_s, cm, cs);
+        }
+        if (score > best) {
+          best = score;
+          best_c = c;
+        }
+        cm = -INFINITY;
+        cs = 0.f;
+      }
+    }
+    __syncthreads();  // the next pass restages buffer 0
+    if (rv && lane < 32) {
+      const float4 out = MODE == MODE_DRAFT ? make_float4(run_m, run_s, best, __int_as_float(best_c))
+                                            : make_float4(mass, 0.f, best, __int_as_float(best_c));
+      a.part[(size_t)b * G + g] = out;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- draft-step kernel (bf16 logits and factors)
+// One draft step over a two-stage LDS pipeline of half chunks (DraftTiles).
+// Iteration u issues the DMA of unit u+1, the MFMA chain of unit u (into
+// accumulator set u & 1, seeded with the unit's logits) and the epilogue of
+// unit u-1 (the other set).  The two waves sharing a SIMD (w and w+4) take
+// these two independent tasks in opposite order, so one feeds the matrix pipe
+// while the other runs the VALU epilogue.  A fragments are read two K-steps
+// ahead of their MFMA.
+template <int R>
+struct DraftUnit {
+  using T = DraftTiles<R>;
+  __device__ __forceinline__ static void mma(const unsigned char* wtile, const bf16x8_t* bfrag, f32x16_t* acc) {
+    constexpr int S = T::kSteps, M = T::kMt;
+    bf16x8_t af[3][M];
+#pragma unroll
+    for (int t = 0; t < 2 && t < S; ++t)
+#pragma unroll
+      for (int mt = 0; mt < M; ++mt)
+        af[t][mt] = *reinterpret_cast<const bf16x8_t*>(wtile + mt * 32 * T::kWStride + 32 * t);
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      if (t + 2 < S) {
+#pragma unroll
+        for (int mt = 0; mt < M; ++mt)
+          af[(t + 2) % 3][mt] = *reinterpret_cast<const bf16x8_t*>(wtile + mt * 32 * T::kWStride + 32 * (t + 2));
+      }
+#pragma unroll
+      for (int mt = 0; mt < M; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t % 3][mt], bfrag[t], acc[mt], 0, 0, 0);
+    }
+  }
+  // accumulator <- this lane's 16 + 16 consecutive logits (entries 16h + [0,16) of each M-tile)
+  __device__ __forceinline__ static void seed(const unsigned char* buf, f32x16_t* acc, int prow, int h) {
+#pragma unroll
+    for (int mt = 0; mt < T::kMt; ++mt) {
+      const int s0 = (mt * 32 + 16 * h) * 2 / 16;
+      const uint4 x = *reinterpret_cast<const uint4*>(buf + T::z_off(prow, s0));
+      const uint4 y = *reinterpret_cast<const uint4*>(buf + T::z_off(prow, s0 + 1));
+      const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc[mt][2 * i] = bf16_lo(w[i]);
+        acc[mt][2 * i + 1] = bf16_hi(w[i]);
+      }
+    }
+  }
+};
+
+// (max, sum) merge in base 2 without branches (an empty side contributes 0)
+__device__ __forceinline__ void lse2_merge_nb(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  const float a = m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f(m - mn);
+  const float c = m2 == -INFINITY ? 0.f : s2 * __builtin_amdgcn_exp2f(m2 - mn);
+  s = a + c;
+  m = mn;
+}
+
+struct DraftRowState {
+  float run_m, run_s, best, cm, cs;
+  int best_c;
+};
+
+// epilogue of one half chunk, branch-free; LAST closes chunk c (Gumbel from the table)
+template <typename T, bool LAST>
+__device__ __forceinline__ void draft_half(const f32x16_t* acc, DraftRowState& st, int c, float scale2,
+                                           const float* grow) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < T::kMt; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[mt][i]);
+  m = fmaxf(m, __shfl_xor(m, 32));
+  const float off = m == -INFINITY ? 0.f : -m * scale2;
+  float s = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < T::kMt; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += __builtin_amdgcn_exp2f(fmaf(acc[mt][i], scale2, off));
+  s += __shfl_xor(s, 32);
+  lse2_merge_nb(st.cm, st.cs, m * scale2, s);
+  if (LAST) {
+    const float score = st.cs > 0.f ? (st.cm + __log2f(st.cs)) * kLn2 + grow[c] : -INFINITY;
+    lse2_merge_nb(st.run_m, st.run_s, st.cm, st.cs);
+    const bool take = score > st.best;
+    st.best = take ? score : st.best;
+    st.best_c = take ? c : st.best_c;
+    st.cm = -INFINITY;
+    st.cs = 0.f;
+  }
+}
+
+// Ragged tail of the vocabulary: logits of entries >= V become -inf (Wt rows
+// past V already read as zero through the buffer bound).  Final unit(s) only.
+template <typename T>
+__device__ __forceinline__ void mask_tail(unsigned char* buf, int v0, int V, int tid) {
+  const int nvalid = V - v0;
+  for (int e = tid; e < kRowsPerPass * T::kUnit; e += kThreads) {
+    const int row = e / T::kUnit, col = e % T::kUnit;
+    if (col >= nvalid) reinterpret_cast<uint16_t*>(buf + T::z_off(row, col / 8))[col % 8] = 0xFF80u;  // -inf
+  }
+}
+
+template <int R>
+__global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
+  using T = DraftTiles<R>;
+  using D = DraftUnit<R>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * T::kStage];
+  unsigned char* const buf0 = lds;
+  unsigned char* const buf1 = lds + T::kStage;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = gridDim.x, g = blockIdx.x;
+  const int c_begin = (int)(((long long)g * a.nchunks) / G);
+  const int c_end = (int)(((long long)(g + 1) * a.nchunks) / G);
+  const int nc = c_end - c_begin;
+  const uint16_t* Z = static_cast<const uint16_t*>(a.Z);
+  const int V = a.V, K = a.K, B = a.B, k = a.k;
+  const float scale2 = a.scale2;
+  const int h = lane >> 5;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.Wt, (uint32_t)((size_t)V * T::kWRow));
+  const uint32_t zrow_bytes = (uint32_t)((size_t)K * V * 2);
+  // this lane's A-fragment base in a Wt tile: LDS row (lane & 31) of M-tile 0, slot h
+  const int abase = T::kZBytes + (lane & 31) * T::kWStride + 16 * h;
+
+  for (int base = 0; base < B; base += kRowsPerPass) {
+    const int rows_valid = B - base < kRowsPerPass ? B - base : kRowsPerPass;
+    const __amdgpu_buffer_rsrc_t zr =
+        make_rsrc(Z + ((size_t)base * K + (k - 1)) * V, (uint32_t)((size_t)(rows_valid - 1) * zrow_bytes + (size_t)V * 2));
+    DraftDma<R> dma;
+    dma.init(wave, lane, rows_valid, zrow_bytes);
+    const int prow = wave * 32 + (lane & 31);
+    const int b = base + prow;
+    const bool rv = b < B;
+    const float* grow = a.gum + ((size_t)(rv ? b : B - 1) * K + (k - 1)) * a.ncpad;
+    bf16x8_t bfrag[T::kSteps];
+    {
+      const int prev = rv ? clamp_id(k == 1 ? a.anchor[b] : a.tok[(size_t)b * K + k - 2], V) : 0;
+      const uint16_t* src = static_cast<const uint16_t*>(a.E) + (size_t)prev * R + 8 * h;
+#pragma unroll
+      for (int t = 0; t < T::kSteps; ++t)
+        bfrag[t] = rv ? *reinterpret_cast<const bf16x8_t*>(src + 16 * t) : bf16x8_t{};
+    }
+    DraftRowState st;
+    st.run_m = -INFINITY;
+    st.run_s = 0.f;
+    st.best = -INFINITY;
+    st.cm = -INFINITY;
+    st.cs = 0.f;
+    st.best_c = 0x7fffffff;
+
+    f32x16_t acc0[T::kMt], acc1[T::kMt];
+    const int vb = c_begin * kChunk;
+    // chunk c_begin: first half (nothing pending yet), then second half
+    dma.stage(buf0, zr, wr, vb, wave);
+    wait_vmem();
+    __syncthreads();
+    dma.stage(buf1, zr, wr, vb + T::kUnit, wave);
+    if (vb + T::kUnit > V) {
+      mask_tail<T>(buf0, vb, V, tid);
+      __syncthreads();
+    }
+    D::seed(buf0, acc0, prow, h);
+    D::mma(buf0 + abase, bfrag, acc0);
+    wait_vmem();
+    __syncthreads();
+    if (nc > 1) dma.stage(buf0, zr, wr, vb + kChunk, wave);
+    if (vb + 2 * T::kUnit > V) {
+      mask_tail<T>(buf1, vb + T::kUnit, V, tid);
+      __syncthreads();
+    }
+    D::seed(buf1, acc1, prow, h);
+    D::mma(buf1 + abase, bfrag, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    draft_half<T, false>(acc0, st, c_begin, scale2, grow);
+    for (int j = 1; j < nc; ++j) {
+      const int c = c_begin + j;
+      const int v0 = c * kChunk;
+      // unit 2j (first half of chunk c) from buf0, with the epilogue closing chunk c-1
+      wait_vmem();
+      __syncthreads();
+      dma.stage(buf1, zr, wr, v0 + T::kUnit, wave);
+      if (v0 + T::kUnit > V) {
+        mask_tail<T>(buf0, v0, V, tid);
+        __syncthreads();
+      }
+      if (wave & 4) {  // the partner wave on this SIMD runs the other order: MFMA and VALU overlap
+        draft_half<T, true>(acc1, st, c - 1, scale2, grow);
+        __builtin_amdgcn_sched_barrier(0);
+        D::seed(buf0, acc0, prow, h);
+        D::mma(buf0 + abase, bfrag, acc0);
+      } else {
+        D::seed(buf0, acc0, prow, h);
+        D::mma(buf0 + abase, bfrag, acc0);
+        __builtin_amdgcn_sched_barrier(0);
+        draft_half<T, true>(acc1, st, c - 1, scale2, grow);
+      }
+      // unit 2j+1 (second half of chunk c) from buf1, with the epilogue of unit 2j
+      wait_vmem();
+      __syncthreads();
+      if (j + 1 < nc) dma.stage(buf0, zr, wr, v0 + kChunk, wave);
+      if (v0 + 2 * T::kUnit > V) {
+        mask_tail<T>(buf1, v0 + T::kUnit, V, tid);
+        __syncthreads();
+      }
+      if (wave & 4) {
+        draft_half<T, false>(acc0, st, c, scale2, grow);
+        __builtin_amdgcn_sched_barrier(0);
+        D::seed(buf1, acc1, prow, h);
+        D::mma(buf1 + abase, bfrag, acc1);
+      } else {
+        D::seed(buf1, acc1, prow, h);
+        D::mma(buf1 + abase, bfrag, acc1);
+        __builtin_amdgcn_sched_barrier(0);
+        draft_half<T, false>(acc0, st, c, scale2, grow);
+      }
+    }
+    draft_half<T, true>(acc1, st, c_end - 1, scale2, grow);
+    __syncthreads();  // the next pass restages buf0
+    if (rv && lane < 32) a.part[(size_t)b * G + g] = make_float4(st.run_m, st.run_s, st.best, __int_as_float(st.best_c));
+  }
+}
+
+// ---------------------------------------------------------------- chunk Gumbels
+// All chunk-level Gumbels of the K draft steps, one Philox call per (request,
+// position, 4 chunks): G[b][k-1][c] = Gumbel of draw (c, b, k, purpose 1).
+__global__ __launch_bounds__(256) void k_chunk_gumbels(float* gum, int B, int K, int nc, int ncpad, Key key) {
+  const int nq = ncpad >> 2;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)B * K * nq) return;
+  const int q = (int)(i % nq);
+  const int row = (int)(i / nq);  // b * K + (k - 1)
+  const int b = row / K, k = row - b * K + 1;
+  const Words4 w = draw_quad(key, (uint32_t)(q * 4), (uint32_t)b, (uint32_t)k, kDraftChunk);
+  float4 g;
+  g.x = gumbel_from_word(w.w[0]);
+  g.y = gumbel_from_word(w.w[1]);
+  g.z = gumbel_from_word(w.w[2]);
+  g.w = gumbel_from_word(w.w[3]);
+  (void)nc;
+  reinterpret_cast<float4*>(gum + (size_t)row * ncpad)[q] = g;
+}
+
 // ---------------------------------------------------------------- select kernel
 template <typename ZT, typename WT>
 __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
@@ -427,35 +1055,83 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
 }  // namespace
 
 // ---------------------------------------------------------------- dispatch
-#define DSPARK_R_CASES_BF16(ZT, MODE)                                                            \
+#define DSPARK_R_CASES_BF16(ZT, MODE)                                                   \
+  switch (P.r) {                                                                        \
+    case 16: hipLaunchKernelGGL((k_stream<ZT, 16, MODE>), G, kThreads, 0, s, a); break;   \
+    case 32: hipLaunchKernelGGL((k_stream<ZT, 32, MODE>), G, kThreads, 0, s, a); break;   \
+    case 64: hipLaunchKernelGGL((k_stream<ZT, 64, MODE>), G, kThreads, 0, s, a); break;   \
+    case 128: hipLaunchKernelGGL((k_stream<ZT, 128, MODE>), G, kThreads, 0, s, a); break; \
+    case 256: hipLaunchKernelGGL((k_stream<ZT, 256, MODE>), G, kThreads, 0, s, a); break; \
+    default: return hipErrorInvalidValue;                                               \
+  }
+#define DSPARK_R_CASES_DRAFT16                                                         \
+  switch (P.r) {                                                                       \
+    case 16: hipLaunchKernelGGL((k_draft<16>), G, kThreads, 0, s, a); break;             \
+    case 32: hipLaunchKernelGGL((k_draft<32>), G, kThreads, 0, s, a); break;             \
+    case 64: hipLaunchKernelGGL((k_draft<64>), G, kThreads, 0, s, a); break;             \
+    case 128: hipLaunchKernelGGL((k_draft<128>), G, kThreads, 0, s, a); break;           \
+    case 256: hipLaunchKernelGGL((k_draft<256>), G, kThreads, 0, s, a); break;           \
+    default: return hipErrorInvalidValue;                                              \
+  }
+#define DSPARK_R_CASES_GENERIC(ZT, WT, MODE)                                                      \
   switch (P.r) {                                                                                 \
-    case 16: hipLaunchKernelGGL((k_stream<ZT, uint16_t, 16, MODE>), G, kThreads, 0, s, a); break;   \
-    case 32: hipLaunchKernelGGL((k_stream<ZT, uint16_t, 32, MODE>), G, kThreads, 0, s, a); break;   \
-    case 64: hipLaunchKernelGGL((k_stream<ZT, uint16_t, 64, MODE>), G, kThreads, 0, s, a); break;   \
-    case 128: hipLaunchKernelGGL((k_stream<ZT, uint16_t, 128, MODE>), G, kThreads, 0, s, a); break; \
-    case 256: hipLaunchKernelGGL((k_stream<ZT, uint16_t, 256, MODE>), G, kThreads, 0, s, a); break; \
+    case 16: hipLaunchKernelGGL((k_stream_generic<ZT, WT, 16, MODE>), G, kThreads, 0, s, a); break;   \
+    case 32: hipLaunchKernelGGL((k_stream_generic<ZT, WT, 32, MODE>), G, kThreads, 0, s, a); break;   \
+    case 64: hipLaunchKernelGGL((k_stream_generic<ZT, WT, 64, MODE>), G, kThreads, 0, s, a); break;   \
+    case 128: hipLaunchKernelGGL((k_stream_generic<ZT, WT, 128, MODE>), G, kThreads, 0, s, a); break; \
+    case 256: hipLaunchKernelGGL((k_stream_generic<ZT, WT, 256, MODE>), G, kThreads, 0, s, a); break; \
     default: return hipErrorInvalidValue;                                                        \
   }
-#define DSPARK_R_CASES_F32(ZT, MODE)                                                         \
-  switch (P.r) {                                                                             \
-    case 16: hipLaunchKernelGGL((k_stream<ZT, float, 16, MODE>), G, kThreads, 0, s, a); break; \
-    case 32: hipLaunchKernelGGL((k_stream<ZT, float, 32, MODE>), G, kThreads, 0, s, a); break; \
-    case 64: hipLaunchKernelGGL((k_stream<ZT, float, 64, MODE>), G, kThreads, 0, s, a); break; \
-    default: return hipErrorInvalidValue;                                                    \
+
+#define DSPARK_R_CASES_F32W(ZT, MODE)                                                                \
+  switch (P.r) {                                                                                     \
+    case 16: hipLaunchKernelGGL((k_stream_generic<ZT, float, 16, MODE>), G, kThreads, 0, s, a); break; \
+    case 32: hipLaunchKernelGGL((k_stream_generic<ZT, float, 32, MODE>), G, kThreads, 0, s, a); break; \
+    case 64: hipLaunchKernelGGL((k_stream_generic<ZT, float, 64, MODE>), G, kThreads, 0, s, a); break; \
+    default: return hipErrorInvalidValue;                                                            \
   }
 
+// bf16 factors: the LDS-pipelined kernel (fp32 logits in verify mode would need
+// 160 KB of LDS per two stages and use the generic kernel); fp32 factors: generic.
 template <int MODE>
 static hipError_t launch_stream(const dspark_problem& P, const StreamArgs& a, int G, hipStream_t s) {
   const bool zb = P.logits_dtype == DSPARK_BF16, wb = P.weight_dtype == DSPARK_BF16;
-  if (zb && wb) {
-    DSPARK_R_CASES_BF16(uint16_t, MODE)
-  } else if (zb && !wb) {
-    DSPARK_R_CASES_F32(uint16_t, MODE)
-  } else if (!zb && wb) {
-    DSPARK_R_CASES_BF16(float, MODE)
+  // the buffer-descriptor draft kernel addresses a pass of 256 logits rows with
+  // 32-bit offsets: (255 * K + 1) * V * 2 bytes must stay below 2^32
+  const bool offsets32 = ((unsigned long long)(kRowsPerPass - 1) * P.K + 1) * (unsigned long long)P.V * 2ull <
+                         (1ull << 32);
+  if (wb && MODE == MODE_DRAFT) {
+    if (zb && offsets32) {
+      DSPARK_R_CASES_DRAFT16
+    } else if (zb) {
+      DSPARK_R_CASES_BF16(uint16_t, MODE_DRAFT)
+    } else {
+      DSPARK_R_CASES_BF16(float, MODE_DRAFT)
+    }
+  } else if (wb) {
+    if (zb) {
+      DSPARK_R_CASES_BF16(uint16_t, MODE_VERIFY)
+    } else {
+      DSPARK_R_CASES_GENERIC(float, uint16_t, MODE_VERIFY)
+    }
   } else {
-    DSPARK_R_CASES_F32(float, MODE)
+    if (zb) {
+      DSPARK_R_CASES_F32W(uint16_t, MODE)
+    } else {
+      DSPARK_R_CASES_F32W(float, MODE)
+    }
   }
+  return hipGetLastError();
+}
+
+bool draft_uses_gumbel_table(const dspark_problem& P) {
+  return P.logits_dtype == DSPARK_BF16 && P.weight_dtype == DSPARK_BF16;
+}
+
+hipError_t launch_chunk_gumbels(const dspark_problem& P, float* gum, int ncpad, Key key, hipStream_t s) {
+  const long long n = (long long)P.B * P.K * (ncpad / 4);
+  hipLaunchKernelGGL(k_chunk_gumbels, (unsigned)((n + 255) / 256), 256, 0, s, gum, P.B, P.K, n_chunks(P.V), ncpad,
+                     key);
   return hipGetLastError();
 }
 
