@@ -21,8 +21,7 @@ Layout make_layout(const dspark_problem& P) {
   L.rows = off;   off = align_up(off + B * K * sizeof(int32_t));
   L.nrows = off;  off = align_up(off + sizeof(int32_t));
   L.sorted = off; off = align_up(off + B * K * sizeof(int32_t));
-  L.ncpad = (n_chunks(P.V) + 3) & ~3;
-  L.gum = off;    off = align_up(off + B * K * (size_t)L.ncpad * sizeof(float));
+  L.efrag = off;  off = align_up(off + (size_t)((B + 31) / 32) * 32 * (size_t)P.r * 2);
   L.total = off;
   return L;
 }
@@ -117,8 +116,9 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
   sa.nchunks = n_chunks(p.V);
   sa.scale2 = kLog2e / p.sampling_temp;
   sa.key = host_key(p.seed);
-  sa.gum = at<float>(workspace, L.gum);
-  sa.ncpad = L.ncpad;
+  uint4* const efrag = at<uint4>(workspace, L.efrag);
+  const bool use_efrag = draft_uses_efrag(p);
+  sa.efrag = efrag;
 
   SelectArgs se{};
   se.Z = Z;
@@ -137,12 +137,11 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
   se.inv_T = 1.0f / p.sampling_temp;
   se.key = sa.key;
 
-  if (draft_uses_gumbel_table(p) &&
-      launch_chunk_gumbels(p, at<float>(workspace, L.gum), L.ncpad, sa.key, stream) != hipSuccess)
-    return DSPARK_E_LAUNCH;
+  if (use_efrag && launch_efrag_gather(p, E, anchor, efrag, stream) != hipSuccess) return DSPARK_E_LAUNCH;
   for (int k = 1; k <= p.K; ++k) {
     sa.k = k;
     se.k = k;
+    se.efrag = use_efrag && k < p.K ? efrag : nullptr;  // fragments of position k feed step k + 1
     if (events && hipEventRecord(events[2 * (k - 1)], stream) != hipSuccess) return DSPARK_E_LAUNCH;
     if (launch_stream_draft(p, sa, L.G, stream) != hipSuccess) return DSPARK_E_LAUNCH;
     if (events && hipEventRecord(events[2 * (k - 1) + 1], stream) != hipSuccess) return DSPARK_E_LAUNCH;

@@ -100,6 +100,16 @@ __device__ __forceinline__ bool better(float s, int i, float best, int best_i) {
   return s > best || (s == best && i < best_i);
 }
 
+// The two half-wave values of x seen from any lane: {x[l & 31], x[(l & 31) + 32]}.
+// One VALU lane swap (gfx950), no trip through the LDS crossbar; both halves
+// receive the operands in the same order, so a combination is bitwise equal.
+__device__ __forceinline__ float2 halves32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves32_max(float x) { const float2 h = halves32(x); return fmaxf(h.x, h.y); }
+__device__ __forceinline__ float halves32_sum(float x) { const float2 h = halves32(x); return h.x + h.y; }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -33,8 +33,7 @@ struct Layout {
   size_t rows;  // int32 [B*K]: compact list of rows to verify, b * 64 + (k - 1)
   size_t nrows; // int32 [1]
   size_t sorted;// int32 [B*K]: candidates in schedule order
-  size_t gum;   // float [B*K][ncpad]: chunk Gumbels of the draft draws
-  int ncpad;    // chunks rounded up to a multiple of 4
+  size_t efrag; // uint4 [ceil(B/32)][r/16][64]: E rows of the previous draft tokens, B-fragment order
   size_t total;
 };
 
@@ -53,8 +52,7 @@ struct StreamArgs {
   const int32_t* job;    // [B] (verify)
   const int32_t* n_sched;// [B] (verify)
   float4* part;          // [B][G]
-  const float* gum;      // [B*K][ncpad] chunk Gumbels (draft mode, bf16 logits and factors)
-  int ncpad;
+  const uint4* efrag;    // B fragments of the previous tokens (draft kernel with bf16 logits and factors)
   int B, K, V, k;        // k: 1-based draft position (draft mode)
   int nchunks;
   float scale2;          // log2(e) / T_s
@@ -70,6 +68,7 @@ struct SelectArgs {
   float* logq;
   float* lse;
   const float4* part;
+  uint4* efrag;          // if set, the chosen token's E row is stored there in B-fragment order
   int B, K, V, r, k, G;
   float inv_T;
   Key key;
@@ -117,8 +116,12 @@ struct VerifyArgs {
 
 // Launchers; each returns hipSuccess or the launch error.
 hipError_t launch_stream_draft(const dspark_problem& P, const StreamArgs& a, int G, hipStream_t s);
-hipError_t launch_chunk_gumbels(const dspark_problem& P, float* gum, int ncpad, Key key, hipStream_t s);
-bool draft_uses_gumbel_table(const dspark_problem& P);
+// true when the draft step runs the buffer-DMA kernel, which takes its B
+// fragments from the efrag region (filled by launch_efrag_gather for the
+// anchors and by the select kernel for later positions)
+bool draft_uses_efrag(const dspark_problem& P);
+hipError_t launch_efrag_gather(const dspark_problem& P, const void* E, const int32_t* tok, uint4* efrag,
+                               hipStream_t s);
 hipError_t launch_stream_verify(const dspark_problem& P, const StreamArgs& a, int G, hipStream_t s);
 hipError_t launch_select(const dspark_problem& P, const SelectArgs& a, hipStream_t s);
 hipError_t launch_conf(const dspark_problem& P, const ConfArgs& a, hipStream_t s);

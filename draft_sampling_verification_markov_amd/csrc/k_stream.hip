@@ -407,6 +407,19 @@ struct Tiles {
 
 // waits until every vector-memory operation of this wave has completed
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Workgroup barrier ordering LDS only: this wave's LDS operations complete
+// first; vector-memory operations (LDS DMA included) are the caller's to wait
+// for.  __syncthreads() carries a release fence that drains every load of the
+// wave, prefetches meant to stay in flight included.  The memory clobber keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds_only() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order), lgkm and export counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // Tiles of the draft step (bf16 logits): per stage a logits tile (256 requests
 // x 64 entries, 128-byte rows, 16-byte slots XOR-swizzled by the row) and a Wt
@@ -428,7 +441,9 @@ struct DraftTiles {
   static constexpr int kWSlots = R / 8;
   static constexpr int kWBytes = kUnit * kWStride;
   static constexpr int kWBlocks = (kWBytes + 1023) / 1024;
-  static constexpr int kStage = (kZBytes + kWBlocks * 1024 + 1023) / 1024 * 1024;
+  // 1 KB sink after the tiles: target of the filler DMA slots (never read)
+  static constexpr int kSink = kZBytes + kWBlocks * 1024;
+  static constexpr int kStage = kSink + 1024;
   static constexpr int kSteps = R / 16;
   static constexpr int kUnitsPerChunk = 2;
   static constexpr int kZRowsPerBlk = 1024 / kZRow;
@@ -439,7 +454,11 @@ struct DraftTiles {
 // MFMA row rho -> vocabulary entry within its M-tile (see the layout notes above)
 __device__ __forceinline__ int mfma_row_entry(int rho) { return ((rho >> 2) & 1) * 16 + (rho >> 3) * 4 + (rho & 3); }
 
-// Per-lane constant byte offsets of the draft DMA (logits: 4 blocks, Wt: up to 5)
+// Per-lane constant byte offsets of the draft DMA (logits: 4 blocks, Wt: up to 5).
+// Every wave issues the same number of DMA instructions per stage, so that the
+// vector-memory counter means the same on every wave and the compiler's own
+// wait accounting stays exact: slots past the Wt tile read past the end of the
+// buffer (the bounds check returns zeros without a memory access) into the sink.
 template <int R>
 struct DraftDma {
   using T = DraftTiles<R>;
@@ -464,9 +483,13 @@ struct DraftDma {
       const int lrow = byte / T::kWStride, slot = (byte % T::kWStride) / 16;
       const bool real = slot < T::kWSlots && lrow < T::kUnit;
       const int entry = (lrow / 32) * 32 + mfma_row_entry(lrow % 32);
-      woff[j] = real ? (uint32_t)entry * T::kWRow + (uint32_t)slot * 16 : 0u;
+      woff[j] = blk >= T::kWBlocks ? kOutOfRange : real ? (uint32_t)entry * T::kWRow + (uint32_t)slot * 16 : 0u;
     }
   }
+  static constexpr uint32_t kOutOfRange = 0x80000000u;  // beyond any Wt buffer (V * r * 2 < 2^31)
+  static constexpr int kOps = kZPer + kWPer;              // DMA instructions per wave and stage
+  // wait until only the most recent stage() of this wave is still in flight
+  __device__ __forceinline__ static void wait_all_but_last_stage() { wait_vmem_n<kOps>(); }
   // DMA of the unit starting at entry v0 into `buf`
   __device__ __forceinline__ void stage(unsigned char* buf, __amdgpu_buffer_rsrc_t zr, __amdgpu_buffer_rsrc_t wr, int v0,
                                         int wave) const {
@@ -478,10 +501,9 @@ struct DraftDma {
 #pragma unroll
     for (int j = 0; j < kWPer; ++j) {
       const int blk = wave + j * kWaves;
-      if (blk < T::kWBlocks)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            wr, (__attribute__((address_space(3))) void*)(buf + T::kZBytes + blk * 1024), 16, (int)woff[j],
-            v0 * T::kWRow, 0, 0);
+      const int dst = blk < T::kWBlocks ? T::kZBytes + blk * 1024 : T::kSink;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(buf + dst), 16,
+                                               (int)woff[j], v0 * T::kWRow, 0, 0);
     }
   }
 };
@@ -778,26 +800,27 @@ struct DraftRowState {
   int best_c;
 };
 
-// epilogue of one half chunk, branch-free; LAST closes chunk c (Gumbel from the table)
+// epilogue of one half chunk, branch-free; LAST closes chunk c, whose chunk
+// Gumbel gc was read from the table one iteration earlier (a table read next
+// to its use would wait on every DMA issued before it)
 template <typename T, bool LAST>
-__device__ __forceinline__ void draft_half(const f32x16_t* acc, DraftRowState& st, int c, float scale2,
-                                           const float* grow) {
+__device__ __forceinline__ void draft_half(const f32x16_t* acc, DraftRowState& st, int c, float scale2, float gc) {
   float m = -INFINITY;
 #pragma unroll
   for (int mt = 0; mt < T::kMt; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[mt][i]);
-  m = fmaxf(m, __shfl_xor(m, 32));
+  m = halves32_max(m);
   const float off = m == -INFINITY ? 0.f : -m * scale2;
   float s = 0.f;
 #pragma unroll
   for (int mt = 0; mt < T::kMt; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += __builtin_amdgcn_exp2f(fmaf(acc[mt][i], scale2, off));
-  s += __shfl_xor(s, 32);
+  s = halves32_sum(s);
   lse2_merge_nb(st.cm, st.cs, m * scale2, s);
   if (LAST) {
-    const float score = st.cs > 0.f ? (st.cm + __log2f(st.cs)) * kLn2 + grow[c] : -INFINITY;
+    const float score = st.cs > 0.f ? (st.cm + __log2f(st.cs)) * kLn2 + gc : -INFINITY;
     lse2_merge_nb(st.run_m, st.run_s, st.cm, st.cs);
     const bool take = score > st.best;
     st.best = take ? score : st.best;
@@ -818,13 +841,37 @@ __device__ __forceinline__ void mask_tail(unsigned char* buf, int v0, int V, int
   }
 }
 
+// Chunk Gumbels of one row, one Philox quad per four consecutive chunks: the
+// two half-waves holding the row each evaluate two of the four Gumbels and
+// swap them.  The quad index is wave-uniform, so the refill branch is scalar.
+struct ChunkGumbels {
+  int quad = -1;
+  float g[4];
+  __device__ __forceinline__ float get(Key key, int b, int k, int c, int h) {
+    if ((c >> 2) != quad) {
+      quad = c >> 2;
+      const Words4 w = draw_quad(key, (uint32_t)(quad * 4), (uint32_t)b, (uint32_t)k, kDraftChunk);
+      const float x0 = gumbel_from_word(h ? w.w[2] : w.w[0]);
+      const float x1 = gumbel_from_word(h ? w.w[3] : w.w[1]);
+      const float2 e0 = halves32(x0), e1 = halves32(x1);
+      g[0] = e0.x;
+      g[1] = e1.x;
+      g[2] = e0.y;
+      g[3] = e1.y;
+    }
+    const int i = c & 3;
+    return i == 0 ? g[0] : i == 1 ? g[1] : i == 2 ? g[2] : g[3];
+  }
+};
+
 template <int R>
 __global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
   using T = DraftTiles<R>;
   using D = DraftUnit<R>;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * T::kStage];
-  unsigned char* const buf0 = lds;
-  unsigned char* const buf1 = lds + T::kStage;
+  // Two distinct LDS objects: the compiler gives them separate alias scopes, so
+  // reads of one stage need not wait for the DMA still landing in the other.
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[T::kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[T::kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x, g = blockIdx.x;
@@ -849,15 +896,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
     const int prow = wave * 32 + (lane & 31);
     const int b = base + prow;
     const bool rv = b < B;
-    const float* grow = a.gum + ((size_t)(rv ? b : B - 1) * K + (k - 1)) * a.ncpad;
+    const int vb = c_begin * kChunk;
+    // Fill: the first unit's tiles, this wave's B fragments (the E rows of the
+    // previous tokens, stored in fragment order so that each K-step is one
+    // contiguous 1 KB block), then the second unit's tiles.  Compute starts
+    // when all but the second unit have landed; the first chunk Gumbels are
+    // drawn in the meantime.
+    dma.stage(buf0, zr, wr, vb, wave);
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8_t bfrag[T::kSteps];
     {
-      const int prev = rv ? clamp_id(k == 1 ? a.anchor[b] : a.tok[(size_t)b * K + k - 2], V) : 0;
-      const uint16_t* src = static_cast<const uint16_t*>(a.E) + (size_t)prev * R + 8 * h;
+      const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(a.efrag) + (size_t)((base >> 5) + wave) * T::kSteps * 64 + lane;
 #pragma unroll
-      for (int t = 0; t < T::kSteps; ++t)
-        bfrag[t] = rv ? *reinterpret_cast<const bf16x8_t*>(src + 16 * t) : bf16x8_t{};
+      for (int t = 0; t < T::kSteps; ++t) bfrag[t] = src[t * 64];
+#pragma unroll
+      for (int t = 0; t < T::kSteps; ++t) bfrag[t] = rv ? bfrag[t] : bf16x8_t{};  // rows past B: slots never written
     }
+    __builtin_amdgcn_sched_barrier(0);
+    dma.stage(buf1, zr, wr, vb + T::kUnit, wave);  // every workgroup has at least one chunk (two units)
+    __builtin_amdgcn_sched_barrier(0);
+    ChunkGumbels cg;
+    float g_prev = cg.get(a.key, b, k, c_begin, h);  // chunk Gumbel of the chunk the next closing epilogue ends
     DraftRowState st;
     st.run_m = -INFINITY;
     st.run_s = 0.f;
@@ -867,12 +926,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
     st.best_c = 0x7fffffff;
 
     f32x16_t acc0[T::kMt], acc1[T::kMt];
-    const int vb = c_begin * kChunk;
     // chunk c_begin: first half (nothing pending yet), then second half
-    dma.stage(buf0, zr, wr, vb, wave);
-    wait_vmem();
-    __syncthreads();
-    dma.stage(buf1, zr, wr, vb + T::kUnit, wave);
+    DraftDma<R>::wait_all_but_last_stage();
+    barrier_lds_only();
     if (vb + T::kUnit > V) {
       mask_tail<T>(buf0, vb, V, tid);
       __syncthreads();
@@ -889,7 +945,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
     D::seed(buf1, acc1, prow, h);
     D::mma(buf1 + abase, bfrag, acc1);
     __builtin_amdgcn_sched_barrier(0);
-    draft_half<T, false>(acc0, st, c_begin, scale2, grow);
+    draft_half<T, false>(acc0, st, c_begin, scale2, 0.f);
     for (int j = 1; j < nc; ++j) {
       const int c = c_begin + j;
       const int v0 = c * kChunk;
@@ -897,12 +953,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
       wait_vmem();
       __syncthreads();
       dma.stage(buf1, zr, wr, v0 + T::kUnit, wave);
+      const float g_cur = cg.get(a.key, b, k, c, h);  // closes chunk c in the next iteration
       if (v0 + T::kUnit > V) {
         mask_tail<T>(buf0, v0, V, tid);
         __syncthreads();
       }
       if (wave & 4) {  // the partner wave on this SIMD runs the other order: MFMA and VALU overlap
-        draft_half<T, true>(acc1, st, c - 1, scale2, grow);
+        draft_half<T, true>(acc1, st, c - 1, scale2, g_prev);
         __builtin_amdgcn_sched_barrier(0);
         D::seed(buf0, acc0, prow, h);
         D::mma(buf0 + abase, bfrag, acc0);
@@ -910,8 +967,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
         D::seed(buf0, acc0, prow, h);
         D::mma(buf0 + abase, bfrag, acc0);
         __builtin_amdgcn_sched_barrier(0);
-        draft_half<T, true>(acc1, st, c - 1, scale2, grow);
+        draft_half<T, true>(acc1, st, c - 1, scale2, g_prev);
       }
+      g_prev = g_cur;
       // unit 2j+1 (second half of chunk c) from buf1, with the epilogue of unit 2j
       wait_vmem();
       __syncthreads();
@@ -921,7 +979,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
         __syncthreads();
       }
       if (wave & 4) {
-        draft_half<T, false>(acc0, st, c, scale2, grow);
+        draft_half<T, false>(acc0, st, c, scale2, 0.f);
         __builtin_amdgcn_sched_barrier(0);
         D::seed(buf1, acc1, prow, h);
         D::mma(buf1 + abase, bfrag, acc1);
@@ -929,33 +987,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
         D::seed(buf1, acc1, prow, h);
         D::mma(buf1 + abase, bfrag, acc1);
         __builtin_amdgcn_sched_barrier(0);
-        draft_half<T, false>(acc0, st, c, scale2, grow);
+        draft_half<T, false>(acc0, st, c, scale2, 0.f);
       }
     }
-    draft_half<T, true>(acc1, st, c_end - 1, scale2, grow);
+    draft_half<T, true>(acc1, st, c_end - 1, scale2, g_prev);
     __syncthreads();  // the next pass restages buf0
     if (rv && lane < 32) a.part[(size_t)b * G + g] = make_float4(st.run_m, st.run_s, st.best, __int_as_float(st.best_c));
   }
 }
 
-// ---------------------------------------------------------------- chunk Gumbels
-// All chunk-level Gumbels of the K draft steps, one Philox call per (request,
-// position, 4 chunks): G[b][k-1][c] = Gumbel of draw (c, b, k, purpose 1).
-__global__ __launch_bounds__(256) void k_chunk_gumbels(float* gum, int B, int K, int nc, int ncpad, Key key) {
-  const int nq = ncpad >> 2;
+// ---------------------------------------------------------------- B fragments
+// E row of token x stored for row b in the B-fragment order of the draft
+// kernel: entries 8p..8p+7 go to 16-byte slot ((b/32)*(r/16) + p/2)*64 + b%32 + 32*(p%2),
+// so lane l of the wave holding rows 32*(b/32).. reads K-step t as one
+// contiguous 1 KB block.
+__device__ __forceinline__ void efrag_store_piece(uint4* efrag, const uint16_t* E, int x, int b, int r, int p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(E + (size_t)x * r + 8 * p);
+  efrag[((size_t)(b >> 5) * (r >> 4) + (p >> 1)) * 64 + (b & 31) + 32 * (p & 1)] = v;
+}
+
+// One thread per 16-byte piece: the fragments of tok[b] for every row b.
+__global__ __launch_bounds__(256) void k_efrag_gather(const uint16_t* E, const int32_t* tok, uint4* efrag, int B,
+                                                      int V, int r) {
+  const int per = r >> 3;
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (long long)B * K * nq) return;
-  const int q = (int)(i % nq);
-  const int row = (int)(i / nq);  // b * K + (k - 1)
-  const int b = row / K, k = row - b * K + 1;
-  const Words4 w = draw_quad(key, (uint32_t)(q * 4), (uint32_t)b, (uint32_t)k, kDraftChunk);
-  float4 g;
-  g.x = gumbel_from_word(w.w[0]);
-  g.y = gumbel_from_word(w.w[1]);
-  g.z = gumbel_from_word(w.w[2]);
-  g.w = gumbel_from_word(w.w[3]);
-  (void)nc;
-  reinterpret_cast<float4*>(gum + (size_t)row * ncpad)[q] = g;
+  if (i >= (long long)B * per) return;
+  const int b = (int)(i / per), p = (int)(i % per);
+  efrag_store_piece(efrag, E, clamp_id(tok[b], V), b, r, p);
 }
 
 // ---------------------------------------------------------------- select kernel
@@ -1049,6 +1107,12 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
     a.tok[o] = X;
     a.logq[o] = s_ell[X - cstar * kChunk] - lse;
     a.lse[o] = lse;
+    s_c[0] = X;
+  }
+  if (a.efrag) {  // the next draft step's B fragments (bf16 factors only)
+    __syncthreads();
+    const int X = s_c[0];
+    if (tid < (a.r >> 3)) efrag_store_piece(a.efrag, static_cast<const uint16_t*>(a.E), X, b, a.r, tid);
   }
 }
 
@@ -1096,12 +1160,8 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
 template <int MODE>
 static hipError_t launch_stream(const dspark_problem& P, const StreamArgs& a, int G, hipStream_t s) {
   const bool zb = P.logits_dtype == DSPARK_BF16, wb = P.weight_dtype == DSPARK_BF16;
-  // the buffer-descriptor draft kernel addresses a pass of 256 logits rows with
-  // 32-bit offsets: (255 * K + 1) * V * 2 bytes must stay below 2^32
-  const bool offsets32 = ((unsigned long long)(kRowsPerPass - 1) * P.K + 1) * (unsigned long long)P.V * 2ull <
-                         (1ull << 32);
   if (wb && MODE == MODE_DRAFT) {
-    if (zb && offsets32) {
+    if (draft_uses_efrag(P)) {
       DSPARK_R_CASES_DRAFT16
     } else if (zb) {
       DSPARK_R_CASES_BF16(uint16_t, MODE_DRAFT)
@@ -1124,14 +1184,20 @@ static hipError_t launch_stream(const dspark_problem& P, const StreamArgs& a, in
   return hipGetLastError();
 }
 
-bool draft_uses_gumbel_table(const dspark_problem& P) {
-  return P.logits_dtype == DSPARK_BF16 && P.weight_dtype == DSPARK_BF16;
+bool draft_uses_efrag(const dspark_problem& P) {
+  // the buffer-descriptor draft kernel (bf16 logits and factors) addresses a
+  // pass of 256 logits rows with 32-bit offsets, (255 * K + 1) * V * 2 bytes
+  // below 2^32, and its filler DMA slots read at offset 2^31, past the end of Wt
+  return P.logits_dtype == DSPARK_BF16 && P.weight_dtype == DSPARK_BF16 &&
+         ((unsigned long long)(kRowsPerPass - 1) * P.K + 1) * (unsigned long long)P.V * 2ull < (1ull << 32) &&
+         (unsigned long long)P.V * (unsigned long long)P.r * 2ull < (1ull << 31);
 }
 
-hipError_t launch_chunk_gumbels(const dspark_problem& P, float* gum, int ncpad, Key key, hipStream_t s) {
-  const long long n = (long long)P.B * P.K * (ncpad / 4);
-  hipLaunchKernelGGL(k_chunk_gumbels, (unsigned)((n + 255) / 256), 256, 0, s, gum, P.B, P.K, n_chunks(P.V), ncpad,
-                     key);
+hipError_t launch_efrag_gather(const dspark_problem& P, const void* E, const int32_t* tok, uint4* efrag,
+                               hipStream_t s) {
+  const long long n = (long long)P.B * (P.r / 8);
+  hipLaunchKernelGGL(k_efrag_gather, (unsigned)((n + 255) / 256), 256, 0, s, static_cast<const uint16_t*>(E), tok,
+                     efrag, P.B, P.V, P.r);
   return hipGetLastError();
 }
 
