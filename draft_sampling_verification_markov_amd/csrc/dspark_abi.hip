@@ -20,7 +20,9 @@ Layout make_layout(const dspark_problem& P) {
   L.job = off;    off = align_up(off + B * sizeof(int32_t));
   L.rows = off;   off = align_up(off + B * K * sizeof(int32_t));
   L.nrows = off;  off = align_up(off + sizeof(int32_t));
-  L.sorted = off; off = align_up(off + B * K * sizeof(int32_t));
+  L.rpart = off;  off = align_up(off + (size_t)sched_segments((int)(B * K)) * B * K * sizeof(int32_t));
+  L.sorts = off;  off = align_up(off + B * K * sizeof(float));
+  L.sorti = off;  off = align_up(off + B * K * sizeof(int32_t));
   L.efrag = off;  off = align_up(off + (size_t)((B + 31) / 32) * 32 * (size_t)P.r * 2);
   L.total = off;
   return L;
@@ -198,7 +200,8 @@ extern "C" dspark_status dspark_schedule(const dspark_problem* P, const float* s
   if (st != DSPARK_OK) return st;
   (void)hipGetLastError();
   const Layout L = make_layout(*P);
-  if (launch_schedule(*P, surv, T_table, n_sched, n_total, at<int32_t>(workspace, L.sorted), stream) != hipSuccess)
+  if (launch_schedule(*P, surv, T_table, n_sched, n_total, at<int32_t>(workspace, L.rpart),
+                      at<float>(workspace, L.sorts), at<int32_t>(workspace, L.sorti), stream) != hipSuccess)
     return DSPARK_E_LAUNCH;
   return DSPARK_OK;
 }
@@ -257,6 +260,7 @@ extern "C" dspark_status dspark_verify(const dspark_problem* P, const void* targ
   va.inv_T = 1.0f / p.sampling_temp;
   va.scale2 = kLog2e / p.sampling_temp;
   va.key = host_key(p.seed);
+  va.efrag = verify_uses_efrag(p) ? at<uint4>(workspace, L.efrag) : nullptr;
   if (launch_verify_pre(p, va, stream) != hipSuccess) return DSPARK_E_LAUNCH;
 
   StreamArgs sa{};
@@ -271,6 +275,7 @@ extern "C" dspark_status dspark_verify(const dspark_problem* P, const void* targ
   sa.job = va.job;
   sa.n_sched = n_sched;
   sa.part = at<float4>(workspace, L.part);
+  sa.efrag = va.efrag;
   sa.B = p.B;
   sa.K = p.K;
   sa.V = p.V;

@@ -192,4 +192,61 @@ __device__ __forceinline__ float half_dot<float>(const float* E, const float* Wt
   return acc;
 }
 
+// The same half dot product with the rank R fixed at compile time: a half row
+// of E or Wt held in registers (so the loads of a whole half row are in flight
+// at once), and the fmas in the same order as half_dot.
+template <typename WT, int R>
+struct HalfRow;
+template <int R>
+struct HalfRow<uint16_t, R> {
+  static constexpr int kN = R / 16;  // uint4 pieces of R/2 bf16 entries
+  uint4 q[kN];
+  __device__ __forceinline__ void load(const uint16_t* row, int h) {
+    const uint4* p = reinterpret_cast<const uint4*>(row + h * (R / 2));
+#pragma unroll
+    for (int j = 0; j < kN; ++j) q[j] = p[j];
+  }
+};
+template <int R>
+struct HalfRow<float, R> {
+  static constexpr int kN = R / 8;  // float4 pieces of R/2 fp32 entries
+  float4 q[kN];
+  __device__ __forceinline__ void load(const float* row, int h) {
+    const float4* p = reinterpret_cast<const float4*>(row + h * (R / 2));
+#pragma unroll
+    for (int j = 0; j < kN; ++j) q[j] = p[j];
+  }
+};
+
+template <int R>
+__device__ __forceinline__ float half_dot_regs(const HalfRow<uint16_t, R>& e, const HalfRow<uint16_t, R>& w) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < HalfRow<uint16_t, R>::kN; ++j) {
+    const uint4 ev = e.q[j], wv = w.q[j];
+    acc = fmaf(bf16_lo(ev.x), bf16_lo(wv.x), acc);
+    acc = fmaf(bf16_hi(ev.x), bf16_hi(wv.x), acc);
+    acc = fmaf(bf16_lo(ev.y), bf16_lo(wv.y), acc);
+    acc = fmaf(bf16_hi(ev.y), bf16_hi(wv.y), acc);
+    acc = fmaf(bf16_lo(ev.z), bf16_lo(wv.z), acc);
+    acc = fmaf(bf16_hi(ev.z), bf16_hi(wv.z), acc);
+    acc = fmaf(bf16_lo(ev.w), bf16_lo(wv.w), acc);
+    acc = fmaf(bf16_hi(ev.w), bf16_hi(wv.w), acc);
+  }
+  return acc;
+}
+template <int R>
+__device__ __forceinline__ float half_dot_regs(const HalfRow<float, R>& e, const HalfRow<float, R>& w) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < HalfRow<float, R>::kN; ++j) {
+    const float4 ev = e.q[j], wv = w.q[j];
+    acc = fmaf(ev.x, wv.x, acc);
+    acc = fmaf(ev.y, wv.y, acc);
+    acc = fmaf(ev.z, wv.z, acc);
+    acc = fmaf(ev.w, wv.w, acc);
+  }
+  return acc;
+}
+
 }  // namespace dspark

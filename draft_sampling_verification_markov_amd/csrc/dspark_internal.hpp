@@ -32,7 +32,9 @@ struct Layout {
   size_t job;   // int32 [B]: position of the first rejection (0 = all accepted)
   size_t rows;  // int32 [B*K]: compact list of rows to verify, b * 64 + (k - 1)
   size_t nrows; // int32 [1]
-  size_t sorted;// int32 [B*K]: candidates in schedule order
+  size_t rpart; // int32 [S][B*K]: partial ranks of the candidates over S segments
+  size_t sorts; // float [B*K]: survivals in schedule order (candidate sets too large for LDS)
+  size_t sorti; // int32 [B*K]: candidate indices in schedule order (same)
   size_t efrag; // uint4 [ceil(B/32)][r/16][64]: E rows of the previous draft tokens, B-fragment order
   size_t total;
 };
@@ -109,10 +111,20 @@ struct VerifyArgs {
   int32_t* rows;
   int32_t* nrows;
   const float4* part;
+  uint4* efrag;          // if set, k_accept stores the resample pass's B fragments there
   int B, K, V, r, G, nseg;
   float inv_T, scale2;
   Key key;
 };
+
+// E row of token x stored for row b in the B-fragment order of the streaming
+// kernels: entries 8p..8p+7 go to 16-byte slot ((b/32)*(r/16) + p/2)*64 + b%32 + 32*(p%2),
+// so lane l of the wave holding rows 32*(b/32).. reads K-step t as one
+// contiguous 1 KB block.  x < 0 stores zeros (a row without a draft term).
+__device__ __forceinline__ void efrag_store_piece(uint4* efrag, const uint16_t* E, int x, int b, int r, int p) {
+  const uint4 v = x >= 0 ? *reinterpret_cast<const uint4*>(E + (size_t)x * r + 8 * p) : make_uint4(0, 0, 0, 0);
+  efrag[((size_t)(b >> 5) * (r >> 4) + (p >> 1)) * 64 + (b & 31) + 32 * (p & 1)] = v;
+}
 
 // Launchers; each returns hipSuccess or the launch error.
 hipError_t launch_stream_draft(const dspark_problem& P, const StreamArgs& a, int G, hipStream_t s);
@@ -123,10 +135,16 @@ bool draft_uses_efrag(const dspark_problem& P);
 hipError_t launch_efrag_gather(const dspark_problem& P, const void* E, const int32_t* tok, uint4* efrag,
                                hipStream_t s);
 hipError_t launch_stream_verify(const dspark_problem& P, const StreamArgs& a, int G, hipStream_t s);
+// true when the verify resample pass runs the buffer-DMA kernel, which takes
+// its B fragments from the efrag region (filled by k_accept)
+bool verify_uses_efrag(const dspark_problem& P);
 hipError_t launch_select(const dspark_problem& P, const SelectArgs& a, hipStream_t s);
 hipError_t launch_conf(const dspark_problem& P, const ConfArgs& a, hipStream_t s);
+// Segments of the candidate range that the partial-rank kernel splits the comparisons into.
+constexpr int kSchedSegMax = 16;
+int sched_segments(int n);
 hipError_t launch_schedule(const dspark_problem& P, const float* surv, const float* T, int32_t* n_sched,
-                           int32_t* n_total, int32_t* sorted, hipStream_t s);
+                           int32_t* n_total, int32_t* part, float* sorted_s, int32_t* sorted_i, hipStream_t s);
 hipError_t launch_verify_pre(const dspark_problem& P, const VerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_finish(const dspark_problem& P, const VerifyArgs& a, hipStream_t s);
 

@@ -16,14 +16,17 @@ namespace dspark {
 namespace {
 
 // ---------------------------------------------------------------- confidence
-template <typename HT, typename WT>
-__device__ __forceinline__ float dot_h(const HT* h, const float* w, int d, int lane);
+// dot(x[0:n], w[0:n]) over one wave; lane-strided 16-byte pieces, four pieces
+// in flight per lane.  w may live in LDS or global memory.
+template <typename T>
+__device__ __forceinline__ float dot_vec(const T* x, const float* w, int n, int lane);
 
 template <>
-__device__ __forceinline__ float dot_h<uint16_t, uint16_t>(const uint16_t* h, const float* w, int d, int lane) {
+__device__ __forceinline__ float dot_vec<uint16_t>(const uint16_t* x, const float* w, int n, int lane) {
   float acc = 0.f;
-  for (int i = lane * 8; i < d; i += 64 * 8) {
-    const uint4 hv = *reinterpret_cast<const uint4*>(h + i);
+#pragma unroll 4
+  for (int i = lane * 8; i < n; i += 64 * 8) {
+    const uint4 hv = *reinterpret_cast<const uint4*>(x + i);
     const float4 w0 = *reinterpret_cast<const float4*>(w + i);
     const float4 w1 = *reinterpret_cast<const float4*>(w + i + 4);
     acc = fmaf(bf16_lo(hv.x), w0.x, acc);
@@ -39,10 +42,11 @@ __device__ __forceinline__ float dot_h<uint16_t, uint16_t>(const uint16_t* h, co
 }
 
 template <>
-__device__ __forceinline__ float dot_h<float, float>(const float* h, const float* w, int d, int lane) {
+__device__ __forceinline__ float dot_vec<float>(const float* x, const float* w, int n, int lane) {
   float acc = 0.f;
-  for (int i = lane * 4; i < d; i += 64 * 4) {
-    const float4 hv = *reinterpret_cast<const float4*>(h + i);
+#pragma unroll 4
+  for (int i = lane * 4; i < n; i += 64 * 4) {
+    const float4 hv = *reinterpret_cast<const float4*>(x + i);
     const float4 wv = *reinterpret_cast<const float4*>(w + i);
     acc = fmaf(hv.x, wv.x, acc);
     acc = fmaf(hv.y, wv.y, acc);
@@ -52,23 +56,31 @@ __device__ __forceinline__ float dot_h<float, float>(const float* h, const float
   return acc;
 }
 
-// Same loops with the tag types used for dispatch (h and E may differ in dtype).
-template <typename T>
-__device__ __forceinline__ float dot_vec(const T* x, const float* w, int n, int lane) {
-  return dot_h<T, T>(x, w, n, lane);
-}
+constexpr int kConfThreads = 1024;
+constexpr int kConfWaves = kConfThreads / 64;
+constexpr int kConfWMax = 16384;  // floats of w_c staged in LDS (64 KB)
 
-template <typename HT, typename WT>
-__global__ __launch_bounds__(256) void k_conf(ConfArgs a) {
+// One workgroup per request, one wave per position; with STAGE the
+// confidence weights [w_h; w_e] are copied to LDS once per workgroup.
+template <typename HT, typename WT, bool STAGE>
+__global__ __launch_bounds__(kConfThreads) void k_conf(ConfArgs a) {
+  extern __shared__ float s_w[];
+  __shared__ float s_c[64];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K, d = a.d, r = a.r;
-  __shared__ float s_c[64];
   const HT* h = static_cast<const HT*>(a.h);
   const WT* E = static_cast<const WT*>(a.E);
-  for (int k = wave; k < K; k += 4) {
+  const float* w = a.w_c;
+  if (STAGE) {
+    for (int i = tid * 4; i < d + r; i += kConfThreads * 4)
+      *reinterpret_cast<float4*>(s_w + i) = *reinterpret_cast<const float4*>(a.w_c + i);
+    __syncthreads();
+    w = s_w;
+  }
+  for (int k = wave; k < K; k += kConfWaves) {
     const int prev = clamp_id(k == 0 ? a.anchor[b] : a.tok[(size_t)b * K + k - 1], a.V);
-    float z = dot_vec<HT>(h + ((size_t)b * K + k) * d, a.w_c, d, lane);
-    z += dot_vec<WT>(E + (size_t)prev * r, a.w_c + d, r, lane);
+    float z = dot_vec<HT>(h + ((size_t)b * K + k) * d, w, d, lane);
+    z += dot_vec<WT>(E + (size_t)prev * r, w + d, r, lane);
     z = wave_sum(z);
     if (lane == 0) {
       const float t = (z + a.b_c) / a.tau[k];
@@ -88,66 +100,63 @@ __global__ __launch_bounds__(256) void k_conf(ConfArgs a) {
 }
 
 // ---------------------------------------------------------------- scheduler
-// Rank of every candidate in the order (survival desc, request asc, position
-// asc).  With candidate index i = b*K + (k-1), candidate j precedes i iff
-// s_j > s_i, or s_j == s_i and j < i.  Each workgroup ranks 64 candidates
-// against all n, streaming the survivals through LDS in 1024-entry tiles; its
-// four waves split every tile and their counts are summed at the end.
-constexpr int kRankCands = 64;
-constexpr int kRankTile = 1024;
-
-__global__ __launch_bounds__(256) void k_sched_rank(const float* surv, int n, int32_t* sorted) {
-  __shared__ float tile[kRankTile];
-  __shared__ int cnt[4][kRankCands];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i = blockIdx.x * kRankCands + lane;
-  const float si = i < n ? surv[i] : 0.f;
-  int count = 0;
-  for (int t0 = 0; t0 < n; t0 += kRankTile) {
-    __syncthreads();
-    for (int j = tid; j < kRankTile; j += 256) tile[j] = t0 + j < n ? surv[t0 + j] : -INFINITY;
-    __syncthreads();
-    const int lo = wave * (kRankTile / 4);
-    const int hi = min(lo + kRankTile / 4, n - t0);
-    for (int jj = lo; jj < hi; ++jj) {
-      const float sj = tile[jj];
-      const int j = t0 + jj;
-      count += (sj > si) || (sj == si && j < i);
-    }
-  }
-  cnt[wave][lane] = count;
-  __syncthreads();
-  if (wave == 0 && i < n) {
-    const int rank = cnt[0][lane] + cnt[1][lane] + cnt[2][lane] + cnt[3][lane];
-    if (rank >= 0 && rank < n) sorted[rank] = i;
-  }
+// The scheduler takes candidates in the order (survival desc, request asc,
+// position asc); with candidate index i = b*K + (k-1) that is (survival desc,
+// i asc), i.e. ascending 64-bit keys: the complemented order-preserving bits
+// of the survival above i.
+__device__ __forceinline__ uint32_t float_order_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ unsigned long long sched_key(float s, int i) {
+  return ((unsigned long long)(~float_order_bits(s)) << 32) | (unsigned)i;
 }
 
-constexpr int kScanThreads = 1024;
+// Partial ranks: candidate i (one per thread) counts the keys below its own
+// in segment blockIdx.y of the candidates; part[seg][i] (no atomics, so
+// nothing needs clearing).
+constexpr int kRankTile = 2048;
+__global__ __launch_bounds__(256) void k_sched_rank(const float* surv, int n, int S, int32_t* part) {
+  __shared__ unsigned long long tile[kRankTile];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int seg = blockIdx.y;
+  const int j0 = (int)(((long long)seg * n) / S), j1 = (int)(((long long)(seg + 1) * n) / S);
+  const unsigned long long ki = i < n ? sched_key(surv[i], i) : ~0ull;
+  int cnt = 0;
+  for (int t0 = j0; t0 < j1; t0 += kRankTile) {
+    const int len = min(kRankTile, j1 - t0);
+    __syncthreads();
+    for (int j = threadIdx.x; j < len; j += 256) tile[j] = sched_key(surv[t0 + j], t0 + j);
+    __syncthreads();
+#pragma unroll 8
+    for (int j = 0; j < len; ++j) cnt += tile[j] < ki ? 1 : 0;
+  }
+  if (i < n) part[(size_t)seg * n + i] = cnt;
+}
 
-// One workgroup: prefix sums of the sorted survivals (double), the greedy
-// test for every candidate, the first refusal, and the per-request counts.
-__global__ __launch_bounds__(kScanThreads) void k_sched_scan(const float* surv, const float* T, int B, int K,
-                                                             const int32_t* sorted, int32_t* n_sched,
-                                                             int32_t* n_total) {
+// Greedy pass over candidates in schedule order (sorted_s / sorted_i, any
+// address space): fp64 prefix sums over per-thread segments, the first
+// refusal of (A + s) * T[N] >= A * T[N + 1], the total and per-request counts.
+template <int THREADS, typename SS, typename SI>
+__device__ __forceinline__ void sched_greedy(const SS* sorted_s, const SI* sorted_i, const float* T, int B, int K,
+                                             int32_t* n_sched, int32_t* n_total, double* s_wsum, int* s_wmin,
+                                             int* s_stop) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = B * K;
-  __shared__ double s_wsum[kScanThreads / 64];
-  __shared__ int s_wmin[kScanThreads / 64];
-  __shared__ int s_stop;
-  const int lo = (int)(((long long)tid * n) / kScanThreads);
-  const int hi = (int)(((long long)(tid + 1) * n) / kScanThreads);
-
-  for (int b = tid; b < B; b += kScanThreads) n_sched[b] = 0;
-  __threadfence();  // the zeros are visible before any counting atomic below
-
+  const int lo = (int)(((long long)tid * n) / THREADS);
+  const int hi = (int)(((long long)(tid + 1) * n) / THREADS);
+  // segments are read in register batches of kBatch (clamped, unconditional
+  // loads), so a batch costs one memory round trip instead of one per element
+  constexpr int kBatch = 8;
   double local = 0.0;
-  for (int m = lo; m < hi; ++m) {
-    int idx = sorted[m];
-    idx = idx < 0 ? 0 : (idx >= n ? n - 1 : idx);
-    local += (double)surv[idx];
+  for (int m0 = lo; m0 < hi; m0 += kBatch) {
+    float sv[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) sv[j] = (float)sorted_s[min(m0 + j, n - 1)];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (m0 + j < hi) local += (double)sv[j];
   }
-  // exclusive scan of the per-thread sums
   double incl = local;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -159,61 +168,117 @@ __global__ __launch_bounds__(kScanThreads) void k_sched_scan(const float* surv, 
   double wbase = 0.0;
   for (int w = 0; w < wave; ++w) wbase += s_wsum[w];
   double A = (double)B + wbase + (incl - local);
-
   int first = n;
-  int N = B + lo;
-  for (int m = lo; m < hi; ++m) {
-    int idx = sorted[m];
-    idx = idx < 0 ? 0 : (idx >= n ? n - 1 : idx);
-    const double s = (double)surv[idx];
-    const double lhs = (A + s) * (double)T[N];
-    const double rhs = A * (double)T[N + 1];
-    if (!(lhs >= rhs)) {
-      first = m;
-      break;
+  bool open = true;
+  for (int m0 = lo; m0 < hi && open; m0 += kBatch) {
+    float sv[kBatch], tv[kBatch + 1];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) sv[j] = (float)sorted_s[min(m0 + j, n - 1)];
+#pragma unroll
+    for (int j = 0; j <= kBatch; ++j) tv[j] = T[B + min(m0 + j, n)];  // T has B + n + 1 entries
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (open && m0 + j < hi) {
+        const double s_ = (double)sv[j];
+        if (!((A + s_) * (double)tv[j] >= A * (double)tv[j + 1])) {
+          first = m0 + j;
+          open = false;
+        } else {
+          A += s_;
+        }
+      }
     }
-    A += s;
-    ++N;
   }
-  // first refusal over the workgroup
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o));
   if (lane == 0) s_wmin[wave] = first;
   __syncthreads();
   if (tid == 0) {
     int f = s_wmin[0];
-    for (int w = 1; w < kScanThreads / 64; ++w) f = min(f, s_wmin[w]);
-    s_stop = f;
+    for (int w = 1; w < THREADS / 64; ++w) f = min(f, s_wmin[w]);
+    *s_stop = f;
     *n_total = B + f;
   }
+  // The counts were zeroed by this workgroup before an earlier barrier, whose
+  // workgroup release waits for those stores; the device-scope atomics below
+  // execute at L2 and see them.  No device-wide fence (an L2 write-back) needed.
   __syncthreads();
-  const int stop = s_stop;
-  __threadfence_block();
-  for (int m = tid; m < stop; m += kScanThreads) {
-    int idx = sorted[m];
+  const int stop = *s_stop;
+  for (int m = tid; m < stop; m += THREADS) {
+    int idx = (int)sorted_i[m];
     idx = idx < 0 ? 0 : (idx >= n ? n - 1 : idx);
     atomicAdd(&n_sched[idx / K], 1);
   }
+}
+
+constexpr int kGreedyThreads = 1024;
+
+// Ranks -> schedule order in global memory, many workgroups (each candidate
+// sums its segment counts); then the greedy pass in one workgroup.
+constexpr int kScatterThreads = 64;
+__global__ __launch_bounds__(kScatterThreads) void k_sched_scatter(const float* surv, const int32_t* part, int S,
+                                                                   int n, float* sorted_s, int32_t* sorted_i) {
+  const int i = blockIdx.x * kScatterThreads + threadIdx.x;
+  if (i >= n) return;
+  // every segment load in flight at once: unconditional loads (segments past S
+  // re-read segment 0) and masked sums, not branches
+  int v[kSchedSegMax];
+#pragma unroll
+  for (int q = 0; q < kSchedSegMax; ++q) v[q] = part[(size_t)(q < S ? q : 0) * n + i];
+  int r = 0;
+#pragma unroll
+  for (int q = 0; q < kSchedSegMax; ++q) r += q < S ? v[q] : 0;
+  r = r < 0 ? 0 : (r >= n ? n - 1 : r);
+  sorted_s[r] = surv[i];
+  sorted_i[r] = i;
+}
+
+__global__ __launch_bounds__(kGreedyThreads) void k_sched_greedy_global(const float* sorted_s,
+                                                                      const int32_t* sorted_i, const float* T,
+                                                                      int B, int K, int32_t* n_sched,
+                                                                      int32_t* n_total) {
+  __shared__ double s_wsum[kGreedyThreads / 64];
+  __shared__ int s_wmin[kGreedyThreads / 64];
+  __shared__ int s_stop;
+  for (int b = threadIdx.x; b < B; b += kGreedyThreads) n_sched[b] = 0;
+  __syncthreads();
+  sched_greedy<kGreedyThreads>(sorted_s, sorted_i, T, B, K, n_sched, n_total, s_wsum, s_wmin, &s_stop);
 }
 
 }  // namespace
 
 hipError_t launch_conf(const dspark_problem& P, const ConfArgs& a, hipStream_t s) {
   const bool hb = P.hidden_dtype == DSPARK_BF16, wb = P.weight_dtype == DSPARK_BF16;
-  if (hb && wb) hipLaunchKernelGGL((k_conf<uint16_t, uint16_t>), P.B, 256, 0, s, a);
-  else if (hb) hipLaunchKernelGGL((k_conf<uint16_t, float>), P.B, 256, 0, s, a);
-  else if (wb) hipLaunchKernelGGL((k_conf<float, uint16_t>), P.B, 256, 0, s, a);
-  else hipLaunchKernelGGL((k_conf<float, float>), P.B, 256, 0, s, a);
+  const bool stage = P.d + P.r <= kConfWMax;  // d and r are multiples of 4, so the float4 copy is exact
+  const size_t lds = stage ? (size_t)(P.d + P.r) * sizeof(float) : 0;
+#define DSPARK_CONF(HT, WT)                                                                      \
+  if (stage) hipLaunchKernelGGL((k_conf<HT, WT, true>), P.B, kConfThreads, lds, s, a);            \
+  else hipLaunchKernelGGL((k_conf<HT, WT, false>), P.B, kConfThreads, 0, s, a);
+  if (hb && wb) { DSPARK_CONF(uint16_t, uint16_t) }
+  else if (hb) { DSPARK_CONF(uint16_t, float) }
+  else if (wb) { DSPARK_CONF(float, uint16_t) }
+  else { DSPARK_CONF(float, float) }
+#undef DSPARK_CONF
   return hipGetLastError();
 }
 
+int sched_segments(int n) {
+  const int s = (n + 255) / 256;
+  return s < kSchedSegMax ? s : kSchedSegMax;
+}
+
 hipError_t launch_schedule(const dspark_problem& P, const float* surv, const float* T, int32_t* n_sched,
-                           int32_t* n_total, int32_t* sorted, hipStream_t s) {
+                           int32_t* n_total, int32_t* part, float* sorted_s, int32_t* sorted_i, hipStream_t s) {
   const int n = P.B * P.K;
-  hipLaunchKernelGGL(k_sched_rank, (n + kRankCands - 1) / kRankCands, 256, 0, s, surv, n, sorted);
+  const int S = sched_segments(n);
+  hipLaunchKernelGGL(k_sched_rank, dim3((n + 255) / 256, S), 256, 0, s, surv, n, S, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sched_scan, 1, kScanThreads, 0, s, surv, T, P.B, P.K, sorted, n_sched, n_total);
+  hipLaunchKernelGGL(k_sched_scatter, (n + kScatterThreads - 1) / kScatterThreads, kScatterThreads, 0, s, surv, part, S, n, sorted_s, sorted_i);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sched_greedy_global, 1, kGreedyThreads, 0, s, sorted_s, sorted_i, T, P.B, P.K, n_sched,
+                     n_total);
   return hipGetLastError();
 }
 

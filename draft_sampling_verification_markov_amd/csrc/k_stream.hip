@@ -846,21 +846,20 @@ __device__ __forceinline__ void mask_tail(unsigned char* buf, int v0, int V, int
 // swap them.  The quad index is wave-uniform, so the refill branch is scalar.
 struct ChunkGumbels {
   int quad = -1;
-  float g[4];
-  __device__ __forceinline__ float get(Key key, int b, int k, int c, int h) {
+  float4 g;  // one vector value: picking a component must not become an indexed (scratch) load
+  __device__ __forceinline__ float get(Key key, int b, int k, int c, int h, uint32_t purpose = kDraftChunk) {
     if ((c >> 2) != quad) {
       quad = c >> 2;
-      const Words4 w = draw_quad(key, (uint32_t)(quad * 4), (uint32_t)b, (uint32_t)k, kDraftChunk);
+      const Words4 w = draw_quad(key, (uint32_t)(quad * 4), (uint32_t)b, (uint32_t)k, purpose);
       const float x0 = gumbel_from_word(h ? w.w[2] : w.w[0]);
       const float x1 = gumbel_from_word(h ? w.w[3] : w.w[1]);
       const float2 e0 = halves32(x0), e1 = halves32(x1);
-      g[0] = e0.x;
-      g[1] = e1.x;
-      g[2] = e0.y;
-      g[3] = e1.y;
+      g = make_float4(e0.x, e1.x, e0.y, e1.y);
     }
+    const float4 v = g;
     const int i = c & 3;
-    return i == 0 ? g[0] : i == 1 ? g[1] : i == 2 ? g[2] : g[3];
+    const float lo = (i & 1) ? v.y : v.x, hi = (i & 1) ? v.w : v.z;
+    return (i & 2) ? hi : lo;
   }
 };
 
@@ -908,9 +907,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
     {
       const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(a.efrag) + (size_t)((base >> 5) + wave) * T::kSteps * 64 + lane;
 #pragma unroll
-      for (int t = 0; t < T::kSteps; ++t) bfrag[t] = src[t * 64];
-#pragma unroll
-      for (int t = 0; t < T::kSteps; ++t) bfrag[t] = rv ? bfrag[t] : bf16x8_t{};  // rows past B: slots never written
+      for (int t = 0; t < T::kSteps; ++t) bfrag[t] = src[t * 64];  // rows past B: unwritten slots, own column only
     }
     __builtin_amdgcn_sched_barrier(0);
     dma.stage(buf1, zr, wr, vb + T::kUnit, wave);  // every workgroup has at least one chunk (two units)
@@ -996,16 +993,311 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- B fragments
-// E row of token x stored for row b in the B-fragment order of the draft
-// kernel: entries 8p..8p+7 go to 16-byte slot ((b/32)*(r/16) + p/2)*64 + b%32 + 32*(p%2),
-// so lane l of the wave holding rows 32*(b/32).. reads K-step t as one
-// contiguous 1 KB block.
-__device__ __forceinline__ void efrag_store_piece(uint4* efrag, const uint16_t* E, int x, int b, int r, int p) {
-  const uint4 v = *reinterpret_cast<const uint4*>(E + (size_t)x * r + 8 * p);
-  efrag[((size_t)(b >> 5) * (r >> 4) + (p >> 1)) * 64 + (b & 31) + 32 * (p & 1)] = v;
+
+// ---------------------------------------------------------------- verify resample pass
+// One pass over the vocabulary for every request's final draw of the cycle
+// (bf16 logits and factors): the residual max(0, p - q) at the first
+// rejection k* (p: target row k*, q: the draft distribution at k*, recomputed
+// as logits + E[x_{k*-1}] Wt^T), or, when every scheduled position passed, the
+// bonus target row n_b + 1.  Per chunk: the residual mass (or the bonus row's
+// log-partition) and its chunk Gumbel score; per (row, workgroup) the mass and
+// the best chunk, which the finishing kernel merges.
+//
+// Same machinery as the draft kernel, 32-entry units: per stage a draft-logit
+// tile, a target tile (256 requests x 64 bytes, 16-byte slots swizzled by
+// (row >> 2) & 3 so that 16 consecutive rows hit 16 distinct bank groups) and
+// a Wt tile of 32 rows in MFMA row order; a three-stage ring of distinct LDS
+// objects, two units in flight.  The B fragments come from the fragment-ordered
+// region that the acceptance kernel fills (zeros for bonus rows, whose q is 0).
+template <int R>
+struct VerifyTiles {
+  static constexpr int kUnit = 32;
+  static constexpr int kZRow = 64, kZSlots = 4;
+  static constexpr int kZBytes = kRowsPerPass * kZRow;  // 16 KB
+  static constexpr int kTOff = kZBytes;                 // target tile
+  static constexpr int kWOff = 2 * kZBytes;             // Wt tile
+  static constexpr int kWRow = R * 2;
+  static constexpr int kWStride = kWRow + 16;
+  static constexpr int kWSlots = R / 8;
+  static constexpr int kWBlocks = (kUnit * kWStride + 1023) / 1024;
+  static constexpr int kSink = kWOff + kWBlocks * 1024;
+  static constexpr int kStage = kSink + 1024;
+  static constexpr int kSteps = R / 16;
+  static constexpr int kUnitsPerChunk = kChunk / kUnit;
+  static constexpr int kZRowsPerBlk = 1024 / kZRow;  // 16
+  static constexpr int kZPer = kZBytes / 1024 / kWaves;
+  static constexpr int kWPer = (kWBlocks + kWaves - 1) / kWaves;
+  static constexpr int kOps = 2 * kZPer + kWPer;  // DMA instructions per wave and stage
+  __device__ __forceinline__ static int z_off(int row, int s) { return row * kZRow + ((s ^ ((row >> 2) & 3)) << 4); }
+};
+
+template <int R>
+struct VerifyDma {
+  using T = VerifyTiles<R>;
+  // beyond every buffer of a pass (each below 2^31 bytes); a filler Wt slot of a
+  // dummy stage wraps round to the start of Wt, which only lands in the sink
+  static constexpr uint32_t kOutOfRange = 0x80000000u;
+  uint32_t zoff[T::kZPer], toff[T::kZPer], woff[T::kWPer];
+
+  // zrow/trow: byte offset of the draft-logit and target rows of pass row `row`
+  __device__ __forceinline__ void init(int wave, int lane, const uint32_t* zrow_lds, const uint32_t* trow_lds) {
+#pragma unroll
+    for (int j = 0; j < T::kZPer; ++j) {
+      const int row = (wave + j * kWaves) * T::kZRowsPerBlk + lane / T::kZSlots;
+      const int s = (lane % T::kZSlots) ^ ((row >> 2) & 3);
+      zoff[j] = zrow_lds[row] + (uint32_t)s * 16;
+      toff[j] = trow_lds[row] + (uint32_t)s * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < T::kWPer; ++j) {
+      const int blk = wave + j * kWaves;
+      const int byte = blk * 1024 + lane * 16;
+      const int lrow = byte / T::kWStride, slot = (byte % T::kWStride) / 16;
+      const bool real = slot < T::kWSlots && lrow < T::kUnit;
+      woff[j] = blk >= T::kWBlocks ? kOutOfRange
+                                   : real ? (uint32_t)mfma_row_entry(lrow) * T::kWRow + (uint32_t)slot * 16 : 0u;
+    }
+  }
+  // unit starting at entry v0, or (v0 < 0) a dummy stage whose reads all fall
+  // past the end of the buffers: zeros, no memory traffic
+  __device__ __forceinline__ void stage(unsigned char* buf, __amdgpu_buffer_rsrc_t zr, __amdgpu_buffer_rsrc_t tr,
+                                        __amdgpu_buffer_rsrc_t wr, int v0, int wave) const {
+    const int zs = v0 >= 0 ? v0 * 2 : (int)kOutOfRange;
+    const int ws = v0 >= 0 ? v0 * T::kWRow : (int)kOutOfRange;
+#pragma unroll
+    for (int j = 0; j < T::kZPer; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          zr, (__attribute__((address_space(3))) void*)(buf + (wave + j * kWaves) * 1024), 16, (int)zoff[j], zs, 0,
+          0);
+#pragma unroll
+    for (int j = 0; j < T::kZPer; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          tr, (__attribute__((address_space(3))) void*)(buf + T::kTOff + (wave + j * kWaves) * 1024), 16,
+          (int)toff[j], zs, 0, 0);
+#pragma unroll
+    for (int j = 0; j < T::kWPer; ++j) {
+      const int blk = wave + j * kWaves;
+      const int dst = blk < T::kWBlocks ? T::kWOff + blk * 1024 : T::kSink;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(buf + dst), 16,
+                                               (int)woff[j], ws, 0, 0);
+    }
+  }
+};
+
+struct VerifyRowState {
+  float mass, best, cm, cs;
+  int best_c;
+};
+
+// One 32-entry unit: seed from the draft-logit tile, MFMA over the rank,
+// then the residual (or bonus log-partition) epilogue.
+template <int R>
+__device__ __forceinline__ void verify_unit(const unsigned char* buf, const bf16x8_t* bfrag, int prow, int h, int lane,
+                                            int v0, int V, bool resid, float scale2, float lsp2, float lsq2,
+                                            VerifyRowState& st) {
+  using T = VerifyTiles<R>;
+  f32x16_t acc;
+  float tz[16];
+  {
+    const uint4 x = *reinterpret_cast<const uint4*>(buf + T::z_off(prow, 2 * h));
+    const uint4 y = *reinterpret_cast<const uint4*>(buf + T::z_off(prow, 2 * h + 1));
+    const uint4 tx = *reinterpret_cast<const uint4*>(buf + T::kTOff + T::z_off(prow, 2 * h));
+    const uint4 ty = *reinterpret_cast<const uint4*>(buf + T::kTOff + T::z_off(prow, 2 * h + 1));
+    const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+    const uint32_t tw[8] = {tx.x, tx.y, tx.z, tx.w, ty.x, ty.y, ty.z, ty.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[2 * i] = bf16_lo(w[i]);
+      acc[2 * i + 1] = bf16_hi(w[i]);
+      tz[2 * i] = bf16_lo(tw[i]);
+      tz[2 * i + 1] = bf16_hi(tw[i]);
+    }
+  }
+  {
+    const unsigned char* wt = buf + T::kWOff + (lane & 31) * T::kWStride + 16 * h;
+    bf16x8_t af[3];
+    af[0] = *reinterpret_cast<const bf16x8_t*>(wt);
+    if (T::kSteps > 1) af[1] = *reinterpret_cast<const bf16x8_t*>(wt + 32);
+#pragma unroll
+    for (int t = 0; t < T::kSteps; ++t) {
+      if (t + 2 < T::kSteps) af[(t + 2) % 3] = *reinterpret_cast<const bf16x8_t*>(wt + 32 * (t + 2));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t % 3], bfrag[t], acc, 0, 0, 0);
+    }
+  }
+  const int e0 = v0 + 16 * h;  // first entry of this lane
+  const bool ragged = v0 + T::kUnit > V;
+  if (resid) {
+    float rs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(tz[i], scale2, -lsp2));
+      const float q = __builtin_amdgcn_exp2f(fmaf(acc[i], scale2, -lsq2));
+      const float d = fmaxf(p - q, 0.f);
+      rs += (!ragged || e0 + i < V) ? d : 0.f;
+    }
+    st.cs += rs;
+  } else {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (ragged && e0 + i >= V) tz[i] = -INFINITY;
+      m = fmaxf(m, tz[i]);
+    }
+    m = halves32_max(m);
+    float s = 0.f;
+    if (m != -INFINITY) {
+      const float off = -m * scale2;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s += __builtin_amdgcn_exp2f(fmaf(tz[i], scale2, off));
+    }
+    s = halves32_sum(s);
+    lse2_merge(st.cm, st.cs, m * scale2, s);
+  }
 }
 
+template <int R, int STAGES>
+__global__ __launch_bounds__(kThreads, 1) void k_verify_stream(StreamArgs a) {
+  using T = VerifyTiles<R>;
+  static_assert(STAGES == 2 || STAGES == 3, "ring of two or three stages");
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[T::kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[T::kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf2[STAGES == 3 ? T::kStage : 16];
+  __shared__ uint32_t s_zrow[kRowsPerPass], s_trow[kRowsPerPass];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = gridDim.x, g = blockIdx.x;
+  const int c_begin = (int)(((long long)g * a.nchunks) / G);
+  const int c_end = (int)(((long long)(g + 1) * a.nchunks) / G);
+  const int nunits = (c_end - c_begin) * T::kUnitsPerChunk;
+  const int V = a.V, K = a.K, B = a.B;
+  const float scale2 = a.scale2;
+  const int h = lane >> 5;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.Wt, (uint32_t)((size_t)V * T::kWRow));
+  const uint16_t* Z = static_cast<const uint16_t*>(a.Z);
+  const uint16_t* Zt = static_cast<const uint16_t*>(a.Zt);
+
+  for (int base = 0; base < B; base += kRowsPerPass) {
+    const int rows_valid = B - base < kRowsPerPass ? B - base : kRowsPerPass;
+    // byte offsets of each pass row's draft-logit and target rows (rows past B
+    // repeat the last valid row; their results are never stored)
+    for (int row = tid; row < kRowsPerPass; row += kThreads) {
+      const int bb = base + (row < rows_valid ? row : rows_valid - 1);
+      const int rr = row < rows_valid ? row : rows_valid - 1;
+      const int ks = a.job[bb];
+      int nb = a.n_sched[bb];
+      nb = nb < 0 ? 0 : (nb > K ? K : nb);
+      // a bonus row has no draft term (B fragments 0, q = 0): any valid draft-logit row will do
+      s_zrow[row] = (uint32_t)(((size_t)rr * K + (ks > 0 ? ks - 1 : 0)) * V * 2);
+      s_trow[row] = (uint32_t)(((size_t)rr * (K + 1) + (ks > 0 ? ks - 1 : nb)) * V * 2);
+    }
+    barrier_lds_only();
+    const __amdgpu_buffer_rsrc_t zr =
+        make_rsrc(Z + (size_t)base * K * V, (uint32_t)((size_t)rows_valid * K * V * 2));
+    const __amdgpu_buffer_rsrc_t tr =
+        make_rsrc(Zt + (size_t)base * (K + 1) * V, (uint32_t)((size_t)rows_valid * (K + 1) * V * 2));
+    VerifyDma<R> dma;
+    dma.init(wave, lane, s_zrow, s_trow);
+
+    const int prow = wave * 32 + (lane & 31);
+    const int b = base + prow;
+    const bool rv = b < B;
+    const bool wave_on = base + wave * 32 < B;
+    bool resid = false;
+    int kpos = 1;
+    uint32_t purpose = kBonusChunk;
+    float lsq2 = INFINITY, lsp2 = 0.f;  // a bonus row: q = exp2(-inf) = 0
+    if (rv) {
+      const int ks = a.job[b];
+      if (ks > 0) {
+        resid = true;
+        kpos = ks;
+        purpose = kResidChunk;
+        lsq2 = a.lse_q[(size_t)b * K + ks - 1] * kLog2e;
+        lsp2 = a.lse_p[(size_t)b * K + ks - 1] * kLog2e;
+      } else {
+        int nb = a.n_sched[b];
+        nb = nb < 0 ? 0 : (nb > K ? K : nb);
+        kpos = nb + 1;
+      }
+    }
+    const int v_first = c_begin * kChunk;
+    auto unit_v0 = [&](int u) { return u < nunits ? v_first + u * T::kUnit : -1; };
+    dma.stage(buf0, zr, tr, wr, unit_v0(0), wave);
+    __builtin_amdgcn_sched_barrier(0);
+    // rows past B read fragment slots nobody wrote: only their own (discarded) MFMA column sees them
+    bf16x8_t bfrag[T::kSteps];
+    {
+      const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(a.efrag) + (size_t)((base >> 5) + wave) * T::kSteps * 64 + lane;
+#pragma unroll
+      for (int t = 0; t < T::kSteps; ++t) bfrag[t] = src[t * 64];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (STAGES == 3) dma.stage(buf1, zr, tr, wr, unit_v0(1), wave);
+    __builtin_amdgcn_sched_barrier(0);
+
+    VerifyRowState st;
+    st.mass = 0.f;
+    st.best = -INFINITY;
+    st.cm = -INFINITY;
+    st.cs = 0.f;
+    st.best_c = 0x7fffffff;
+    ChunkGumbels cg;
+
+    // unit u from stage u % 3; at its start the DMA of unit u + 2 goes into the
+    // stage that unit u - 1 used (every wave is past it at the barrier).  Every
+    // step issues exactly one stage (a dummy one past the last unit), so that
+    // one wait count means "unit u has landed" on every path.
+    auto step = [&](int u, unsigned char* cur, unsigned char* nxt2) {
+      if (STAGES == 3) wait_vmem_n<T::kOps>();
+      else wait_vmem();
+      barrier_lds_only();
+      dma.stage(nxt2, zr, tr, wr, unit_v0(u + STAGES - 1), wave);
+      if (!wave_on || u >= nunits) return;
+      const int v0 = v_first + u * T::kUnit;
+      verify_unit<R>(cur, bfrag, prow, h, lane, v0, V, resid, scale2, lsp2, lsq2, st);
+      if ((u & (T::kUnitsPerChunk - 1)) == T::kUnitsPerChunk - 1) {  // chunk closes
+        const int c = c_begin + u / T::kUnitsPerChunk;
+        const float gum = cg.get(a.key, b, kpos, c, h, purpose);
+        float score;
+        if (resid) {
+          const float rc = halves32_sum(st.cs);
+          st.mass += rc;
+          score = rc > 0.f ? logf(rc) + gum : -INFINITY;
+        } else {
+          score = st.cs > 0.f ? (st.cm + log2f(st.cs)) * kLn2 + gum : -INFINITY;
+        }
+        if (score > st.best) {
+          st.best = score;
+          st.best_c = c;
+        }
+        st.cm = -INFINITY;
+        st.cs = 0.f;
+      }
+    };
+    // the first step is peeled: the B fragments are first used outside the loop,
+    // so the compiler does not drain every load (the DMA in flight included)
+    // before entering it
+    if (STAGES == 3) {
+      step(0, buf0, buf2);
+      for (int u = 1; u < nunits; u += 3) {
+        step(u, buf1, buf0);
+        step(u + 1, buf2, buf1);
+        step(u + 2, buf0, buf2);
+      }
+    } else {  // two stages: unit u + 1 streams in while unit u is computed
+      step(0, buf0, buf1);
+      for (int u = 1; u < nunits; u += 2) {
+        step(u, buf1, buf0);
+        step(u + 1, buf0, buf1);
+      }
+    }
+    wait_vmem();         // the dummy stages have landed
+    barrier_lds_only();  // the next pass restages the ring and the row offsets
+    if (rv && lane < 32) a.part[(size_t)b * G + g] = make_float4(st.mass, 0.f, st.best, __int_as_float(st.best_c));
+  }
+}
+
+// ---------------------------------------------------------------- B fragments
 // One thread per 16-byte piece: the fragments of tok[b] for every row b.
 __global__ __launch_bounds__(256) void k_efrag_gather(const uint16_t* E, const int32_t* tok, uint4* efrag, int B,
                                                       int V, int r) {
@@ -1017,7 +1309,10 @@ __global__ __launch_bounds__(256) void k_efrag_gather(const uint16_t* E, const i
 }
 
 // ---------------------------------------------------------------- select kernel
-template <typename ZT, typename WT>
+// One workgroup per row.  The loads that do not depend on the winning chunk
+// (the previous token, then its E half row) are issued before the partials
+// are merged, so the chain is: partials -> winning chunk -> its Wt rows.
+template <typename ZT, typename WT, int R>
 __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K, V = a.V;
@@ -1025,6 +1320,11 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   __shared__ int s_c[4];
   __shared__ float s_lse;
   __shared__ int s_cstar;
+
+  const int j = tid >> 1, h = tid & 1;
+  const int prev = clamp_id(a.k == 1 ? a.anchor[b] : a.tok[(size_t)b * K + a.k - 2], V);
+  HalfRow<WT, R> erow;
+  erow.load(static_cast<const WT*>(a.E) + (size_t)prev * R, h);
 
   // 1. merge the per-workgroup partials of row b
   float m = -INFINITY, s = 0.f, best = -INFINITY;
@@ -1070,18 +1370,18 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   const float lse = s_lse;
 
   // 2. recompute the winning chunk's logits and draw the entry
-  const int prev = clamp_id(a.k == 1 ? a.anchor[b] : a.tok[(size_t)b * K + a.k - 2], V);
-  const int j = tid >> 1, h = tid & 1;
   const int v = cstar * kChunk + j;
   const bool inside = v < V;
-  float dot = inside ? half_dot<WT>(static_cast<const WT*>(a.E), static_cast<const WT*>(a.Wt), prev, v, a.r, h)
-                     : 0.f;
+  HalfRow<WT, R> wrow;
+  wrow.load(static_cast<const WT*>(a.Wt) + (size_t)(inside ? v : 0) * R, h);
+  const ZT* zrow = static_cast<const ZT*>(a.Z) + ((size_t)b * K + (a.k - 1)) * V;
+  const float z = logit_at<ZT>(zrow, inside ? v : 0);
+  float dot = inside ? half_dot_regs<R>(erow, wrow) : 0.f;
   dot += __shfl_xor(dot, 1);
   float score = -INFINITY;
   int idx = 0x7fffffff;
   if (h == 0 && inside) {
-    const ZT* zrow = static_cast<const ZT*>(a.Z) + ((size_t)b * K + (a.k - 1)) * V;
-    const float ell = (logit_at<ZT>(zrow, v) + dot) * a.inv_T;
+    const float ell = (z + dot) * a.inv_T;
     s_ell[j] = ell;
     score = ell + gumbel_from_word(draw_word(a.key, (uint32_t)v, (uint32_t)b, (uint32_t)a.k, kDraftElem));
     idx = v;
@@ -1112,7 +1412,7 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   if (a.efrag) {  // the next draft step's B fragments (bf16 factors only)
     __syncthreads();
     const int X = s_c[0];
-    if (tid < (a.r >> 3)) efrag_store_piece(a.efrag, static_cast<const uint16_t*>(a.E), X, b, a.r, tid);
+    if (tid < (R >> 3)) efrag_store_piece(a.efrag, static_cast<const uint16_t*>(a.E), X, b, R, tid);
   }
 }
 
@@ -1127,6 +1427,19 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
     case 128: hipLaunchKernelGGL((k_stream<ZT, 128, MODE>), G, kThreads, 0, s, a); break; \
     case 256: hipLaunchKernelGGL((k_stream<ZT, 256, MODE>), G, kThreads, 0, s, a); break; \
     default: return hipErrorInvalidValue;                                               \
+  }
+#ifndef DSPARK_VERIFY_STAGES
+#define DSPARK_VERIFY_STAGES 2
+#endif
+constexpr int kVerifyStages = DSPARK_VERIFY_STAGES;
+#define DSPARK_R_CASES_VERIFY16                                                        \
+  switch (P.r) {                                                                       \
+    case 16: hipLaunchKernelGGL((k_verify_stream<16, kVerifyStages>), G, kThreads, 0, s, a); break;     \
+    case 32: hipLaunchKernelGGL((k_verify_stream<32, kVerifyStages>), G, kThreads, 0, s, a); break;     \
+    case 64: hipLaunchKernelGGL((k_verify_stream<64, kVerifyStages>), G, kThreads, 0, s, a); break;     \
+    case 128: hipLaunchKernelGGL((k_verify_stream<128, kVerifyStages>), G, kThreads, 0, s, a); break;   \
+    case 256: hipLaunchKernelGGL((k_verify_stream<256, kVerifyStages>), G, kThreads, 0, s, a); break;   \
+    default: return hipErrorInvalidValue;                                              \
   }
 #define DSPARK_R_CASES_DRAFT16                                                         \
   switch (P.r) {                                                                       \
@@ -1169,7 +1482,9 @@ static hipError_t launch_stream(const dspark_problem& P, const StreamArgs& a, in
       DSPARK_R_CASES_BF16(float, MODE_DRAFT)
     }
   } else if (wb) {
-    if (zb) {
+    if (verify_uses_efrag(P)) {
+      DSPARK_R_CASES_VERIFY16
+    } else if (zb) {
       DSPARK_R_CASES_BF16(uint16_t, MODE_VERIFY)
     } else {
       DSPARK_R_CASES_GENERIC(float, uint16_t, MODE_VERIFY)
@@ -1193,6 +1508,16 @@ bool draft_uses_efrag(const dspark_problem& P) {
          (unsigned long long)P.V * (unsigned long long)P.r * 2ull < (1ull << 31);
 }
 
+bool verify_uses_efrag(const dspark_problem& P) {
+  // the buffer-descriptor resample kernel (bf16 logits and factors) addresses a
+  // pass of 256 draft-logit and target rows through buffers below 2^31 bytes,
+  // 256 * (K + 1) * V * 2, and its dummy and filler DMA slots read at offset
+  // 2^31, past the end of every buffer (Wt included)
+  return P.logits_dtype == DSPARK_BF16 && P.weight_dtype == DSPARK_BF16 &&
+         (unsigned long long)kRowsPerPass * (P.K + 1) * (unsigned long long)P.V * 2ull < (1ull << 31) &&
+         (unsigned long long)P.V * (unsigned long long)P.r * 2ull < (1ull << 31);
+}
+
 hipError_t launch_efrag_gather(const dspark_problem& P, const void* E, const int32_t* tok, uint4* efrag,
                                hipStream_t s) {
   const long long n = (long long)P.B * (P.r / 8);
@@ -1211,10 +1536,30 @@ hipError_t launch_stream_verify(const dspark_problem& P, const StreamArgs& a, in
 
 hipError_t launch_select(const dspark_problem& P, const SelectArgs& a, hipStream_t s) {
   const bool zb = P.logits_dtype == DSPARK_BF16, wb = P.weight_dtype == DSPARK_BF16;
-  if (zb && wb) hipLaunchKernelGGL((k_select<uint16_t, uint16_t>), P.B, 256, 0, s, a);
-  else if (zb) hipLaunchKernelGGL((k_select<uint16_t, float>), P.B, 256, 0, s, a);
-  else if (wb) hipLaunchKernelGGL((k_select<float, uint16_t>), P.B, 256, 0, s, a);
-  else hipLaunchKernelGGL((k_select<float, float>), P.B, 256, 0, s, a);
+#define DSPARK_SEL(ZT, WT, R) hipLaunchKernelGGL((k_select<ZT, WT, R>), P.B, 256, 0, s, a)
+#define DSPARK_SEL_R(ZT, WT)                  \
+  switch (P.r) {                              \
+    case 16: DSPARK_SEL(ZT, WT, 16); break;   \
+    case 32: DSPARK_SEL(ZT, WT, 32); break;   \
+    case 64: DSPARK_SEL(ZT, WT, 64); break;   \
+    case 128: DSPARK_SEL(ZT, WT, 128); break; \
+    case 256: DSPARK_SEL(ZT, WT, 256); break; \
+    default: return hipErrorInvalidValue;     \
+  }
+#define DSPARK_SEL_R32(ZT)                        \
+  switch (P.r) {                                  \
+    case 16: DSPARK_SEL(ZT, float, 16); break;    \
+    case 32: DSPARK_SEL(ZT, float, 32); break;    \
+    case 64: DSPARK_SEL(ZT, float, 64); break;    \
+    default: return hipErrorInvalidValue;         \
+  }
+  if (zb && wb) { DSPARK_SEL_R(uint16_t, uint16_t) }
+  else if (zb) { DSPARK_SEL_R32(uint16_t) }
+  else if (wb) { DSPARK_SEL_R(float, uint16_t) }
+  else { DSPARK_SEL_R32(float) }
+#undef DSPARK_SEL_R32
+#undef DSPARK_SEL_R
+#undef DSPARK_SEL
   return hipGetLastError();
 }
 

@@ -156,7 +156,13 @@ __global__ __launch_bounds__(64) void k_accept(VerifyArgs a) {
   }
   if (k0 < K) a.logp[(size_t)b * K + k0] = logp;
   const unsigned long long mask = __ballot(rej);
-  if (k0 == 0) a.job[b] = mask ? __ffsll((long long)mask) : 0;
+  const int ks = mask ? __ffsll((long long)mask) : 0;
+  if (k0 == 0) a.job[b] = ks;
+  if (a.efrag && k0 < (a.r >> 3)) {
+    // B fragments of the resample pass: E[x_{k*-1}] for a rejection at k*, zeros for a bonus row
+    const int prev = ks > 0 ? clamp_id(ks == 1 ? a.anchor[b] : a.tok[(size_t)b * K + ks - 2], a.V) : -1;
+    efrag_store_piece(a.efrag, static_cast<const uint16_t*>(a.E), prev, b, a.r, k0);
+  }
 }
 
 // Two-level Gumbel-max over a whole row of x / T_s inside one workgroup (used

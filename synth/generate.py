@@ -128,3 +128,17 @@ def make_inputs(cfg: Config, threads: int | None = None) -> dict:
         "h": h, "w_c": w_c, "b_c": float(cfg.b_c), "tau": tau,
         "anchor": anchor, "T": T_table(cfg),
     }
+
+
+def make_survivals(B: int, K: int, seed: int, ties: bool = False) -> np.ndarray:
+    """Scheduler-only input: float32 [B, K] rows in (0, 1], non-increasing along
+    each row (sorted uniform draws).  With ``ties`` the values are rounded to
+    multiples of 1/16, so that many candidates of different requests, and of the
+    same request, share one survival and the tie-break decides their order."""
+    rng = np.random.default_rng([seed, 90, B, K])
+    u = rng.uniform(0.0, 1.0, (B, K))
+    if ties:
+        u = np.ceil(u * 16.0) / 16.0
+    u = np.maximum(u, 2.0 ** -20)
+    return -np.sort(-u, axis=1).astype(np.float32)
+

@@ -151,6 +151,11 @@ EDGE = [
     # fp32 logits with bf16 factors, T_s != 1, 300 requests (two row passes)
     synth.get_config("tbias_bf16").replace(name="edge_two_pass", B=300, K=2, V=2048, r=128, d=32,
                                            logits_dtype="f32", T_s=0.7, seed=10),
+    # bf16 everything with 300 requests: two row passes of the draft and resample kernels, ragged last wave
+    synth.get_config("tbias_bf16").replace(name="edge_two_pass_bf16", B=300, K=3, V=2056, r=128, d=32, seed=12),
+    # K = 32: the resample pass exceeds the buffer-offset range of its DMA kernel at the full vocabulary,
+    # here a small vocabulary keeps it on that kernel while the draft spans 32 positions
+    synth.get_config("tbias_bf16").replace(name="edge_k32", B=20, K=32, V=1032, r=64, d=32, seed=13),
     # identical draft and target: every scheduled position is accepted
     synth.get_config("tbias").replace(name="edge_p_eq_q", B=3, K=4, V=640, r=16, d=16, target_noise=0.0,
                                       ew_std=0.0, ttable=("linear", 1.0, 0.0), seed=11),

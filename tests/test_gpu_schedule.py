@@ -1,0 +1,65 @@
+"""Scheduler alone (HIP, through the C ABI) vs the oracle scheduler, at
+candidate counts on both sides of the single-workgroup limit (16384) and with
+exact ties between survivals, so that the (survival desc, request asc,
+position asc) order is decided by the tie-break."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import sched as osched
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from draft_sampling_verification_markov_amd import dspark
+    dspark.load()
+    return dspark
+
+
+CASES = [
+    (256, 16, False),   # 4096 candidates, the batch of the throughput workload
+    (512, 32, False),   # exactly 16384: the largest set ordered in LDS
+    (1024, 32, False),  # 32768: ordered through global memory
+    (700, 9, True),     # ties everywhere
+    (3000, 7, True),    # ties, global path
+]
+
+
+@pytest.mark.parametrize("B,K,ties", CASES, ids=[f"B{b}_K{k}{'_ties' if t else ''}" for b, k, t in CASES])
+def test_schedule_sizes(lib, B, K, ties):
+    dspark = lib
+    n = B * K
+    print(f"[gpu] schedule B={B} K={K} n={n} ties={ties}", flush=True)
+    sys.stdout.flush()
+    S = synth.make_survivals(B, K, seed=5, ties=ties)
+    # cliff table: flat up to N0, then 100x.  Every candidate before the cliff
+    # passes exactly (s > 0) and the one at the cliff fails by a wide margin,
+    # so which n/3 candidates are taken, and hence every per-request count,
+    # is decided by the order alone; the comparison is exact.
+    N0 = B + n // 3
+    T = np.where(np.arange(B * (K + 1) + 1) <= N0, 1.0, 100.0).astype(np.float32)
+    ref = osched.schedule(S.astype(np.float64), T)
+    assert ref["N"] == N0
+    P = dspark.Problem.make(B, K, 1024, 16, 8)
+    ws = torch.empty(dspark.workspace_bytes(P), dtype=torch.uint8, device="cuda")
+    surv = torch.from_numpy(S).cuda()
+    T_d = torch.from_numpy(T).cuda()
+    n_sched = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    n_total = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dspark.schedule(P, surv, T_d, n_sched, n_total, ws)
+    torch.cuda.synchronize()
+    g = n_sched.cpu().numpy()
+    print(f"[gpu]   N = {int(n_total.item())} (oracle {ref['N']}); requests differing: "
+          f"{int((g != np.array(ref['n'])).sum())}", flush=True)
+    np.testing.assert_array_equal(g, np.array(ref["n"]))
+    assert int(n_total.item()) == ref["N"]
