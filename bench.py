@@ -94,10 +94,13 @@ class Hip:
             self.lib.hipEventDestroy(h)
 
 
+DOMINANT = "k_draft"   # the draft-step vocabulary stream kernel
+
+
 def traffic_from_profile(workload: str):
-    """HBM bytes per stream launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(PROFILE_DIR, f"k_stream_draft_{workload}_pmc.json")
+    """HBM bytes per draft-stream launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, f"{DOMINANT}_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -107,7 +110,7 @@ def traffic_from_profile(workload: str):
     return float(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(cfg, inp, gpu, n_req: int):
+def cpu_baseline(cfg, inp, gpu, n_req: int, min_seconds: float = 10.0):
     """The oracle, as it stands, on a bounded sample: all K draft steps, the
     confidence head and verification for n_req requests, and the scheduler over
     the whole batch (on the GPU's survivals)."""
@@ -120,20 +123,114 @@ def cpu_baseline(cfg, inp, gpu, n_req: int):
     from oracle import verify as overify
 
     reqs = np.arange(n_req)
+    reps = 0
     t0 = time.perf_counter()
-    d = odraft.draft(inp["Z"], inp["E"], inp["Wt"], inp["anchor"], cfg.T_s, cfg.seed, requests=reqs)
-    oconf.confidence(inp["h"][reqs], inp["E"], inp["w_c"], inp["b_c"], inp["tau"], inp["anchor"][reqs], d["x"])
-    sc = osched.schedule(gpu["surv"].astype(np.float64), inp["T"])
-    x = gpu["tok"].astype(np.int64).copy()
-    x[reqs] = d["x"]
-    overify.verify(inp["Zt"], inp["Z"], inp["E"], inp["Wt"], inp["anchor"], x, sc["n"], cfg.T_s, cfg.seed,
-                   requests=reqs)
+    while True:  # the sample, repeated until at least min_seconds of CPU work
+        d = odraft.draft(inp["Z"], inp["E"], inp["Wt"], inp["anchor"], cfg.T_s, cfg.seed, requests=reqs)
+        oconf.confidence(inp["h"][reqs], inp["E"], inp["w_c"], inp["b_c"], inp["tau"], inp["anchor"][reqs], d["x"])
+        sc = osched.schedule(gpu["surv"].astype(np.float64), inp["T"])
+        x = gpu["tok"].astype(np.int64).copy()
+        x[reqs] = d["x"]
+        overify.verify(inp["Zt"], inp["Z"], inp["E"], inp["Wt"], inp["anchor"], x, sc["n"], cfg.T_s, cfg.seed,
+                       requests=reqs)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
     t = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": n_req * cfg.K / t, "unit": "positions/s", "cores": int(threads), "kind": "oracle",
+    return {"value": reps * n_req * cfg.K / t, "unit": "positions/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n_req} of {cfg.B} requests x all {cfg.K} positions (draft, confidence, verify) "
-                      f"+ full-batch schedule; {t:.1f} s wall; host {platform.processor() or platform.machine()}, "
-                      f"{os.cpu_count()} logical CPUs"}
+                      f"+ full-batch schedule, {reps} pass(es); {t:.1f} s wall; host "
+                      f"{platform.processor() or platform.machine()}, {os.cpu_count()} logical CPUs"}
+
+
+def _short_kernel_name(name: str) -> str:
+    """'void dspark::(anonymous namespace)::k_draft<256>(dspark::StreamArgs)' -> 'k_draft'."""
+    n = name.replace("(anonymous namespace)", "")
+    n = n.split("(")[0].split("<")[0]
+    return n.split("::")[-1].split()[-1] if n.strip() else name
+
+
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _pmc_means(directory: str, counter: str):
+    """Mean counter value (KiB) per dispatch, by short kernel name."""
+    acc = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        k = _short_kernel_name(r["Kernel_Name"])
+        acc.setdefault(k, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+PROFILE_COMMANDS = """cd /tmp && export TMPDIR=/tmp; R=<repository root>
+rocprofv3 --kernel-trace --stats -T -d $R/gpurun_out/prof/trace -o trace --output-format csv -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline
+rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/prof/fetch -o fetch --output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/prof/write -o write --output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/prof/cfetch -o cfetch --output-format csv -- python3 $R/bench.py --calibrate-copy
+rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/prof/cwrite -o cwrite --output-format csv -- python3 $R/bench.py --calibrate-copy
+python3 $R/bench.py --summarize-profiles $R/gpurun_out/prof"""
+
+
+def summarize_profiles(prof_dir: str, workload: str) -> None:
+    """Writes the kernel-trace and HBM-counter summaries of one profiling run
+    (the commands in PROFILE_COMMANDS) under profiles/, and the per-launch
+    traffic record of the dominant kernel that the roofline entry reads."""
+    import subprocess
+    try:
+        commit = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short", "HEAD"], capture_output=True,
+                                text=True).stdout.strip() or "unknown"
+    except OSError:
+        commit = "unknown"
+    src = kernel_source_hash()
+    # kernel trace
+    rows = _csv_rows(os.path.join(prof_dir, "trace"), "kernel_stats.csv")
+    lines = [f"# Kernel trace: {workload} workload, bench.py --steps 5 --warmup 2", "",
+             "Command (one of the sequence below; trace run first):", "", "```", PROFILE_COMMANDS, "```", "",
+             "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        lines.append(f"| {_short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
+    lines += ["", f"Library source: commit {commit} (kernel sources sha256 {src[:16]}...).",
+              "roll_cuda_kernel is torch.roll building the rotated input sets before the timed region."]
+    with open(os.path.join(PROFILE_DIR, f"cycle_{workload}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    # HBM counters, scaled by what the same counters read for a plain 1 GiB copy
+    fetch, write = _pmc_means(os.path.join(prof_dir, "fetch"), "FETCH_SIZE"), _pmc_means(os.path.join(prof_dir, "write"), "WRITE_SIZE")
+    cf, cw = _pmc_means(os.path.join(prof_dir, "cfetch"), "FETCH_SIZE"), _pmc_means(os.path.join(prof_dir, "cwrite"), "WRITE_SIZE")
+    copy_kib = (1 << 30) / 1024.0
+    ck = [k for k in cf if "copy" in k.lower()]
+    fscale, wscale = copy_kib / cf[ck[0]], copy_kib / cw[ck[0]]
+    lines = [f"# HBM counters per dispatch: {workload} workload", "", "Commands:", "", "```", PROFILE_COMMANDS, "```", "",
+             f"Calibration: a plain 1 GiB device copy ({ck[0]}) reads FETCH_SIZE = {cf[ck[0]]:.1f} KiB and "
+             f"WRITE_SIZE = {cw[ck[0]]:.1f} KiB per dispatch against {copy_kib:.0f} KiB moved each way, so "
+             f"FETCH_SIZE is scaled by {fscale:.4f} and WRITE_SIZE by {wscale:.4f} below.", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM MB per dispatch |", "|---|---:|---:|---:|"]
+    for k in sorted(fetch, key=lambda k: -fetch[k]):
+        if "roll" in k or "copy" in k.lower():
+            continue
+        w = write.get(k, 0.0)
+        lines.append(f"| {k} | {fetch[k]:.1f} | {w:.1f} | {(fetch[k] * fscale + w * wscale) * 1024 / 1e6:.1f} |")
+    lines += ["", f"Library source: commit {commit} (kernel sources sha256 {src[:16]}...)."]
+    with open(os.path.join(PROFILE_DIR, f"cycle_{workload}_hbm_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    rec = {"kernel": DOMINANT, "workload": workload, "commit": commit, "kernel_source_sha256": src,
+           "fetch_kib_per_launch": fetch[DOMINANT], "write_kib_per_launch": write.get(DOMINANT, 0.0),
+           "fetch_scale": fscale, "write_scale": wscale,
+           "hbm_bytes_per_launch": (fetch[DOMINANT] * fscale + write.get(DOMINANT, 0.0) * wscale) * 1024,
+           "source": f"profiles/cycle_{workload}_hbm_counters.md"}
+    with open(os.path.join(PROFILE_DIR, f"{DOMINANT}_{workload}_pmc.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def main() -> int:
@@ -142,11 +239,17 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="high_concurrency")
-    ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the oracle's timed sample")
+    ap.add_argument("--cpu-requests", type=int, default=0,
+                    help="requests in the oracle's timed sample (default: the whole batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (scale for HBM counters)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ summaries of a rocprofv3 run laid out as in PROFILE_COMMANDS")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.config)
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this step has no multi-GPU path; "
               "each GPU would run its own batch, table and scheduler independently.", file=sys.stderr)
@@ -278,7 +381,7 @@ def main() -> int:
         "scheduled_N": N,
         "mean_accepted": float(g["n_acc"].mean()),
         "roofline": {
-            "kernel": "k_stream (draft step)",
+            "kernel": f"{DOMINANT} (draft step)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
@@ -290,8 +393,9 @@ def main() -> int:
         },
     }
     if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle on {args.cpu_requests} requests")
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, g, args.cpu_requests)
+        n_cpu = args.cpu_requests if args.cpu_requests > 0 else cfg.B
+        log(f"timing the CPU oracle on {n_cpu} requests")
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, g, n_cpu)
     print(json.dumps(line), flush=True)
     return 0
 
