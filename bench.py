@@ -39,9 +39,15 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(all_sources: bool = False) -> str:
+    """sha256 of the draft-stream kernel's sources (or of every library source)."""
+    rels = KERNEL_SOURCES
+    if all_sources:
+        csrc = os.path.join(ROOT, "draft_sampling_verification_markov_amd", "csrc")
+        rels = sorted(os.path.relpath(os.path.join(csrc, f), ROOT) for f in os.listdir(csrc)
+                      if f.endswith((".hip", ".hpp")))
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in rels:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -97,17 +103,32 @@ class Hip:
 DOMINANT = "k_draft"   # the draft-step vocabulary stream kernel
 
 
-def traffic_from_profile(workload: str):
-    """HBM bytes per draft-stream launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+def _profile_record(workload: str):
     path = os.path.join(PROFILE_DIR, f"{DOMINANT}_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return json.load(f)
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per draft-stream launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    rec = _profile_record(workload)
+    if rec is None or rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return float(rec["hbm_bytes_per_launch"])
+
+
+def step_traffic_from_profile(workload: str, K: int):
+    """HBM bytes of one whole step (every kernel, counter-measured, times its calls
+    per step: K for the draft stream and select, one for the others), if the
+    counters were taken on the current library sources; else None."""
+    rec = _profile_record(workload)
+    if rec is None or rec.get("all_sources_sha256") != kernel_source_hash(all_sources=True):
+        return None
+    per = rec.get("per_kernel_bytes", {})
+    return float(sum(v * (K if k in (DOMINANT, "k_select") else 1) for k, v in per.items()))
 
 
 def cpu_baseline(cfg, inp, gpu, n_req: int, min_seconds: float = 10.0):
@@ -223,7 +244,10 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
     lines += ["", f"Library source: commit {commit} (kernel sources sha256 {src[:16]}...)."]
     with open(os.path.join(PROFILE_DIR, f"cycle_{workload}_hbm_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
+    per_kernel = {k: (fetch[k] * fscale + write.get(k, 0.0) * wscale) * 1024 for k in fetch
+                  if k.startswith("k_")}
     rec = {"kernel": DOMINANT, "workload": workload, "commit": commit, "kernel_source_sha256": src,
+           "all_sources_sha256": kernel_source_hash(all_sources=True), "per_kernel_bytes": per_kernel,
            "fetch_kib_per_launch": fetch[DOMINANT], "write_kib_per_launch": write.get(DOMINANT, 0.0),
            "fetch_scale": fscale, "write_scale": wscale,
            "hbm_bytes_per_launch": (fetch[DOMINANT] * fscale + write.get(DOMINANT, 0.0) * wscale) * 1024,
@@ -357,6 +381,7 @@ def main() -> int:
     launch_bytes = stream_launch_bytes(cfg, G)
     achieved = launch_bytes / (k_ms / 1e3) / 1e9
     traffic = traffic_from_profile(cfg.name)
+    step_traffic = step_traffic_from_profile(cfg.name, cfg.K)
 
     line = {
         "metric": METRIC,
@@ -375,6 +400,7 @@ def main() -> int:
                    "logits": cfg.logits_dtype, "factors": cfg.weight_dtype, "T_s": cfg.T_s, "seed": cfg.seed},
         "hbm_gbs_algorithmic": alg_bytes / (ms_step / 1e3) / 1e9,
         "hbm_frac_algorithmic": alg_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "hbm_gbs_counters": None if step_traffic is None else step_traffic / (ms_step / 1e3) / 1e9,
         "algorithmic_bytes_per_step": alg_bytes,
         "logits_per_s": (positions + N) * cfg.V / (ms_step / 1e3),
         "ms_split": {"draft": split[0], "schedule": split[1], "verify": split[2]},
