@@ -405,6 +405,17 @@ struct Tiles {
   }
 };
 
+// Chunks [c_begin, c_end) of workgroup g of G: nchunks / G each, the first
+// nchunks % G workgroups one more.  32-bit arithmetic (nchunks < 2^24): the
+// 64-bit division it replaces cost hundreds of scalar instructions ahead of the
+// first DMA of every launch.
+__device__ __forceinline__ void chunk_range(int g, int G, int nchunks, int& c_begin, int& c_end) {
+  const unsigned q = (unsigned)nchunks / (unsigned)G, rem = (unsigned)nchunks - q * (unsigned)G;
+  const unsigned ug = (unsigned)g;
+  c_begin = (int)(ug * q + (ug < rem ? ug : rem));
+  c_end = c_begin + (int)q + (ug < rem ? 1 : 0);
+}
+
 // waits until every vector-memory operation of this wave has completed
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Workgroup barrier ordering LDS only: this wave's LDS operations complete
@@ -746,27 +757,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(StreamArgs a) {
 // these two independent tasks in opposite order, so one feeds the matrix pipe
 // while the other runs the VALU epilogue.  A fragments are read two K-steps
 // ahead of their MFMA.
+#ifndef DSPARK_DRAFT_PREFETCH
+#define DSPARK_DRAFT_PREFETCH 2
+#endif
 template <int R>
 struct DraftUnit {
   using T = DraftTiles<R>;
+  static constexpr int kPrefetch = DSPARK_DRAFT_PREFETCH;  // K-steps of A fragments read ahead
   __device__ __forceinline__ static void mma(const unsigned char* wtile, const bf16x8_t* bfrag, f32x16_t* acc) {
-    constexpr int S = T::kSteps, M = T::kMt;
-    bf16x8_t af[3][M];
+    constexpr int S = T::kSteps, M = T::kMt, D = kPrefetch;
+    bf16x8_t af[D + 1][M];
 #pragma unroll
-    for (int t = 0; t < 2 && t < S; ++t)
+    for (int t = 0; t < D && t < S; ++t)
 #pragma unroll
       for (int mt = 0; mt < M; ++mt)
         af[t][mt] = *reinterpret_cast<const bf16x8_t*>(wtile + mt * 32 * T::kWStride + 32 * t);
 #pragma unroll
     for (int t = 0; t < S; ++t) {
-      if (t + 2 < S) {
+      if (t + D < S) {
 #pragma unroll
         for (int mt = 0; mt < M; ++mt)
-          af[(t + 2) % 3][mt] = *reinterpret_cast<const bf16x8_t*>(wtile + mt * 32 * T::kWStride + 32 * (t + 2));
+          af[(t + D) % (D + 1)][mt] = *reinterpret_cast<const bf16x8_t*>(wtile + mt * 32 * T::kWStride + 32 * (t + D));
       }
+      // keep the prefetch D K-steps ahead: without this the scheduler sinks
+      // each read next to its MFMA and every MFMA pair waits a full LDS latency
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int mt = 0; mt < M; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t % 3][mt], bfrag[t], acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t % (D + 1)][mt], bfrag[t], acc[mt], 0, 0, 0);
     }
   }
   // accumulator <- this lane's 16 + 16 consecutive logits (entries 16h + [0,16) of each M-tile)
@@ -874,8 +892,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x, g = blockIdx.x;
-  const int c_begin = (int)(((long long)g * a.nchunks) / G);
-  const int c_end = (int)(((long long)(g + 1) * a.nchunks) / G);
+  int c_begin, c_end;
+  chunk_range(g, G, a.nchunks, c_begin, c_end);
   const int nc = c_end - c_begin;
   const uint16_t* Z = static_cast<const uint16_t*>(a.Z);
   const int V = a.V, K = a.K, B = a.B, k = a.k;
@@ -1166,8 +1184,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify_stream(StreamArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x, g = blockIdx.x;
-  const int c_begin = (int)(((long long)g * a.nchunks) / G);
-  const int c_end = (int)(((long long)(g + 1) * a.nchunks) / G);
+  int c_begin, c_end;
+  chunk_range(g, G, a.nchunks, c_begin, c_end);
   const int nunits = (c_end - c_begin) * T::kUnitsPerChunk;
   const int V = a.V, K = a.K, B = a.B;
   const float scale2 = a.scale2;
