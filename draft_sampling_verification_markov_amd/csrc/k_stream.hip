@@ -1340,6 +1340,9 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   __shared__ int s_cstar;
 
   const int j = tid >> 1, h = tid & 1;
+  // the partials first (G <= 256: at most one per thread), so that the merge
+  // waits for nothing else; then the previous token and its E half row
+  const float4 p = tid < a.G ? a.part[(size_t)b * a.G + tid] : make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
   const int prev = clamp_id(a.k == 1 ? a.anchor[b] : a.tok[(size_t)b * K + a.k - 2], V);
   HalfRow<WT, R> erow;
   erow.load(static_cast<const WT*>(a.E) + (size_t)prev * R, h);
@@ -1347,8 +1350,7 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   // 1. merge the per-workgroup partials of row b
   float m = -INFINITY, s = 0.f, best = -INFINITY;
   int bc = 0x7fffffff;
-  for (int i = tid; i < a.G; i += 256) {
-    const float4 p = a.part[(size_t)b * a.G + i];
+  if (tid < a.G) {
     lse2_merge(m, s, p.x, p.y);
     const int pc = __float_as_int(p.w);
     if (better(p.z, pc, best, bc)) {

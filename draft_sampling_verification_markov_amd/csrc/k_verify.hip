@@ -84,37 +84,66 @@ struct Vec16<float> {
   }
 };
 
+// Raw 16-byte pieces of one (row, segment) item, prefetched one item ahead.
+template <typename ZT>
+struct VlseItem {
+  static constexpr int kLoads = kVlseSeg / 256 / Vec16<ZT>::N;  // 16-byte loads per thread
+  uint4 raw[kLoads];
+  __device__ __forceinline__ void load(const ZT* row, int lo, int V, int tid) {
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      const int v = lo + (l * 256 + tid) * Vec16<ZT>::N;
+      raw[l] = *reinterpret_cast<const uint4*>(row + (v < V ? v : 0));  // past V: a valid address, masked below
+    }
+  }
+};
+
+template <typename ZT>
+__device__ __forceinline__ const ZT* vlse_row(const VerifyArgs& a, int w, int& b, int& k0, int& seg) {
+  const int j = w / a.nseg;
+  seg = w - j * a.nseg;
+  const int code = a.rows[j];
+  b = code >> 6;
+  k0 = code & 63;
+  return static_cast<const ZT*>(a.Zt) + ((size_t)b * (a.K + 1) + k0) * a.V;
+}
+
+// (row, segment) items, round-robin over the workgroups; the loads of the next
+// item are in flight while the current one is reduced.
 template <typename ZT>
 __global__ __launch_bounds__(256) void k_vlse(VerifyArgs a) {
   using Vec = Vec16<ZT>;
+  using It = VlseItem<ZT>;
   constexpr int kPer = kVlseSeg / 256;  // entries per thread
-  constexpr int kLoads = kPer / Vec::N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float s_m[4], s_s[4];
   const int M = *a.nrows;
   const int items = M * a.nseg;
-  const ZT* Zt = static_cast<const ZT*>(a.Zt);
-  for (int w = blockIdx.x; w < items; w += gridDim.x) {
-    const int j = w / a.nseg, seg = w - j * a.nseg;
-    const int code = a.rows[j];
-    const int b = code >> 6, k0 = code & 63;
-    const ZT* row = Zt + ((size_t)b * (a.K + 1) + k0) * a.V;
+  int w = blockIdx.x;
+  if (w >= items) return;
+  int b, k0, seg;
+  const ZT* row = vlse_row<ZT>(a, w, b, k0, seg);
+  It cur;
+  cur.load(row, seg * kVlseSeg, a.V, tid);
+  for (; w < items; w += gridDim.x) {
+    const int wn = w + gridDim.x;
+    int bn = 0, kn = 0, segn = 0;
+    It nxt;
+    if (wn < items) {
+      const ZT* rown = vlse_row<ZT>(a, wn, bn, kn, segn);
+      nxt.load(rown, segn * kVlseSeg, a.V, tid);
+    }
     const int lo = seg * kVlseSeg;
     float x[kPer];
     float m = -INFINITY;
 #pragma unroll
-    for (int l = 0; l < kLoads; ++l) {
+    for (int l = 0; l < It::kLoads; ++l) {
       const int v = lo + (l * 256 + tid) * Vec::N;
-      if (v < a.V) {
-        Vec::load(row + v, x + l * Vec::N);
+      Vec::load(reinterpret_cast<const ZT*>(&cur.raw[l]), x + l * Vec::N);
 #pragma unroll
-        for (int i = 0; i < Vec::N; ++i) {
-          x[l * Vec::N + i] *= a.scale2;
-          m = fmaxf(m, x[l * Vec::N + i]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < Vec::N; ++i) x[l * Vec::N + i] = -INFINITY;
+      for (int i = 0; i < Vec::N; ++i) {
+        x[l * Vec::N + i] = v < a.V ? x[l * Vec::N + i] * a.scale2 : -INFINITY;
+        m = fmaxf(m, x[l * Vec::N + i]);
       }
     }
     m = wave_max(m);
@@ -129,6 +158,10 @@ __global__ __launch_bounds__(256) void k_vlse(VerifyArgs a) {
     __syncthreads();
     if (tid == 0) a.vlse[((size_t)b * a.K + k0) * a.nseg + seg] = make_float2(m, s_s[0] + s_s[1] + s_s[2] + s_s[3]);
     __syncthreads();
+    cur = nxt;
+    b = bn;
+    k0 = kn;
+    seg = segn;
   }
 }
 
