@@ -23,6 +23,7 @@ Layout make_layout(const dspark_problem& P) {
   L.rpart = off;  off = align_up(off + (size_t)sched_segments((int)(B * K)) * B * K * sizeof(int32_t));
   L.sorts = off;  off = align_up(off + B * K * sizeof(float));
   L.sorti = off;  off = align_up(off + B * K * sizeof(int32_t));
+  L.lagn = off;   off = align_up(off + (B + 1) * sizeof(int32_t));
   L.efrag = off;  off = align_up(off + (size_t)((B + 31) / 32) * 32 * (size_t)P.r * 2);
   L.total = off;
   return L;
@@ -202,6 +203,27 @@ extern "C" dspark_status dspark_schedule(const dspark_problem* P, const float* s
   const Layout L = make_layout(*P);
   if (launch_schedule(*P, surv, T_table, n_sched, n_total, at<int32_t>(workspace, L.rpart),
                       at<float>(workspace, L.sorts), at<int32_t>(workspace, L.sorti), stream) != hipSuccess)
+    return DSPARK_E_LAUNCH;
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status dspark_schedule_async(const dspark_problem* P, const float* surv_lag, const float* surv,
+                                               const float* T_table, int32_t* n_sched, int32_t* n_total,
+                                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dspark_status st = check_problem(P);
+  if (st != DSPARK_OK) return st;
+  if (!surv_lag || !surv || !T_table || !n_sched || !n_total) return DSPARK_E_POINTER;
+  for (const void* q : {(const void*)surv_lag, (const void*)surv, (const void*)T_table, (const void*)n_sched,
+                        (const void*)n_total})
+    if (!aligned(q, 4)) return DSPARK_E_POINTER;
+  st = check_workspace(*P, workspace, workspace_bytes);
+  if (st != DSPARK_OK) return st;
+  (void)hipGetLastError();
+  const Layout L = make_layout(*P);
+  int32_t* lag = at<int32_t>(workspace, L.lagn);
+  if (launch_schedule_async(*P, surv_lag, surv, T_table, n_sched, n_total, at<int32_t>(workspace, L.rpart),
+                            at<float>(workspace, L.sorts), at<int32_t>(workspace, L.sorti), lag, lag + P->B,
+                            stream) != hipSuccess)
     return DSPARK_E_LAUNCH;
   return DSPARK_OK;
 }

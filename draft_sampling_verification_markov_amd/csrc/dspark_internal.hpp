@@ -35,6 +35,7 @@ struct Layout {
   size_t rpart; // int32 [S][B*K]: partial ranks of the candidates over S segments
   size_t sorts; // float [B*K]: survivals in schedule order (candidate sets too large for LDS)
   size_t sorti; // int32 [B*K]: candidate indices in schedule order (same)
+  size_t lagn;  // int32 [B + 1]: the lagged schedule of the asynchronous scheduler (n_b, then N)
   size_t efrag; // uint4 [ceil(B/32)][r/16][64]: E rows of the previous draft tokens, B-fragment order
   size_t total;
 };
@@ -145,6 +146,11 @@ constexpr int kSchedSegMax = 16;
 int sched_segments(int n);
 hipError_t launch_schedule(const dspark_problem& P, const float* surv, const float* T, int32_t* n_sched,
                            int32_t* n_total, int32_t* part, float* sorted_s, int32_t* sorted_i, hipStream_t s);
+// Asynchronous form: budget from surv_lag's first-drop schedule (into lag_n,
+// lag_total), then the leading candidates of surv in schedule order.
+hipError_t launch_schedule_async(const dspark_problem& P, const float* surv_lag, const float* surv, const float* T,
+                                 int32_t* n_sched, int32_t* n_total, int32_t* part, float* sorted_s,
+                                 int32_t* sorted_i, int32_t* lag_n, int32_t* lag_total, hipStream_t s);
 hipError_t launch_verify_pre(const dspark_problem& P, const VerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_finish(const dspark_problem& P, const VerifyArgs& a, hipStream_t s);
 

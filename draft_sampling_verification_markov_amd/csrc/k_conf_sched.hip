@@ -245,6 +245,23 @@ __global__ __launch_bounds__(kGreedyThreads) void k_sched_greedy_global(const fl
   sched_greedy<kGreedyThreads>(sorted_s, sorted_i, T, B, K, n_sched, n_total, s_wsum, s_wmin, &s_stop);
 }
 
+// Asynchronous budget: the first M = lag_total - B candidates of the current
+// schedule order are taken; one workgroup.
+__global__ __launch_bounds__(kGreedyThreads) void k_sched_topk(const int32_t* sorted_i, const int32_t* lag_total,
+                                                               int B, int K, int32_t* n_sched, int32_t* n_total) {
+  const int n = B * K, tid = threadIdx.x;
+  for (int b = tid; b < B; b += kGreedyThreads) n_sched[b] = 0;
+  int M = *lag_total - B;
+  M = M < 0 ? 0 : (M > n ? n : M);
+  __syncthreads();  // the zeroed counts (workgroup release) before the counting atomics at L2
+  for (int m = tid; m < M; m += kGreedyThreads) {
+    int idx = sorted_i[m];
+    idx = idx < 0 ? 0 : (idx >= n ? n - 1 : idx);
+    atomicAdd(&n_sched[idx / K], 1);
+  }
+  if (tid == 0) *n_total = B + M;
+}
+
 }  // namespace
 
 hipError_t launch_conf(const dspark_problem& P, const ConfArgs& a, hipStream_t s) {
@@ -279,6 +296,24 @@ hipError_t launch_schedule(const dspark_problem& P, const float* surv, const flo
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_sched_greedy_global, 1, kGreedyThreads, 0, s, sorted_s, sorted_i, T, P.B, P.K, n_sched,
                      n_total);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule_async(const dspark_problem& P, const float* surv_lag, const float* surv, const float* T,
+                                 int32_t* n_sched, int32_t* n_total, int32_t* part, float* sorted_s,
+                                 int32_t* sorted_i, int32_t* lag_n, int32_t* lag_total, hipStream_t s) {
+  hipError_t e = launch_schedule(P, surv_lag, T, lag_n, lag_total, part, sorted_s, sorted_i, s);
+  if (e != hipSuccess) return e;
+  const int n = P.B * P.K;
+  const int S = sched_segments(n);
+  hipLaunchKernelGGL(k_sched_rank, dim3((n + 255) / 256, S), 256, 0, s, surv, n, S, part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sched_scatter, (n + kScatterThreads - 1) / kScatterThreads, kScatterThreads, 0, s, surv, part,
+                     S, n, sorted_s, sorted_i);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sched_topk, 1, kGreedyThreads, 0, s, sorted_i, lag_total, P.B, P.K, n_sched, n_total);
   return hipGetLastError();
 }
 

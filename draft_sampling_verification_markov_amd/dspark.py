@@ -21,7 +21,7 @@ _DT = {"f32": F32, "bf16": BF16}
 _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 
 SYMBOLS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft", "dspark_draft_timed",
-           "dspark_schedule", "dspark_verify")
+           "dspark_schedule", "dspark_schedule_async", "dspark_verify")
 
 
 class Problem(ctypes.Structure):
@@ -72,6 +72,8 @@ def load() -> ctypes.CDLL:
     lib.dspark_draft_timed.restype = i32
     lib.dspark_schedule.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_schedule.restype = i32
+    lib.dspark_schedule_async.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dspark_schedule_async.restype = i32
     lib.dspark_verify.argtypes = [P] + [vp] * 14 + [vp, sz, vp]
     lib.dspark_verify.restype = i32
     _lib = lib
@@ -149,6 +151,15 @@ def schedule(P: Problem, surv, T_table, n_sched, n_total, workspace, stream=None
         _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
         _stream(stream))
     _check("dspark_schedule", st)
+
+
+def schedule_async(P: Problem, surv_lag, surv, T_table, n_sched, n_total, workspace, stream=None) -> None:
+    st = load().dspark_schedule_async(
+        ctypes.byref(P), _ptr(surv_lag, torch.float32, "surv_lag"), _ptr(surv, torch.float32, "surv"),
+        _ptr(T_table, torch.float32, "T_table"), _ptr(n_sched, torch.int32, "n_sched"),
+        _ptr(n_total, torch.int32, "n_total"), _ptr(workspace, None, "workspace"),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check("dspark_schedule_async", st)
 
 
 def verify(P: Problem, target, Z, E, Wt, anchor, draft_tok, draft_logq, draft_lse, n_sched,

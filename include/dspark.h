@@ -11,6 +11,8 @@
  *                      logits, tokens sampled position after position) and
  *                      Method > Confidence-scheduled verification (confidence
  *                      head, Sequential Temperature Scaling, prefix survival);
+ *   dspark_schedule_async -- Production deployment results (asynchronous
+ *                     dynamic top-k budget)
  *   dspark_schedule -- Method > Confidence-scheduled verification (hardware-aware
  *                      prefix scheduler against a step-time table profiled once
  *                      at start-up; greedy in survival order, stopping at the
@@ -160,6 +162,31 @@ dspark_status dspark_schedule(const dspark_problem* P,
                               const float* surv, const float* T_table,
                               int32_t* n_sched, int32_t* n_total,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_schedule_async -- the asynchronous "dynamic top-k" form of the
+ * scheduler (DSpark page, Production deployment results): the verification
+ * budget is sized from the confidence-head outputs of two steps earlier and
+ * filled with the current step's candidates in order of their latest
+ * cumulative confidence, so that the budget can be fixed ahead of the step
+ * (graph replay, overlapped scheduling).
+ *
+ * M = the number of candidates dspark_schedule would take on surv_lag (same
+ * table, same rule); then the first M current candidates in the order (surv
+ * descending, b ascending, k ascending) are taken.  Within a request a later
+ * position never precedes an earlier one, so each n_b is a prefix length and
+ * does not depend on the request's confidences beyond it.
+ *
+ * Inputs:  surv_lag [B][K] fp32, the survivals of two steps earlier (rows
+ *          non-increasing); surv [B][K] fp32, the current survivals (rows
+ *          non-increasing); T_table as for dspark_schedule.
+ * Outputs: n_sched [B] int32; n_total [1] int32 = B + M.
+ * Same errors as dspark_schedule; the workspace is used as scratch.
+ */
+dspark_status dspark_schedule_async(const dspark_problem* P,
+                                    const float* surv_lag, const float* surv, const float* T_table,
+                                    int32_t* n_sched, int32_t* n_total,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * dspark_verify -- lossless rejection-sampling verification.

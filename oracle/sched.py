@@ -26,8 +26,9 @@ Readings:
   candidate that fails;
 * n_b = number of request b's positions taken; N = B + sum_b n_b.
 
-The function is written with plain Python arithmetic so that it runs on
-floats or on exact ``fractions.Fraction`` values alike.
+The functions are written with plain Python arithmetic so that they run on
+floats or on exact ``fractions.Fraction`` values alike.  schedule_async() is
+the production variant (budget from lagged survivals, dynamic top-k).
 """
 from __future__ import annotations
 
@@ -79,3 +80,43 @@ def schedule(S, T):
         if s_in != 0:
             cut_gap = float((s_in - s_out) / s_in)
     return {"n": n, "N": N, "order": cands, "taken": taken, "margin": margin, "cut_gap": cut_gap}
+
+
+def schedule_async(S_lag, S, T):
+    """Asynchronous dynamic-top-k schedule.
+
+    DSpark page, Production deployment results: in production the scheduler
+    runs one step behind its inputs so that it fits graph replay and the
+    engine's overlapped scheduling.  It sizes the coming verification budget
+    from the confidence-head outputs of two steps earlier and fills that
+    budget with the current step's candidates ordered by their latest
+    cumulative confidence.
+
+    Readings: the budget is the number of candidates the first-drop schedule
+    takes on the lagged survivals S_lag (same B x K shape), M = taken(S_lag);
+    the current candidates are ordered as in schedule() (survival descending,
+    request ascending, position ascending) and the first M are taken.  Within
+    a request a later position never precedes an earlier one in that order,
+    so every selection is a prefix and [n_b >= j] does not depend on the
+    request's confidences after j.
+
+    Returns dict with n, N = B + M, M, capacity_margin (the lagged schedule's
+    margin) and cut_gap (relative survival gap between the M-th and the
+    (M+1)-th current candidate; inf if M is 0 or every candidate is taken).
+    """
+    lag = schedule(S_lag, T)
+    S = _as_seq(S)
+    B, K = len(S), len(S[0])
+    M = lag["taken"]
+    cands = [(S[b][k], b, k + 1) for b in range(B) for k in range(K)]
+    cands.sort(key=lambda t: (-t[0], t[1], t[2]))
+    n = [0] * B
+    for s, b, k in cands[:M]:
+        n[b] += 1
+    cut_gap = math.inf
+    if 0 < M < len(cands):
+        s_in, s_out = cands[M - 1][0], cands[M][0]
+        if s_in != 0:
+            cut_gap = float((s_in - s_out) / s_in)
+    return {"n": n, "N": B + M, "M": M, "capacity_margin": lag["margin"], "cut_gap": cut_gap, "order": cands}
+

@@ -28,8 +28,8 @@ def _declared():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == sorted(["dspark_draft", "dspark_draft_timed", "dspark_schedule", "dspark_verify",
-                                  "dspark_workspace_bytes", "dspark_status_string"])
+    assert _declared() == sorted(["dspark_draft", "dspark_draft_timed", "dspark_schedule", "dspark_schedule_async",
+                                  "dspark_verify", "dspark_workspace_bytes", "dspark_status_string"])
 
 
 def test_library_exports_every_declared_symbol(ds):
@@ -110,6 +110,12 @@ def test_null_and_misaligned_pointers(ds):
     st = lib.dspark_schedule(ctypes.byref(P), None, fake[0], fake[1], fake[2], ctypes.c_void_p(0x10000), 1 << 20,
                              None)
     assert st == ds.E_POINTER
+    # the asynchronous scheduler: missing lagged survivals, then a misaligned count buffer
+    st = lib.dspark_schedule_async(ctypes.byref(P), None, *fake[:4], ctypes.c_void_p(0x10000), 1 << 20, None)
+    assert st == ds.E_POINTER
+    st = lib.dspark_schedule_async(ctypes.byref(P), *fake[:3], ctypes.c_void_p(0x1002), fake[4],
+                                   ctypes.c_void_p(0x10000), 1 << 20, None)
+    assert st == ds.E_POINTER
 
 
 def test_workspace_checks(ds):
@@ -119,6 +125,8 @@ def test_workspace_checks(ds):
     fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(4)]
     for ws, nbytes in ((None, need), (ctypes.c_void_p(0x10080), need), (ctypes.c_void_p(0x10000), need - 1)):
         st = lib.dspark_schedule(ctypes.byref(P), *fake, ws, nbytes, None)
+        assert st == ds.E_WORKSPACE
+        st = lib.dspark_schedule_async(ctypes.byref(P), fake[0], *fake, ws, nbytes, None)
         assert st == ds.E_WORKSPACE
 
 

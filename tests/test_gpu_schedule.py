@@ -63,3 +63,36 @@ def test_schedule_sizes(lib, B, K, ties):
           f"{int((g != np.array(ref['n'])).sum())}", flush=True)
     np.testing.assert_array_equal(g, np.array(ref["n"]))
     assert int(n_total.item()) == ref["N"]
+
+
+ASYNC_CASES = [(256, 16, False), (700, 9, True), (1024, 32, False), (3000, 7, True)]
+
+
+@pytest.mark.parametrize("B,K,ties", ASYNC_CASES, ids=[f"B{b}_K{k}{'_ties' if t else ''}" for b, k, t in ASYNC_CASES])
+def test_schedule_async_sizes(lib, B, K, ties):
+    # budget from survivals two steps earlier (cliff table: decided exactly), the
+    # current candidates in schedule order; the comparison is exact
+    dspark = lib
+    n = B * K
+    print(f"[gpu] schedule_async B={B} K={K} n={n} ties={ties}", flush=True)
+    S_lag = synth.make_survivals(B, K, seed=6, ties=False)
+    S = synth.make_survivals(B, K, seed=5, ties=ties)
+    N0 = B + n // 5
+    T = np.where(np.arange(B * (K + 1) + 1) <= N0, 1.0, 100.0).astype(np.float32)
+    ref = osched.schedule_async(S_lag.astype(np.float64), S.astype(np.float64), T)
+    assert ref["N"] == N0
+    P = dspark.Problem.make(B, K, 1024, 16, 8)
+    ws = torch.empty(dspark.workspace_bytes(P), dtype=torch.uint8, device="cuda")
+    n_sched = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    n_total = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dspark.schedule_async(P, torch.from_numpy(S_lag).cuda(), torch.from_numpy(S).cuda(), torch.from_numpy(T).cuda(),
+                          n_sched, n_total, ws)
+    torch.cuda.synchronize()
+    g = n_sched.cpu().numpy()
+    print(f"[gpu]   N = {int(n_total.item())} (oracle {ref['N']}); requests differing: "
+          f"{int((g != np.array(ref['n'])).sum())}", flush=True)
+    np.testing.assert_array_equal(g, np.array(ref["n"]))
+    assert int(n_total.item()) == ref["N"]
+    # the synchronous schedule of the current survivals differs (a different budget): the lag matters
+    assert ref["N"] != osched.schedule(S.astype(np.float64),
+                                       np.where(np.arange(B * (K + 1) + 1) <= B + n // 3, 1.0, 100.0))["N"]
