@@ -353,6 +353,50 @@ def main() -> int:
         split += [ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]), ev[2].elapsed_time(ev[3])]
     split /= args.steps
 
+    # the asynchronous scheduler (budget from the survivals of two steps earlier):
+    # the current step's survivals and those of a step on another input set
+    runner.draft(P, sets[1], o)
+    surv_lag = o.surv.clone()
+    runner.draft(P, sets[0], o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dspark.schedule_async(P, surv_lag, o.surv, sets[0].T, o.n_sched, o.n_total, o.workspace)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_async = e0.elapsed_time(e1) / args.steps
+
+    # the verification baselines in place of the first-drop scheduler: whole
+    # cycles (draft, baseline schedule, verify) on the same inputs
+    def baseline_cycle(sched_fn):
+        for i in range(args.warmup):
+            xs = sets[i % 3]
+            runner.draft(P, xs, o)
+            sched_fn(xs)
+            runner.verify(P, xs, o)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            xs = sets[i % 3]
+            runner.draft(P, xs, o)
+            sched_fn(xs)
+            runner.verify(P, xs, o)
+        e1.record()
+        torch.cuda.synchronize()
+        h = o.host()
+        return {"ms_per_step": e0.elapsed_time(e1) / args.steps, "scheduled_N": int(h["n_total"][0]),
+                "mean_accepted": float(h["n_acc"].mean())}
+
+    baselines = {
+        f"fixed_gamma{cfg.K}": baseline_cycle(
+            lambda xs: dspark.schedule_fixed(P, cfg.K, o.n_sched, o.n_total)),
+        f"fixed_gamma{cfg.K // 4}": baseline_cycle(
+            lambda xs: dspark.schedule_fixed(P, cfg.K // 4, o.n_sched, o.n_total)),
+        "threshold_0.5": baseline_cycle(
+            lambda xs: dspark.schedule_threshold(P, o.surv, 0.5, o.n_sched, o.n_total)),
+    }
+
     # dominant kernel: the draft-step stream kernel, timed by events the library
     # records around each of its launches on the same stream
     hip = Hip()
@@ -404,6 +448,8 @@ def main() -> int:
         "algorithmic_bytes_per_step": alg_bytes,
         "logits_per_s": (positions + N) * cfg.V / (ms_step / 1e3),
         "ms_split": {"draft": split[0], "schedule": split[1], "verify": split[2]},
+        "ms_schedule_async": ms_async,
+        "baselines": baselines,
         "scheduled_N": N,
         "mean_accepted": float(g["n_acc"].mean()),
         "roofline": {

@@ -207,6 +207,32 @@ extern "C" dspark_status dspark_schedule(const dspark_problem* P, const float* s
   return DSPARK_OK;
 }
 
+extern "C" dspark_status dspark_schedule_fixed(const dspark_problem* P, int32_t gamma, int32_t* n_sched,
+                                               int32_t* n_total, hipStream_t stream) {
+  dspark_status st = check_problem(P);
+  if (st != DSPARK_OK) return st;
+  if (gamma < 0 || gamma > P->K) return DSPARK_E_INVALID;
+  if (!n_sched || !n_total) return DSPARK_E_POINTER;
+  if (!aligned(n_sched, 4) || !aligned(n_total, 4)) return DSPARK_E_POINTER;
+  (void)hipGetLastError();
+  if (launch_schedule_static(*P, nullptr, 0, gamma, 0.f, n_sched, n_total, stream) != hipSuccess)
+    return DSPARK_E_LAUNCH;
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status dspark_schedule_threshold(const dspark_problem* P, const float* surv, float theta,
+                                                   int32_t* n_sched, int32_t* n_total, hipStream_t stream) {
+  dspark_status st = check_problem(P);
+  if (st != DSPARK_OK) return st;
+  if (!isfinite(theta)) return DSPARK_E_INVALID;
+  if (!surv || !n_sched || !n_total) return DSPARK_E_POINTER;
+  for (const void* q : {(const void*)surv, (const void*)n_sched, (const void*)n_total})
+    if (!aligned(q, 4)) return DSPARK_E_POINTER;
+  (void)hipGetLastError();
+  if (launch_schedule_static(*P, surv, 1, 0, theta, n_sched, n_total, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+  return DSPARK_OK;
+}
+
 extern "C" dspark_status dspark_schedule_async(const dspark_problem* P, const float* surv_lag, const float* surv,
                                                const float* T_table, int32_t* n_sched, int32_t* n_total,
                                                void* workspace, size_t workspace_bytes, hipStream_t stream) {

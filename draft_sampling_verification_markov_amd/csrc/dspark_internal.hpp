@@ -146,6 +146,9 @@ constexpr int kSchedSegMax = 16;
 int sched_segments(int n);
 hipError_t launch_schedule(const dspark_problem& P, const float* surv, const float* T, int32_t* n_sched,
                            int32_t* n_total, int32_t* part, float* sorted_s, int32_t* sorted_i, hipStream_t s);
+// Baselines: mode 0 fixed length gamma, mode 1 survival threshold theta.
+hipError_t launch_schedule_static(const dspark_problem& P, const float* surv, int mode, int gamma, float theta,
+                                  int32_t* n_sched, int32_t* n_total, hipStream_t s);
 // Asynchronous form: budget from surv_lag's first-drop schedule (into lag_n,
 // lag_total), then the leading candidates of surv in schedule order.
 hipError_t launch_schedule_async(const dspark_problem& P, const float* surv_lag, const float* surv, const float* T,

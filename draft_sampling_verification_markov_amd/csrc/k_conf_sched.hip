@@ -262,6 +262,33 @@ __global__ __launch_bounds__(kGreedyThreads) void k_sched_topk(const int32_t* so
   if (tid == 0) *n_total = B + M;
 }
 
+// Fixed-length (mode 0) and survival-threshold (mode 1) baselines; one workgroup.
+__global__ __launch_bounds__(kGreedyThreads) void k_sched_static(const float* surv, int B, int K, int mode,
+                                                                 int gamma, float theta, int32_t* n_sched,
+                                                                 int32_t* n_total) {
+  __shared__ int s_sum[kGreedyThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int total = 0;
+  for (int b = tid; b < B; b += kGreedyThreads) {
+    int nb = gamma;
+    if (mode == 1) {
+      nb = 0;
+      while (nb < K && surv[(size_t)b * K + nb] >= theta) ++nb;
+    }
+    n_sched[b] = nb;
+    total += nb;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) total += __shfl_xor(total, o);
+  if (lane == 0) s_sum[wave] = total;
+  __syncthreads();
+  if (tid == 0) {
+    int t = 0;
+    for (int w = 0; w < kGreedyThreads / 64; ++w) t += s_sum[w];
+    *n_total = B + t;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_conf(const dspark_problem& P, const ConfArgs& a, hipStream_t s) {
@@ -314,6 +341,12 @@ hipError_t launch_schedule_async(const dspark_problem& P, const float* surv_lag,
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_sched_topk, 1, kGreedyThreads, 0, s, sorted_i, lag_total, P.B, P.K, n_sched, n_total);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule_static(const dspark_problem& P, const float* surv, int mode, int gamma, float theta,
+                                  int32_t* n_sched, int32_t* n_total, hipStream_t s) {
+  hipLaunchKernelGGL(k_sched_static, 1, kGreedyThreads, 0, s, surv, P.B, P.K, mode, gamma, theta, n_sched, n_total);
   return hipGetLastError();
 }
 

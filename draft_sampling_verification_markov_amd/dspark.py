@@ -21,7 +21,8 @@ _DT = {"f32": F32, "bf16": BF16}
 _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 
 SYMBOLS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft", "dspark_draft_timed",
-           "dspark_schedule", "dspark_schedule_async", "dspark_verify")
+           "dspark_schedule", "dspark_schedule_async", "dspark_schedule_fixed", "dspark_schedule_threshold",
+           "dspark_verify")
 
 
 class Problem(ctypes.Structure):
@@ -74,6 +75,10 @@ def load() -> ctypes.CDLL:
     lib.dspark_schedule.restype = i32
     lib.dspark_schedule_async.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_schedule_async.restype = i32
+    lib.dspark_schedule_fixed.argtypes = [P, i32, vp, vp, vp]
+    lib.dspark_schedule_fixed.restype = i32
+    lib.dspark_schedule_threshold.argtypes = [P, vp, ctypes.c_float, vp, vp, vp]
+    lib.dspark_schedule_threshold.restype = i32
     lib.dspark_verify.argtypes = [P] + [vp] * 14 + [vp, sz, vp]
     lib.dspark_verify.restype = i32
     _lib = lib
@@ -160,6 +165,19 @@ def schedule_async(P: Problem, surv_lag, surv, T_table, n_sched, n_total, worksp
         _ptr(n_total, torch.int32, "n_total"), _ptr(workspace, None, "workspace"),
         ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream))
     _check("dspark_schedule_async", st)
+
+
+def schedule_fixed(P: Problem, gamma: int, n_sched, n_total, stream=None) -> None:
+    st = load().dspark_schedule_fixed(ctypes.byref(P), int(gamma), _ptr(n_sched, torch.int32, "n_sched"),
+                                      _ptr(n_total, torch.int32, "n_total"), _stream(stream))
+    _check("dspark_schedule_fixed", st)
+
+
+def schedule_threshold(P: Problem, surv, theta: float, n_sched, n_total, stream=None) -> None:
+    st = load().dspark_schedule_threshold(ctypes.byref(P), _ptr(surv, torch.float32, "surv"), ctypes.c_float(theta),
+                                          _ptr(n_sched, torch.int32, "n_sched"),
+                                          _ptr(n_total, torch.int32, "n_total"), _stream(stream))
+    _check("dspark_schedule_threshold", st)
 
 
 def verify(P: Problem, target, Z, E, Wt, anchor, draft_tok, draft_logq, draft_lse, n_sched,

@@ -11,6 +11,8 @@
  *                      logits, tokens sampled position after position) and
  *                      Method > Confidence-scheduled verification (confidence
  *                      head, Sequential Temperature Scaling, prefix survival);
+ *   dspark_schedule_fixed, dspark_schedule_threshold -- Main results (the
+ *                     fixed-length and static-threshold baselines)
  *   dspark_schedule_async -- Production deployment results (asynchronous
  *                     dynamic top-k budget)
  *   dspark_schedule -- Method > Confidence-scheduled verification (hardware-aware
@@ -187,6 +189,24 @@ dspark_status dspark_schedule_async(const dspark_problem* P,
                                     const float* surv_lag, const float* surv, const float* T_table,
                                     int32_t* n_sched, int32_t* n_total,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_schedule_fixed / dspark_schedule_threshold -- the verification
+ * baselines the scheduler is compared against (DSpark page, Main results:
+ * offline benchmark with fixed-length blocks; static threshold sweep over the
+ * confidence head).
+ *
+ * fixed:     n_b = gamma for every request (0 <= gamma <= K).
+ * threshold: n_b = the longest prefix of positions with surv[b][k-1] >= theta
+ *            (theta finite; fp32 comparison).
+ * Outputs:   n_sched [B] int32; n_total [1] int32 = B + sum_b n_b.
+ * No workspace.  DSPARK_E_INVALID for gamma outside [0, K] or a non-finite theta;
+ * DSPARK_E_POINTER for NULL or misaligned (4-byte) pointers.
+ */
+dspark_status dspark_schedule_fixed(const dspark_problem* P, int32_t gamma,
+                                    int32_t* n_sched, int32_t* n_total, hipStream_t stream);
+dspark_status dspark_schedule_threshold(const dspark_problem* P, const float* surv, float theta,
+                                        int32_t* n_sched, int32_t* n_total, hipStream_t stream);
 
 /*
  * dspark_verify -- lossless rejection-sampling verification.

@@ -120,3 +120,28 @@ def schedule_async(S_lag, S, T):
             cut_gap = float((s_in - s_out) / s_in)
     return {"n": n, "N": B + M, "M": M, "capacity_margin": lag["margin"], "cut_gap": cut_gap, "order": cands}
 
+
+def schedule_fixed(B, K, gamma):
+    """Fixed-length verification (DSpark page, Main results > Offline
+    benchmark: the scheduler switched off, every drafter proposing a block of
+    fixed length): every request verifies min(gamma, K) positions."""
+    g = max(0, min(int(gamma), K))
+    return {"n": [g] * B, "N": B + B * g}
+
+
+def schedule_threshold(S, theta):
+    """Static-threshold verification (DSpark page, Main results: the static
+    threshold sweep over the confidence head).  Reading: request b verifies
+    the longest prefix of positions whose survival is at least theta."""
+    S = _as_seq(S)
+    n = []
+    for row in S:
+        c = 0
+        for s in row:
+            if s >= theta:
+                c += 1
+            else:
+                break
+        n.append(c)
+    return {"n": n, "N": len(S) + sum(n)}
+

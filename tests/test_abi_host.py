@@ -29,7 +29,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["dspark_draft", "dspark_draft_timed", "dspark_schedule", "dspark_schedule_async",
-                                  "dspark_verify", "dspark_workspace_bytes", "dspark_status_string"])
+                                  "dspark_schedule_fixed", "dspark_schedule_threshold", "dspark_verify",
+                                  "dspark_workspace_bytes", "dspark_status_string"])
 
 
 def test_library_exports_every_declared_symbol(ds):
@@ -116,6 +117,20 @@ def test_null_and_misaligned_pointers(ds):
     st = lib.dspark_schedule_async(ctypes.byref(P), *fake[:3], ctypes.c_void_p(0x1002), fake[4],
                                    ctypes.c_void_p(0x10000), 1 << 20, None)
     assert st == ds.E_POINTER
+
+
+def test_baseline_schedulers_validate(ds):
+    lib = ds.load()
+    P = _P(ds, B=4, K=3, V=1024, r=32, d=64)
+    fake = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(3)]
+    assert lib.dspark_schedule_fixed(ctypes.byref(P), -1, fake[0], fake[1], None) == ds.E_INVALID
+    assert lib.dspark_schedule_fixed(ctypes.byref(P), 4, fake[0], fake[1], None) == ds.E_INVALID
+    assert lib.dspark_schedule_fixed(ctypes.byref(P), 2, None, fake[1], None) == ds.E_POINTER
+    assert lib.dspark_schedule_fixed(ctypes.byref(P), 2, ctypes.c_void_p(0x1001), fake[1], None) == ds.E_POINTER
+    assert lib.dspark_schedule_threshold(ctypes.byref(P), fake[0], ctypes.c_float(float("nan")), fake[1], fake[2],
+                                         None) == ds.E_INVALID
+    assert lib.dspark_schedule_threshold(ctypes.byref(P), None, ctypes.c_float(0.5), fake[1], fake[2],
+                                         None) == ds.E_POINTER
 
 
 def test_workspace_checks(ds):

@@ -96,3 +96,34 @@ def test_schedule_async_sizes(lib, B, K, ties):
     # the synchronous schedule of the current survivals differs (a different budget): the lag matters
     assert ref["N"] != osched.schedule(S.astype(np.float64),
                                        np.where(np.arange(B * (K + 1) + 1) <= B + n // 3, 1.0, 100.0))["N"]
+
+
+STATIC_CASES = [(256, 16, False), (1500, 7, True), (1, 1, False), (2049, 32, True)]
+
+
+@pytest.mark.parametrize("B,K,ties", STATIC_CASES, ids=[f"B{b}_K{k}{'_ties' if t else ''}" for b, k, t in STATIC_CASES])
+def test_schedule_baselines(lib, B, K, ties):
+    """Fixed-length and static-threshold baselines, bit-exact against the oracle.
+    Thresholds include values equal to a survival (the comparison is >=, and
+    both sides compare the same fp32 numbers), 0, 1 and beyond."""
+    dspark = lib
+    print(f"[gpu] baselines B={B} K={K} ties={ties}", flush=True)
+    S = synth.make_survivals(B, K, seed=11, ties=ties)
+    P = dspark.Problem.make(B, K, 1024, 16, 8)
+    surv = torch.from_numpy(S).cuda()
+    n_sched = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    n_total = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for gamma in sorted({0, 1, K // 2, K}):
+        dspark.schedule_fixed(P, gamma, n_sched, n_total)
+        torch.cuda.synchronize()
+        ref = osched.schedule_fixed(B, K, gamma)
+        assert n_sched.cpu().tolist() == ref["n"] and int(n_total.item()) == ref["N"]
+    thetas = [0.0, 0.5, 1.0, 1.5, -1.0, float(S[0, min(1, K - 1)]), float(S[B // 2, 0])]
+    for theta in thetas:
+        dspark.schedule_threshold(P, surv, theta, n_sched, n_total)
+        torch.cuda.synchronize()
+        ref = osched.schedule_threshold(S, np.float32(theta))
+        assert n_sched.cpu().tolist() == list(ref["n"]), theta
+        assert int(n_total.item()) == ref["N"], theta
+    with pytest.raises(RuntimeError):
+        dspark.schedule_fixed(P, K + 1, n_sched, n_total)
