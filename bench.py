@@ -222,7 +222,10 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
         lines.append(f"| {_short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
     lines += ["", f"Library source: commit {commit} (kernel sources sha256 {src[:16]}...).",
-              "roll_cuda_kernel is torch.roll building the rotated input sets before the timed region."]
+              "roll_cuda_kernel is torch.roll building the rotated input sets before the timed region.",
+              "The verify kernels (k_rowlist, k_vlse, k_accept, k_verify_stream, k_finish) also run in the "
+              "baseline cycles, whose schedules are larger (the fixed length 16 verifies all B(K+1) rows), "
+              "so their averages mix schedule sizes; the cycle of the first-drop schedule is the minimum."]
     with open(os.path.join(PROFILE_DIR, f"cycle_{workload}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     # HBM counters, scaled by what the same counters read for a plain 1 GiB copy
