@@ -225,7 +225,7 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
               "roll_cuda_kernel is torch.roll building the rotated input sets before the timed region.",
               "The verify kernels (k_rowlist, k_vlse, k_accept, k_verify_stream, k_finish) also run in the "
               "baseline cycles, whose schedules are larger (the fixed length 16 verifies all B(K+1) rows), "
-              "so their averages mix schedule sizes; the cycle of the first-drop schedule is the minimum."]
+              "so their averages mix schedule sizes."]
     with open(os.path.join(PROFILE_DIR, f"cycle_{workload}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     # HBM counters, scaled by what the same counters read for a plain 1 GiB copy
