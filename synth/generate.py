@@ -142,3 +142,33 @@ def make_survivals(B: int, K: int, seed: int, ties: bool = False) -> np.ndarray:
     u = np.maximum(u, 2.0 ** -20)
     return -np.sort(-u, axis=1).astype(np.float32)
 
+
+
+def make_sts_samples(M: int, K: int, seed: int, censor: bool = True) -> tuple:
+    """Calibration samples for fitting per-position temperatures: raw confidences
+    c float32 [M, K] in (0, 1] (1% exactly 1), accepted lengths int32 [M] and
+    verified lengths int32 [M].  The acceptance chain is drawn from a head that is
+    overconfident: position k passes with probability 0.5 + 0.7 (c_k - 0.5) given
+    that every earlier position passed.  With ``censor`` half of the samples verify a random
+    length in [0, K] (so later positions are unobserved unless a rejection came
+    first); the others verify all K."""
+    rng = np.random.default_rng([seed, 91, M, K])
+    c = rng.uniform(0.35, 1.0, (M, K)).astype(np.float32)
+    c[rng.random((M, K)) < 0.01] = 1.0
+    passed = rng.random((M, K)) < 0.5 + 0.7 * (c.astype(np.float64) - 0.5)
+    chain = np.argmin(np.concatenate([passed, np.zeros((M, 1), bool)], axis=1), axis=1)
+    if censor:
+        n_ver = np.where(rng.random(M) < 0.5, K, rng.integers(0, K + 1, M))
+    else:
+        n_ver = np.full(M, K)
+    acc = np.minimum(chain, n_ver)
+    return c, acc.astype(np.int32), n_ver.astype(np.int32)
+
+
+def sts_grid(G: int = 129, lo: float = 0.25, hi: float = 4.0) -> np.ndarray:
+    """Candidate temperatures: G values spaced evenly in log between lo and hi
+    (float64), with the middle entry exactly 1 when G is odd and lo * hi = 1."""
+    g = np.exp(np.linspace(np.log(lo), np.log(hi), G))
+    if G % 2 == 1 and lo * hi == 1.0:
+        g[G // 2] = 1.0
+    return g
