@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -391,6 +392,42 @@ def main() -> int:
         return {"ms_per_step": e0.elapsed_time(e1) / args.steps, "scheduled_N": int(h["n_total"][0]),
                 "mean_accepted": float(h["n_acc"].mean())}
 
+    # STS fitting on (raw confidence, accepted length, verified length) triples
+    # produced by the verify path: 64 cycles at temperature 1 with every draft
+    # verified, then one fit of the K temperatures over a 129-point grid
+    n_cyc, G_sts, bins_sts = 64, 129, 15
+    M_sts = n_cyc * cfg.B
+    c_all = torch.empty((M_sts, cfg.K), dtype=torch.float32, device="cuda")
+    acc_all = torch.empty((M_sts,), dtype=torch.int32, device="cuda")
+    nv_all = torch.empty((M_sts,), dtype=torch.int32, device="cuda")
+    ones = torch.ones_like(sets[0].tau)
+    for i in range(n_cyc):
+        xs = dataclasses.replace(sets[i % 3], tau=ones)
+        runner.draft(P, xs, o)
+        dspark.schedule_fixed(P, cfg.K, o.n_sched, o.n_total)
+        runner.verify(P, xs, o)
+        c_all[i * cfg.B:(i + 1) * cfg.B].copy_(o.conf)
+        acc_all[i * cfg.B:(i + 1) * cfg.B].copy_(o.n_acc)
+        nv_all[i * cfg.B:(i + 1) * cfg.B].copy_(o.n_sched)
+    grid_sts = torch.from_numpy(synth.sts_grid(G_sts)).cuda()
+    sts_out = [torch.empty(cfg.K, dtype=torch.float64, device="cuda"), torch.empty(cfg.K, dtype=torch.int32, device="cuda"),
+               torch.empty(cfg.K, dtype=torch.float64, device="cuda"), torch.empty(cfg.K, dtype=torch.float64, device="cuda")]
+    ws_sts = torch.empty(dspark.sts_workspace_bytes(M_sts, cfg.K, G_sts, bins_sts), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        dspark.sts_fit(c_all, acc_all, nv_all, grid_sts, *sts_out, ws_sts, n_bins=bins_sts)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        dspark.sts_fit(c_all, acc_all, nv_all, grid_sts, *sts_out, ws_sts, n_bins=bins_sts)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_sts = e0.elapsed_time(e1) / args.steps
+    sts_line = {"samples": M_sts, "positions": cfg.K, "grid": G_sts, "bins": bins_sts, "ms": ms_sts,
+                "candidate_evals_per_s": (G_sts + 1) * M_sts * cfg.K / (ms_sts / 1e3),
+                "source": f"verify path: {n_cyc} cycles x {cfg.B} requests, raw confidences, all {cfg.K} drafts verified",
+                "ece_raw_mean": float(np.nanmean(sts_out[3].cpu().numpy())),
+                "ece_fit_mean": float(np.nanmean(sts_out[2].cpu().numpy()))}
+
     baselines = {
         f"fixed_gamma{cfg.K}": baseline_cycle(
             lambda xs: dspark.schedule_fixed(P, cfg.K, o.n_sched, o.n_total)),
@@ -453,6 +490,7 @@ def main() -> int:
         "ms_split": {"draft": split[0], "schedule": split[1], "verify": split[2]},
         "ms_schedule_async": ms_async,
         "baselines": baselines,
+        "sts_fit": sts_line,
         "scheduled_N": N,
         "mean_accepted": float(g["n_acc"].mean()),
         "roofline": {

@@ -233,6 +233,37 @@ extern "C" dspark_status dspark_schedule_threshold(const dspark_problem* P, cons
   return DSPARK_OK;
 }
 
+static bool sts_sizes_ok(int32_t M, int32_t K, int32_t G, int32_t n_bins) {
+  return M >= 0 && M <= (1 << 24) && K >= 1 && K <= 1024 && G >= 1 && G <= 4096 && n_bins >= 1 &&
+         n_bins <= kStsBinsMax;
+}
+
+extern "C" size_t dspark_sts_workspace_bytes(int32_t M, int32_t K, int32_t G, int32_t n_bins) {
+  if (!sts_sizes_ok(M, K, G, n_bins)) return 0;
+  return make_sts_layout(M, K, G, n_bins).total;
+}
+
+extern "C" dspark_status dspark_sts_fit(int32_t M, int32_t K, const float* conf_raw, const int32_t* acc_len,
+                                        const int32_t* n_verified, const double* tau_grid, int32_t G,
+                                        int32_t n_bins, double* tau, int32_t* tau_idx, double* ece_fit,
+                                        double* ece_raw, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  if (!sts_sizes_ok(M, K, G, n_bins)) return DSPARK_E_INVALID;
+  if (!tau_grid || !tau || !tau_idx || !ece_fit || !ece_raw) return DSPARK_E_POINTER;
+  if (M > 0 && (!conf_raw || !acc_len || !n_verified)) return DSPARK_E_POINTER;
+  for (const void* q : {(const void*)conf_raw, (const void*)acc_len, (const void*)n_verified, (const void*)tau_idx})
+    if (!aligned(q, 4)) return DSPARK_E_POINTER;
+  for (const void* q : {(const void*)tau_grid, (const void*)tau, (const void*)ece_fit, (const void*)ece_raw})
+    if (!aligned(q, 8)) return DSPARK_E_POINTER;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < make_sts_layout(M, K, G, n_bins).total)
+    return DSPARK_E_WORKSPACE;
+  (void)hipGetLastError();
+  if (launch_sts_fit(M, K, conf_raw, acc_len, n_verified, tau_grid, G, n_bins, tau, tau_idx, ece_fit, ece_raw,
+                     workspace, stream) != hipSuccess)
+    return DSPARK_E_LAUNCH;
+  return DSPARK_OK;
+}
+
 extern "C" dspark_status dspark_schedule_async(const dspark_problem* P, const float* surv_lag, const float* surv,
                                                const float* T_table, int32_t* n_sched, int32_t* n_total,
                                                void* workspace, size_t workspace_bytes, hipStream_t stream) {

@@ -146,6 +146,27 @@ constexpr int kSchedSegMax = 16;
 int sched_segments(int n);
 hipError_t launch_schedule(const dspark_problem& P, const float* surv, const float* T, int32_t* n_sched,
                            int32_t* n_total, int32_t* part, float* sorted_s, int32_t* sorted_i, hipStream_t s);
+// STS fitting: bin partial of one (candidate, sample split) pair.
+struct StsPart {
+  double sum;    // sum of predictions in the bin
+  uint32_t cnt;  // observed samples in the bin
+  uint32_t lab;  // of which accepted
+};
+constexpr int kStsBinsMax = 16;
+struct StsLayout {
+  int S;         // sample splits per candidate
+  size_t zl;     // double [K][M]: logits of the raw confidences
+  size_t fit;    // double [M]: running products with the fitted temperatures
+  size_t raw;    // double [M]: same at temperature 1
+  size_t part;   // StsPart [G+1][S][n_bins]
+  size_t total;
+};
+int sts_splits(int M);
+StsLayout make_sts_layout(int M, int K, int G, int n_bins);
+hipError_t launch_sts_fit(int M, int K, const float* c, const int32_t* acc, const int32_t* nver, const double* grid,
+                          int G, int n_bins, double* tau, int32_t* tau_idx, double* ece_fit, double* ece_raw,
+                          void* ws, hipStream_t s);
+
 // Baselines: mode 0 fixed length gamma, mode 1 survival threshold theta.
 hipError_t launch_schedule_static(const dspark_problem& P, const float* surv, int mode, int gamma, float theta,
                                   int32_t* n_sched, int32_t* n_total, hipStream_t s);

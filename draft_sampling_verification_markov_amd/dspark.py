@@ -22,7 +22,7 @@ _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 
 SYMBOLS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft", "dspark_draft_timed",
            "dspark_schedule", "dspark_schedule_async", "dspark_schedule_fixed", "dspark_schedule_threshold",
-           "dspark_verify")
+           "dspark_sts_workspace_bytes", "dspark_sts_fit", "dspark_verify")
 
 
 class Problem(ctypes.Structure):
@@ -75,6 +75,10 @@ def load() -> ctypes.CDLL:
     lib.dspark_schedule.restype = i32
     lib.dspark_schedule_async.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_schedule_async.restype = i32
+    lib.dspark_sts_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.dspark_sts_workspace_bytes.restype = sz
+    lib.dspark_sts_fit.argtypes = [i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.dspark_sts_fit.restype = i32
     lib.dspark_schedule_fixed.argtypes = [P, i32, vp, vp, vp]
     lib.dspark_schedule_fixed.restype = i32
     lib.dspark_schedule_threshold.argtypes = [P, vp, ctypes.c_float, vp, vp, vp]
@@ -178,6 +182,24 @@ def schedule_threshold(P: Problem, surv, theta: float, n_sched, n_total, stream=
                                           _ptr(n_sched, torch.int32, "n_sched"),
                                           _ptr(n_total, torch.int32, "n_total"), _stream(stream))
     _check("dspark_schedule_threshold", st)
+
+
+def sts_workspace_bytes(M: int, K: int, G: int, n_bins: int = 15) -> int:
+    return int(load().dspark_sts_workspace_bytes(int(M), int(K), int(G), int(n_bins)))
+
+
+def sts_fit(conf_raw, acc_len, n_verified, tau_grid, tau, tau_idx, ece_fit, ece_raw, workspace,
+            n_bins: int = 15, stream=None) -> None:
+    """Per-position STS temperatures by grid search on ECE (conf_raw [M][K] float32)."""
+    M, K = (int(x) for x in conf_raw.shape)
+    G = int(tau_grid.numel())
+    st = load().dspark_sts_fit(M, K, _ptr(conf_raw, torch.float32, "conf_raw"),
+                               _ptr(acc_len, torch.int32, "acc_len"), _ptr(n_verified, torch.int32, "n_verified"),
+                               _ptr(tau_grid, torch.float64, "tau_grid"), G, int(n_bins),
+                               _ptr(tau, torch.float64, "tau"), _ptr(tau_idx, torch.int32, "tau_idx"),
+                               _ptr(ece_fit, torch.float64, "ece_fit"), _ptr(ece_raw, torch.float64, "ece_raw"),
+                               _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    _check("dspark_sts_fit", st)
 
 
 def verify(P: Problem, target, Z, E, Wt, anchor, draft_tok, draft_logq, draft_lse, n_sched,

@@ -13,6 +13,8 @@
  *                      head, Sequential Temperature Scaling, prefix survival);
  *   dspark_schedule_fixed, dspark_schedule_threshold -- Main results (the
  *                     fixed-length and static-threshold baselines)
+ *   dspark_sts_fit  -- Method > Confidence-scheduled verification (fitting the
+ *                      STS temperatures left to right by grid search on ECE)
  *   dspark_schedule_async -- Production deployment results (asynchronous
  *                     dynamic top-k budget)
  *   dspark_schedule -- Method > Confidence-scheduled verification (hardware-aware
@@ -207,6 +209,43 @@ dspark_status dspark_schedule_fixed(const dspark_problem* P, int32_t gamma,
                                     int32_t* n_sched, int32_t* n_total, hipStream_t stream);
 dspark_status dspark_schedule_threshold(const dspark_problem* P, const float* surv, float theta,
                                         int32_t* n_sched, int32_t* n_total, hipStream_t stream);
+
+/*
+ * dspark_sts_workspace_bytes / dspark_sts_fit -- fitting the Sequential
+ * Temperature Scaling temperatures (Method > Confidence-scheduled verification,
+ * the STS paragraph; Main results for the calibration it reaches).
+ *
+ * Left to right over the K positions, with the temperatures of earlier
+ * positions fixed, a one-dimensional search over the caller's grid picks the
+ * temperature tau_k that minimises the Expected Calibration Error of the
+ * survival S_k = S_{k-1} * sigmoid(logit(c_k) / tau_k) (logit(c) = ln c - ln(1-c),
+ * S_0 = 1) against the label "accepted length >= k", over the samples that
+ * verified position k (k <= n_verified[m]).  ECE uses n_bins equal-width bins
+ * on [0, 1] (bin = min(floor(p * n_bins), n_bins - 1)):
+ *   ECE = sum over bins |sum of predictions - accepted count| / observed count.
+ * Arithmetic is float64.  Grid entries that are not finite and positive are
+ * never chosen; ties go to the smallest index.  A position with no observed
+ * sample, or no usable grid entry, keeps tau = 1 with tau_idx = -1 and a NaN
+ * ece_fit (ece_raw is NaN only when nothing is observed).
+ *
+ *   conf_raw   [M][K] float32  raw confidences (the head at temperature 1), in [0, 1]
+ *   acc_len    [M] int32       accepted drafts of each sample (0..n_verified)
+ *   n_verified [M] int32       drafts each sample verified (0..K)
+ *   tau_grid   [G] float64     candidate temperatures
+ *   tau        [K] float64     out: fitted temperatures
+ *   tau_idx    [K] int32       out: their grid indices (-1: kept at 1)
+ *   ece_fit    [K] float64     out: ECE of the fitted survival
+ *   ece_raw    [K] float64     out: ECE of the raw survival (every tau = 1)
+ * Limits: 0 <= M <= 2^24, 1 <= K <= 1024, 1 <= G <= 4096, 1 <= n_bins <= 16
+ * (DSPARK_E_INVALID otherwise; the workspace size is then 0).  Float64 arrays
+ * 8-byte aligned, the others 4-byte (DSPARK_E_POINTER).  Workspace as for the
+ * other entry points, at least dspark_sts_workspace_bytes(M, K, G, n_bins).
+ */
+size_t dspark_sts_workspace_bytes(int32_t M, int32_t K, int32_t G, int32_t n_bins);
+dspark_status dspark_sts_fit(int32_t M, int32_t K, const float* conf_raw, const int32_t* acc_len,
+                             const int32_t* n_verified, const double* tau_grid, int32_t G, int32_t n_bins,
+                             double* tau, int32_t* tau_idx, double* ece_fit, double* ece_raw,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * dspark_verify -- lossless rejection-sampling verification.

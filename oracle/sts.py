@@ -78,7 +78,8 @@ def sts_fit(c: np.ndarray, acc_len: np.ndarray, n_verified: np.ndarray, grid: np
     c [M][K] raw confidences (float32 values), acc_len [M] accepted drafts,
     n_verified [M] verified drafts, grid [G] candidate temperatures.
     Returns tau [K], idx [K], ece_fit [K], ece_raw [K] and the decision margin
-    of each position (relative gap between the best and the runner-up ECE).
+    of each position (the runner-up ECE minus the best, over distinct grid
+    indices; 0 for equal grid values).
     """
     c = np.asarray(c)
     M, K = c.shape
@@ -111,7 +112,7 @@ def sts_fit(c: np.ndarray, acc_len: np.ndarray, n_verified: np.ndarray, grid: np
                 tau[j], idx[j], ece_fit[j] = grid[best_g], best_g, best_e
                 rest = [e for e, g in scores if g != best_g]
                 if rest:
-                    margin[j] = (min(rest) - best_e) / max(best_e, 1e-300)
+                    margin[j] = min(rest) - best_e
         s_fit = s_fit * sigmoid(z[:, j] / tau[j])
         s_raw = s_raw * sigmoid(z[:, j])
     return {"tau": tau, "idx": idx, "ece_fit": ece_fit, "ece_raw": ece_raw, "margin": margin}

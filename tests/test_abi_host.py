@@ -29,8 +29,9 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["dspark_draft", "dspark_draft_timed", "dspark_schedule", "dspark_schedule_async",
-                                  "dspark_schedule_fixed", "dspark_schedule_threshold", "dspark_verify",
-                                  "dspark_workspace_bytes", "dspark_status_string"])
+                                  "dspark_schedule_fixed", "dspark_schedule_threshold", "dspark_sts_fit",
+                                  "dspark_sts_workspace_bytes", "dspark_verify", "dspark_workspace_bytes",
+                                  "dspark_status_string"])
 
 
 def test_library_exports_every_declared_symbol(ds):
@@ -131,6 +132,30 @@ def test_baseline_schedulers_validate(ds):
                                          None) == ds.E_INVALID
     assert lib.dspark_schedule_threshold(ctypes.byref(P), None, ctypes.c_float(0.5), fake[1], fake[2],
                                          None) == ds.E_POINTER
+
+
+def test_sts_validation(ds):
+    lib = ds.load()
+    assert lib.dspark_sts_workspace_bytes(1000, 16, 129, 15) > 16 * 1000 * 8
+    for bad in [(-1, 4, 8, 15), (10, 0, 8, 15), (10, 4, 0, 15), (10, 4, 8, 0), (10, 4, 8, 17), (10, 4, 5000, 15)]:
+        assert lib.dspark_sts_workspace_bytes(*bad) == 0
+    f = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(10)]
+    ws = ctypes.c_void_p(0x100000)
+    need = lib.dspark_sts_workspace_bytes(10, 4, 8, 15)
+    ok = dict(M=10, K=4, c=f[0], a=f[1], n=f[2], g=f[3], G=8, nb=15, t=f[4], i=f[5], ef=f[6], er=f[7])
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.dspark_sts_fit(a["M"], a["K"], a["c"], a["a"], a["n"], a["g"], a["G"], a["nb"], a["t"], a["i"],
+                                  a["ef"], a["er"], kw.get("ws", ws), kw.get("wsb", need), None)
+    assert call(nb=17) == ds.E_INVALID
+    assert call(K=0) == ds.E_INVALID
+    assert call(g=None) == ds.E_POINTER
+    assert call(c=None) == ds.E_POINTER
+    assert call(t=ctypes.c_void_p(0x1004)) == ds.E_POINTER   # float64 output needs 8-byte alignment
+    assert call(ws=None) == ds.E_WORKSPACE
+    assert call(wsb=need - 1) == ds.E_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x100010)) == ds.E_WORKSPACE
 
 
 def test_workspace_checks(ds):
