@@ -20,4 +20,4 @@ status: every function is pinned by ``tests/test_oracle_*.py`` (known-answer
 vectors, closed forms, exhaustive enumeration, chi-square sampling tests and
 special cases); no function is parity-unpinned.
 """
-from . import philox, sampling, draft, conf, sched, sts, verify, cycle  # noqa: F401
+from . import philox, sampling, draft, rnn, conf, sched, sts, verify, cycle  # noqa: F401

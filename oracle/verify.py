@@ -19,8 +19,9 @@ Kalman, Matias 2023; Chen et al. 2023):
 * emitted: x_1 .. x_{a_b}, then the drawn token, which is the next anchor.
 
 Readings: p_k = softmax(Zt[b, k] / T_s) (the sampling temperature applies to
-the target too); q_k is the Markov-head draft distribution of ``draft``
-recomputed from the prefix; if the residual mass is exactly zero (possible
+the target too); q_k is the draft distribution recomputed from the prefix:
+the Markov head's (``draft``) or, when the projection operands ``vec`` of the
+positions are given, the one those operands define (the RNN head, ``rnn``); if the residual mass is exactly zero (possible
 only through rounding) the token is drawn from p_k* with purposes 4/5.
 ``accept_probability`` and ``residual_weights`` use plain arithmetic so the
 enumeration tests can run them on exact fractions.
@@ -49,8 +50,10 @@ def residual_weights(p, q):
     return np.where(d > 0, d, 0 * d)
 
 
-def verify_request(b: int, n_b: int, x_row, Zt_b, Z_b, E64, W64, anchor_b: int, T_s: float, seed: int):
-    """Verify request b's first n_b draft tokens.  Zt_b: (K+1, V) target rows; Z_b: (K, V) base rows."""
+def verify_request(b: int, n_b: int, x_row, Zt_b, Z_b, E64, W64, anchor_b: int, T_s: float, seed: int,
+                   vec_b=None):
+    """Verify request b's first n_b draft tokens.  Zt_b: (K+1, V) target rows; Z_b: (K, V) base rows;
+    vec_b: (K, r) projection operands of the positions (None: E of the previous token)."""
     K = len(x_row)
     x_row = [int(t) for t in x_row]
     logp = np.full(K, np.nan)
@@ -61,8 +64,11 @@ def verify_request(b: int, n_b: int, x_row, Zt_b, Z_b, E64, W64, anchor_b: int, 
         logp[k - 1] = lp[x_row[k - 1]] - logsumexp(lp)
     accept_margin = math.inf
     for k in range(1, n_b + 1):
-        prev = int(anchor_b) if k == 1 else x_row[k - 2]
-        ell = markov_logits(Z_b[k - 1][None, :], E64, W64, prev, T_s)[0]
+        if vec_b is None:
+            prev = int(anchor_b) if k == 1 else x_row[k - 2]
+            ell = markov_logits(Z_b[k - 1][None, :], E64, W64, prev, T_s)[0]
+        else:
+            ell = (f64(Z_b[k - 1]) + np.asarray(vec_b[k - 1], np.float64) @ W64.T) / float(T_s)
         lse_q = logsumexp(ell)
         logq_k = ell[x_row[k - 1]] - lse_q
         a = accept_probability(math.exp(logp[k - 1]), math.exp(logq_k))
@@ -91,9 +97,11 @@ def verify_request(b: int, n_b: int, x_row, Zt_b, Z_b, E64, W64, anchor_b: int, 
             "kind": "bonus", "k_star": 0, "accept_margin": accept_margin, "token_margin": tmargin}
 
 
-def verify(Zt, Z, E, Wt, anchor, x, n, T_s: float, seed: int, requests=None):
-    """Verify every listed request (default: all).  Returns a list of per-request dicts."""
+def verify(Zt, Z, E, Wt, anchor, x, n, T_s: float, seed: int, requests=None, vec=None):
+    """Verify every listed request (default: all).  Returns a list of per-request dicts.
+    vec: (B, K, r) projection operands (RNN head), indexed by request like Z."""
     B = Z.shape[0]
     reqs = range(B) if requests is None else [int(b) for b in requests]
     E64, W64 = f64(E), f64(Wt)
-    return [verify_request(b, int(n[b]), x[b], Zt[b], Z[b], E64, W64, int(anchor[b]), T_s, seed) for b in reqs]
+    return [verify_request(b, int(n[b]), x[b], Zt[b], Z[b], E64, W64, int(anchor[b]), T_s, seed,
+                           None if vec is None else vec[b]) for b in reqs]

@@ -7,7 +7,8 @@ anchors and the step-time table).  Both the CPU oracle (``oracle/``) and the
 GPU path consume exactly the bytes produced here.
 """
 from .configs import CONFIGS, Config, get_config
-from .generate import make_inputs, make_survivals, make_sts_samples, sts_grid, bf16_bits_from_f32, T_table
+from .generate import (make_inputs, make_survivals, make_sts_samples, sts_grid, make_rnn_weights,
+                       bf16_bits_from_f32, T_table)
 
-__all__ = ["CONFIGS", "Config", "get_config", "make_inputs", "make_survivals", "make_sts_samples", "sts_grid",
+__all__ = ["CONFIGS", "Config", "get_config", "make_inputs", "make_survivals", "make_sts_samples", "sts_grid", "make_rnn_weights",
            "bf16_bits_from_f32", "T_table"]

@@ -172,3 +172,20 @@ def sts_grid(G: int = 129, lo: float = 0.25, hi: float = 4.0) -> np.ndarray:
     if G % 2 == 1 and lo * hi == 1.0:
         g[G // 2] = 1.0
     return g
+
+
+def make_rnn_weights(cfg: Config) -> dict:
+    """Weights of the gated recurrent head for a workload: W_ih (3r, d + r) over the
+    input [h_k; E[x_{k-1}]], W_hh (3r, r), biases b_ih, b_hh (3r,) float32.  The
+    matrices are stored in the workload's factor dtype.  Scales put every
+    pre-activation near unit variance: h columns 1 / (h_std sqrt(d)), E columns
+    1 / (ew_std sqrt(r)), W_hh 1 / sqrt(r); biases N(0, 0.1^2)."""
+    d, r = cfg.d, cfg.r
+    g = _rng(cfg, 20)
+    Wh = g.standard_normal((3 * r, d), dtype=np.float32) * np.float32(1.0 / (cfg.h_std * np.sqrt(d)))
+    We = _rng(cfg, 21).standard_normal((3 * r, r), dtype=np.float32) * np.float32(1.0 / (cfg.ew_std * np.sqrt(r)))
+    W_hh = _rng(cfg, 22).standard_normal((3 * r, r), dtype=np.float32) * np.float32(1.0 / np.sqrt(r))
+    bb = _rng(cfg, 23).standard_normal((2, 3 * r), dtype=np.float32) * np.float32(0.1)
+    return {"W_ih": _store(np.concatenate([Wh, We], axis=1), cfg.weight_dtype),
+            "W_hh": _store(W_hh, cfg.weight_dtype),
+            "b_ih": bb[0].astype(np.float32), "b_hh": bb[1].astype(np.float32)}
