@@ -84,14 +84,30 @@ extern "C" const char* dspark_status_string(int status) {
   }
 }
 
+// The RNN head's weights and its state output (absent for the Markov head).
+struct RnnDraft {
+  const void* W_ih;
+  const float* b_ih;
+  const void* W_hh;
+  const float* b_hh;
+  float* state;
+};
+
 static dspark_status draft_impl(const dspark_problem* P, const void* Z, const void* E, const void* Wt,
                                 const void* h, const float* w_conf, float b_conf, const float* tau,
                                 const int32_t* anchor, int32_t* draft_tok, float* draft_logq, float* draft_lse,
                                 float* conf, float* surv, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream, hipEvent_t* events) {
+                                hipStream_t stream, hipEvent_t* events, const RnnDraft* rnn = nullptr) {
   dspark_status st = check_problem(P);
   if (st != DSPARK_OK) return st;
   const dspark_problem& p = *P;
+  if (rnn) {
+    if (!rnn_supported(p)) return DSPARK_E_UNSUPPORTED;
+    if (!rnn->W_ih || !rnn->b_ih || !rnn->W_hh || !rnn->b_hh || !rnn->state) return DSPARK_E_POINTER;
+    if (!aligned(rnn->W_ih, 16) || !aligned(rnn->W_hh, 16) || !aligned(rnn->state, 16) || !aligned(rnn->b_ih, 4) ||
+        !aligned(rnn->b_hh, 4))
+      return DSPARK_E_POINTER;
+  }
   if (!Z || !E || !Wt || !h || !w_conf || !tau || !anchor || !draft_tok || !draft_logq || !draft_lse || !conf ||
       !surv)
     return DSPARK_E_POINTER;
@@ -102,6 +118,7 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
     if (!aligned(q, 4)) return DSPARK_E_POINTER;
   st = check_workspace(p, workspace, workspace_bytes);
   if (st != DSPARK_OK) return st;
+  if (rnn && workspace_bytes < make_layout(p).total + rnn_extra_bytes(p)) return DSPARK_E_WORKSPACE;
   (void)hipGetLastError();
 
   const Layout L = make_layout(p);
@@ -140,11 +157,22 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
   se.inv_T = 1.0f / p.sampling_temp;
   se.key = sa.key;
 
-  if (use_efrag && launch_efrag_gather(p, E, anchor, efrag, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+  float* Gh = rnn ? at<float>(workspace, L.total) : nullptr;
+  if (rnn) {
+    se.state = rnn->state;
+    if (launch_rnn_gemm(p, h, rnn->W_ih, rnn->b_ih, Gh, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+  } else if (use_efrag && launch_efrag_gather(p, E, anchor, efrag, stream) != hipSuccess) {
+    return DSPARK_E_LAUNCH;
+  }
   for (int k = 1; k <= p.K; ++k) {
     sa.k = k;
     se.k = k;
-    se.efrag = use_efrag && k < p.K ? efrag : nullptr;  // fragments of position k feed step k + 1
+    // Markov head: the select kernel stores the fragments of position k for step k + 1;
+    // RNN head: the step kernel stores those of the state of position k before step k
+    se.efrag = !rnn && use_efrag && k < p.K ? efrag : nullptr;
+    if (rnn && launch_rnn_step(p, Gh, rnn->W_ih, rnn->W_hh, rnn->b_hh, E, anchor, draft_tok, rnn->state, efrag, k,
+                               stream) != hipSuccess)
+      return DSPARK_E_LAUNCH;
     if (events && hipEventRecord(events[2 * (k - 1)], stream) != hipSuccess) return DSPARK_E_LAUNCH;
     if (launch_stream_draft(p, sa, L.G, stream) != hipSuccess) return DSPARK_E_LAUNCH;
     if (events && hipEventRecord(events[2 * (k - 1) + 1], stream) != hipSuccess) return DSPARK_E_LAUNCH;
@@ -187,6 +215,22 @@ extern "C" dspark_status dspark_draft_timed(const dspark_problem* P, const void*
   if (!events) return DSPARK_E_POINTER;
   return draft_impl(P, Z, E, Wt, h, w_conf, b_conf, tau, anchor, draft_tok, draft_logq, draft_lse, conf, surv,
                     workspace, workspace_bytes, stream, events);
+}
+
+extern "C" size_t dspark_rnn_workspace_bytes(const dspark_problem* P) {
+  if (check_problem(P) != DSPARK_OK) return 0;
+  return make_layout(*P).total + rnn_extra_bytes(*P);
+}
+
+extern "C" dspark_status dspark_draft_rnn(const dspark_problem* P, const void* Z, const void* E, const void* Wt,
+                                          const void* h, const void* W_ih, const float* b_ih, const void* W_hh,
+                                          const float* b_hh, const float* w_conf, float b_conf, const float* tau,
+                                          const int32_t* anchor, int32_t* draft_tok, float* draft_logq,
+                                          float* draft_lse, float* conf, float* surv, float* state, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  const RnnDraft rnn{W_ih, b_ih, W_hh, b_hh, state};
+  return draft_impl(P, Z, E, Wt, h, w_conf, b_conf, tau, anchor, draft_tok, draft_logq, draft_lse, conf, surv,
+                    workspace, workspace_bytes, stream, nullptr, &rnn);
 }
 
 extern "C" dspark_status dspark_schedule(const dspark_problem* P, const float* surv, const float* T_table,
@@ -285,15 +329,19 @@ extern "C" dspark_status dspark_schedule_async(const dspark_problem* P, const fl
   return DSPARK_OK;
 }
 
-extern "C" dspark_status dspark_verify(const dspark_problem* P, const void* target, const void* Z, const void* E,
-                                       const void* Wt, const int32_t* anchor, const int32_t* draft_tok,
-                                       const float* draft_logq, const float* draft_lse, const int32_t* n_sched,
-                                       int32_t* out_tok, int32_t* n_accepted, int32_t* next_anchor, float* logp,
-                                       float* resid_mass, void* workspace, size_t workspace_bytes,
-                                       hipStream_t stream) {
+static dspark_status verify_impl(const dspark_problem* P, const void* target, const void* Z, const void* E,
+                                 const void* Wt, const int32_t* anchor, const int32_t* draft_tok,
+                                 const float* draft_logq, const float* draft_lse, const int32_t* n_sched,
+                                 int32_t* out_tok, int32_t* n_accepted, int32_t* next_anchor, float* logp,
+                                 float* resid_mass, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                 const float* state) {
   dspark_status st = check_problem(P);
   if (st != DSPARK_OK) return st;
   const dspark_problem& p = *P;
+  if (state) {
+    if (!rnn_supported(p)) return DSPARK_E_UNSUPPORTED;
+    if (!aligned(state, 16)) return DSPARK_E_POINTER;
+  }
   if (!target || !Z || !E || !Wt || !anchor || !draft_tok || !draft_logq || !draft_lse || !n_sched || !out_tok ||
       !n_accepted || !next_anchor || !logp || !resid_mass)
     return DSPARK_E_POINTER;
@@ -340,6 +388,7 @@ extern "C" dspark_status dspark_verify(const dspark_problem* P, const void* targ
   va.scale2 = kLog2e / p.sampling_temp;
   va.key = host_key(p.seed);
   va.efrag = verify_uses_efrag(p) ? at<uint4>(workspace, L.efrag) : nullptr;
+  va.state = state;
   if (launch_verify_pre(p, va, stream) != hipSuccess) return DSPARK_E_LAUNCH;
 
   StreamArgs sa{};
@@ -365,4 +414,25 @@ extern "C" dspark_status dspark_verify(const dspark_problem* P, const void* targ
   if (launch_stream_verify(p, sa, L.G, stream) != hipSuccess) return DSPARK_E_LAUNCH;
   if (launch_verify_finish(p, va, stream) != hipSuccess) return DSPARK_E_LAUNCH;
   return DSPARK_OK;
+}
+
+extern "C" dspark_status dspark_verify(const dspark_problem* P, const void* target, const void* Z, const void* E,
+                                       const void* Wt, const int32_t* anchor, const int32_t* draft_tok,
+                                       const float* draft_logq, const float* draft_lse, const int32_t* n_sched,
+                                       int32_t* out_tok, int32_t* n_accepted, int32_t* next_anchor, float* logp,
+                                       float* resid_mass, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  return verify_impl(P, target, Z, E, Wt, anchor, draft_tok, draft_logq, draft_lse, n_sched, out_tok, n_accepted,
+                     next_anchor, logp, resid_mass, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" dspark_status dspark_verify_rnn(const dspark_problem* P, const void* target, const void* Z,
+                                           const void* E, const void* Wt, const int32_t* anchor,
+                                           const int32_t* draft_tok, const float* draft_logq, const float* draft_lse,
+                                           const float* state, const int32_t* n_sched, int32_t* out_tok,
+                                           int32_t* n_accepted, int32_t* next_anchor, float* logp, float* resid_mass,
+                                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!state) return DSPARK_E_POINTER;
+  return verify_impl(P, target, Z, E, Wt, anchor, draft_tok, draft_logq, draft_lse, n_sched, out_tok, n_accepted,
+                     next_anchor, logp, resid_mass, workspace, workspace_bytes, stream, state);
 }

@@ -90,6 +90,21 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+// float -> bfloat16 bits, round to nearest, ties to even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+// eight consecutive floats rounded to bfloat16, as one 16-byte piece
+__device__ __forceinline__ uint4 bf16x8_from_f32(const float* p) {
+  const float4 x0 = reinterpret_cast<const float4*>(p)[0], x1 = reinterpret_cast<const float4*>(p)[1];
+  return make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
+                    pack_bf16x2(x1.z, x1.w));
+}
 
 // Token id used as an index, clamped into [0, V) so that a corrupt id cannot
 // address outside the factor tables.
@@ -176,6 +191,27 @@ __device__ __forceinline__ float half_dot<uint16_t>(const uint16_t* E, const uin
   return acc;
 }
 
+// The same product with the operand taken from a float row rounded to bfloat16
+// (the RNN head's state) instead of a row of E.
+__device__ __forceinline__ float half_dot_state(const float* srow, const uint16_t* Wt, int v, int r, int h) {
+  const int n = r >> 1;
+  const float* e = srow + h * n;
+  const uint4* w = reinterpret_cast<const uint4*>(Wt + (size_t)v * r + h * n);
+  float acc = 0.f;
+  for (int j = 0; j < n / 8; ++j) {
+    const uint4 ev = bf16x8_from_f32(e + 8 * j), wv = w[j];
+    acc = fmaf(bf16_lo(ev.x), bf16_lo(wv.x), acc);
+    acc = fmaf(bf16_hi(ev.x), bf16_hi(wv.x), acc);
+    acc = fmaf(bf16_lo(ev.y), bf16_lo(wv.y), acc);
+    acc = fmaf(bf16_hi(ev.y), bf16_hi(wv.y), acc);
+    acc = fmaf(bf16_lo(ev.z), bf16_lo(wv.z), acc);
+    acc = fmaf(bf16_hi(ev.z), bf16_hi(wv.z), acc);
+    acc = fmaf(bf16_lo(ev.w), bf16_lo(wv.w), acc);
+    acc = fmaf(bf16_hi(ev.w), bf16_hi(wv.w), acc);
+  }
+  return acc;
+}
+
 template <>
 __device__ __forceinline__ float half_dot<float>(const float* E, const float* Wt, int prev, int v, int r, int h) {
   const int n = r >> 1;
@@ -206,6 +242,11 @@ struct HalfRow<uint16_t, R> {
 #pragma unroll
     for (int j = 0; j < kN; ++j) q[j] = p[j];
   }
+  // a float row (a recurrent state), rounded to bfloat16 as the projection operand
+  __device__ __forceinline__ void load_f32(const float* row, int h) {
+#pragma unroll
+    for (int j = 0; j < kN; ++j) q[j] = bf16x8_from_f32(row + h * (R / 2) + 8 * j);
+  }
 };
 template <int R>
 struct HalfRow<float, R> {
@@ -216,6 +257,7 @@ struct HalfRow<float, R> {
 #pragma unroll
     for (int j = 0; j < kN; ++j) q[j] = p[j];
   }
+  __device__ __forceinline__ void load_f32(const float* row, int h) { load(row, h); }
 };
 
 template <int R>

@@ -72,6 +72,7 @@ struct SelectArgs {
   float* lse;
   const float4* part;
   uint4* efrag;          // if set, the chosen token's E row is stored there in B-fragment order
+  const float* state;    // RNN head: [B][K][r] states; bf16(state[b][k-1]) replaces E[x_{k-1}] (bf16 factors)
   int B, K, V, r, k, G;
   float inv_T;
   Key key;
@@ -113,6 +114,7 @@ struct VerifyArgs {
   int32_t* nrows;
   const float4* part;
   uint4* efrag;          // if set, k_accept stores the resample pass's B fragments there
+  const float* state;    // RNN head: [B][K][r] states, the projection operands (bf16-rounded) of the positions
   int B, K, V, r, G, nseg;
   float inv_T, scale2;
   Key key;
@@ -126,6 +128,20 @@ __device__ __forceinline__ void efrag_store_piece(uint4* efrag, const uint16_t* 
   const uint4 v = x >= 0 ? *reinterpret_cast<const uint4*>(E + (size_t)x * r + 8 * p) : make_uint4(0, 0, 0, 0);
   efrag[((size_t)(b >> 5) * (r >> 4) + (p >> 1)) * 64 + (b & 31) + 32 * (p & 1)] = v;
 }
+// The same piece taken from a float row rounded to bfloat16 (null row: zeros).
+__device__ __forceinline__ void efrag_store_piece_f32(uint4* efrag, const float* row, int b, int r, int p) {
+  const uint4 v = row ? bf16x8_from_f32(row + 8 * p) : make_uint4(0, 0, 0, 0);
+  efrag[((size_t)(b >> 5) * (r >> 4) + (p >> 1)) * 64 + (b & 31) + 32 * (p & 1)] = v;
+}
+
+// RNN head.  Gh: [B*K][3r] float, the hidden-state part of the input gates.
+size_t rnn_extra_bytes(const dspark_problem& P);
+bool rnn_supported(const dspark_problem& P);
+hipError_t launch_rnn_gemm(const dspark_problem& P, const void* h, const void* W_ih, const float* b_ih, float* Gh,
+                           hipStream_t s);
+hipError_t launch_rnn_step(const dspark_problem& P, const float* Gh, const void* W_ih, const void* W_hh,
+                           const float* b_hh, const void* E, const int32_t* anchor, const int32_t* tok, float* state,
+                           uint4* efrag, int k, hipStream_t s);
 
 // Launchers; each returns hipSuccess or the launch error.
 hipError_t launch_stream_draft(const dspark_problem& P, const StreamArgs& a, int G, hipStream_t s);

@@ -1343,9 +1343,13 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   // the partials first (G <= 256: at most one per thread), so that the merge
   // waits for nothing else; then the previous token and its E half row
   const float4 p = tid < a.G ? a.part[(size_t)b * a.G + tid] : make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
-  const int prev = clamp_id(a.k == 1 ? a.anchor[b] : a.tok[(size_t)b * K + a.k - 2], V);
   HalfRow<WT, R> erow;
-  erow.load(static_cast<const WT*>(a.E) + (size_t)prev * R, h);
+  if (a.state) {  // RNN head: the state of position k
+    erow.load_f32(a.state + ((size_t)b * K + (a.k - 1)) * R, h);
+  } else {
+    const int prev = clamp_id(a.k == 1 ? a.anchor[b] : a.tok[(size_t)b * K + a.k - 2], V);
+    erow.load(static_cast<const WT*>(a.E) + (size_t)prev * R, h);
+  }
 
   // 1. merge the per-workgroup partials of row b
   float m = -INFINITY, s = 0.f, best = -INFINITY;

@@ -193,8 +193,12 @@ __global__ __launch_bounds__(64) void k_accept(VerifyArgs a) {
   if (k0 == 0) a.job[b] = ks;
   if (a.efrag && k0 < (a.r >> 3)) {
     // B fragments of the resample pass: E[x_{k*-1}] for a rejection at k*, zeros for a bonus row
-    const int prev = ks > 0 ? clamp_id(ks == 1 ? a.anchor[b] : a.tok[(size_t)b * K + ks - 2], a.V) : -1;
-    efrag_store_piece(a.efrag, static_cast<const uint16_t*>(a.E), prev, b, a.r, k0);
+    if (a.state) {  // RNN head: the state of position k*
+      efrag_store_piece_f32(a.efrag, ks > 0 ? a.state + ((size_t)b * K + ks - 1) * a.r : nullptr, b, a.r, k0);
+    } else {
+      const int prev = ks > 0 ? clamp_id(ks == 1 ? a.anchor[b] : a.tok[(size_t)b * K + ks - 2], a.V) : -1;
+      efrag_store_piece(a.efrag, static_cast<const uint16_t*>(a.E), prev, b, a.r, k0);
+    }
   }
 }
 
@@ -316,8 +320,16 @@ __global__ __launch_bounds__(256) void k_finish(VerifyArgs a) {
       const int j = tid >> 1, h = tid & 1;
       const int v = cstar * kChunk + j;
       const bool inside = v < V;
-      float dot = inside ? half_dot<WT>(static_cast<const WT*>(a.E), static_cast<const WT*>(a.Wt), prev, v, a.r, h)
-                         : 0.f;
+      float dot = 0.f;
+      if (inside) {
+        if constexpr (sizeof(WT) == 2) {
+          dot = a.state ? half_dot_state(a.state + ((size_t)b * K + k0) * a.r, static_cast<const uint16_t*>(a.Wt), v,
+                                         a.r, h)
+                        : half_dot<WT>(static_cast<const WT*>(a.E), static_cast<const WT*>(a.Wt), prev, v, a.r, h);
+        } else {
+          dot = half_dot<WT>(static_cast<const WT*>(a.E), static_cast<const WT*>(a.Wt), prev, v, a.r, h);
+        }
+      }
       dot += __shfl_xor(dot, 1);
       float sc = -INFINITY;
       int idx = 0x7fffffff;

@@ -22,7 +22,8 @@ _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 
 SYMBOLS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft", "dspark_draft_timed",
            "dspark_schedule", "dspark_schedule_async", "dspark_schedule_fixed", "dspark_schedule_threshold",
-           "dspark_sts_workspace_bytes", "dspark_sts_fit", "dspark_verify")
+           "dspark_sts_workspace_bytes", "dspark_sts_fit", "dspark_verify", "dspark_rnn_workspace_bytes",
+           "dspark_draft_rnn", "dspark_verify_rnn")
 
 
 class Problem(ctypes.Structure):
@@ -85,6 +86,12 @@ def load() -> ctypes.CDLL:
     lib.dspark_schedule_threshold.restype = i32
     lib.dspark_verify.argtypes = [P] + [vp] * 14 + [vp, sz, vp]
     lib.dspark_verify.restype = i32
+    lib.dspark_rnn_workspace_bytes.argtypes = [P]
+    lib.dspark_rnn_workspace_bytes.restype = sz
+    lib.dspark_draft_rnn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float] + [vp] * 8 + [vp, sz, vp]
+    lib.dspark_draft_rnn.restype = i32
+    lib.dspark_verify_rnn.argtypes = [P] + [vp] * 15 + [vp, sz, vp]
+    lib.dspark_verify_rnn.restype = i32
     _lib = lib
     return lib
 
@@ -215,3 +222,41 @@ def verify(P: Problem, target, Z, E, Wt, anchor, draft_tok, draft_logq, draft_ls
         _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
         _stream(stream))
     _check("dspark_verify", st)
+
+
+def rnn_workspace_bytes(P: Problem) -> int:
+    return int(load().dspark_rnn_workspace_bytes(ctypes.byref(P)))
+
+
+def draft_rnn(P: Problem, Z, E, Wt, h, W_ih, b_ih, W_hh, b_hh, w_conf, b_conf: float, tau, anchor,
+              draft_tok, draft_logq, draft_lse, conf, surv, state, workspace, stream=None) -> None:
+    """dspark_draft with the RNN head; state [B][K][r] float32 receives s_k."""
+    lt, wt, ht = _TORCH_DT[P.logits_dtype], _TORCH_DT[P.weight_dtype], _TORCH_DT[P.hidden_dtype]
+    st = load().dspark_draft_rnn(
+        ctypes.byref(P), _ptr(Z, lt, "Z"), _ptr(E, wt, "E"), _ptr(Wt, wt, "Wt"), _ptr(h, ht, "h"),
+        _ptr(W_ih, wt, "W_ih"), _ptr(b_ih, torch.float32, "b_ih"), _ptr(W_hh, wt, "W_hh"),
+        _ptr(b_hh, torch.float32, "b_hh"), _ptr(w_conf, torch.float32, "w_conf"), ctypes.c_float(b_conf),
+        _ptr(tau, torch.float32, "tau"), _ptr(anchor, torch.int32, "anchor"),
+        _ptr(draft_tok, torch.int32, "draft_tok"), _ptr(draft_logq, torch.float32, "draft_logq"),
+        _ptr(draft_lse, torch.float32, "draft_lse"), _ptr(conf, torch.float32, "conf"),
+        _ptr(surv, torch.float32, "surv"), _ptr(state, torch.float32, "state"),
+        _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+        _stream(stream))
+    _check("dspark_draft_rnn", st)
+
+
+def verify_rnn(P: Problem, target, Z, E, Wt, anchor, draft_tok, draft_logq, draft_lse, state, n_sched,
+               out_tok, n_accepted, next_anchor, logp, resid_mass, workspace, stream=None) -> None:
+    """dspark_verify with the RNN head's states as the projection operands."""
+    lt, wt = _TORCH_DT[P.logits_dtype], _TORCH_DT[P.weight_dtype]
+    st = load().dspark_verify_rnn(
+        ctypes.byref(P), _ptr(target, lt, "target"), _ptr(Z, lt, "Z"), _ptr(E, wt, "E"), _ptr(Wt, wt, "Wt"),
+        _ptr(anchor, torch.int32, "anchor"), _ptr(draft_tok, torch.int32, "draft_tok"),
+        _ptr(draft_logq, torch.float32, "draft_logq"), _ptr(draft_lse, torch.float32, "draft_lse"),
+        _ptr(state, torch.float32, "state"), _ptr(n_sched, torch.int32, "n_sched"),
+        _ptr(out_tok, torch.int32, "out_tok"), _ptr(n_accepted, torch.int32, "n_accepted"),
+        _ptr(next_anchor, torch.int32, "next_anchor"), _ptr(logp, torch.float32, "logp"),
+        _ptr(resid_mass, torch.float32, "resid_mass"),
+        _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+        _stream(stream))
+    _check("dspark_verify_rnn", st)

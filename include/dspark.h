@@ -13,6 +13,8 @@
  *                      head, Sequential Temperature Scaling, prefix survival);
  *   dspark_schedule_fixed, dspark_schedule_threshold -- Main results (the
  *                     fixed-length and static-threshold baselines)
+ *   dspark_draft_rnn, dspark_verify_rnn -- Method > Semi-autoregressive
+ *                      generation (the RNN head as the sequential block)
  *   dspark_sts_fit  -- Method > Confidence-scheduled verification (fitting the
  *                      STS temperatures left to right by grid search on ECE)
  *   dspark_schedule_async -- Production deployment results (asynchronous
@@ -209,6 +211,49 @@ dspark_status dspark_schedule_fixed(const dspark_problem* P, int32_t gamma,
                                     int32_t* n_sched, int32_t* n_total, hipStream_t stream);
 dspark_status dspark_schedule_threshold(const dspark_problem* P, const float* surv, float theta,
                                         int32_t* n_sched, int32_t* n_total, hipStream_t stream);
+
+/*
+ * dspark_rnn_workspace_bytes / dspark_draft_rnn / dspark_verify_rnn -- the RNN
+ * head as the sequential block (Method > Semi-autoregressive generation: the
+ * second sequential block keeps a recurrent state over the whole drafted prefix
+ * and applies a gated update from the current state, the previous token's
+ * embedding and the backbone hidden state; Main results: small gains over the
+ * Markov head at long draft lengths).
+ *
+ * The gated update is a GRU cell (gate order reset, update, new; the reset gate
+ * scales the recurrent product of the new gate), with input u_k = [h_k; E[x_{k-1}]]:
+ *   a = W_ih u_k + b_ih,  c = W_hh s_{k-1} + b_hh,  s_0 = 0,
+ *   rho = sigmoid(a_r + c_r), z = sigmoid(a_z + c_z), n = tanh(a_n + rho * c_n),
+ *   s_k = (1 - z) * n + z * s_{k-1};
+ * bf16(s_k) (round to nearest even) replaces E[x_{k-1}] as the operand of the
+ * logit projection at position k, in the draft and in the resample of the
+ * verification.  Everything else is dspark_draft / dspark_verify: the same
+ * sampling, randomness, confidence head (inputs [h_k; E[x_{k-1}]]), outputs
+ * and errors.
+ *
+ *   W_ih  [3r][d + r] bf16   input weights (columns 0..d-1 act on h_k, d.. on E[x_{k-1}])
+ *   b_ih  [3r] float32
+ *   W_hh  [3r][r] bf16        recurrent weights
+ *   b_hh  [3r] float32
+ *   state [B][K][r] float32   draft: out, s_k of every position; verify: in (the draft's)
+ * Supported for bf16 logits, factors and hidden states with d a multiple of 32,
+ * within the sizes the fragment-fed kernels address (DSPARK_E_UNSUPPORTED
+ * otherwise).  Workspace: at least dspark_rnn_workspace_bytes(P) for the draft
+ * (the draft's regions plus the hidden-state part of the input gates for all
+ * B*K positions); the verification needs dspark_workspace_bytes(P).
+ */
+size_t dspark_rnn_workspace_bytes(const dspark_problem* P);
+dspark_status dspark_draft_rnn(const dspark_problem* P, const void* Z, const void* E, const void* Wt, const void* h,
+                               const void* W_ih, const float* b_ih, const void* W_hh, const float* b_hh,
+                               const float* w_conf, float b_conf, const float* tau, const int32_t* anchor,
+                               int32_t* draft_tok, float* draft_logq, float* draft_lse, float* conf, float* surv,
+                               float* state, void* workspace, size_t workspace_bytes, hipStream_t stream);
+dspark_status dspark_verify_rnn(const dspark_problem* P, const void* target, const void* Z, const void* E,
+                                const void* Wt, const int32_t* anchor, const int32_t* draft_tok,
+                                const float* draft_logq, const float* draft_lse, const float* state,
+                                const int32_t* n_sched, int32_t* out_tok, int32_t* n_accepted, int32_t* next_anchor,
+                                float* logp, float* resid_mass, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 
 /*
  * dspark_sts_workspace_bytes / dspark_sts_fit -- fitting the Sequential

@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     assert _declared() == sorted(["dspark_draft", "dspark_draft_timed", "dspark_schedule", "dspark_schedule_async",
                                   "dspark_schedule_fixed", "dspark_schedule_threshold", "dspark_sts_fit",
                                   "dspark_sts_workspace_bytes", "dspark_verify", "dspark_workspace_bytes",
-                                  "dspark_status_string"])
+                                  "dspark_status_string", "dspark_rnn_workspace_bytes", "dspark_draft_rnn",
+                                  "dspark_verify_rnn"])
 
 
 def test_library_exports_every_declared_symbol(ds):
@@ -132,6 +133,33 @@ def test_baseline_schedulers_validate(ds):
                                          None) == ds.E_INVALID
     assert lib.dspark_schedule_threshold(ctypes.byref(P), None, ctypes.c_float(0.5), fake[1], fake[2],
                                          None) == ds.E_POINTER
+
+
+def test_rnn_validation(ds):
+    lib = ds.load()
+    P = _P(ds)
+    assert ds.rnn_workspace_bytes(P) == ds.workspace_bytes(P) + ((256 * 16 * 3 * 256 * 4 + 255) // 256) * 256
+    f = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(24)]
+    ws = ctypes.c_void_p(0x40000000)
+    need = ds.rnn_workspace_bytes(P)
+
+    def draft(P, wsb=need, **kw):
+        a = list(f[:9]) + [ctypes.c_float(0.0)] + list(f[9:16]) + [kw.get("state", f[17])]
+        return lib.dspark_draft_rnn(ctypes.byref(P), *a, ws, wsb, None)
+    # fp32 logits or hidden states, or d not a multiple of 32: no RNN kernels
+    assert draft(_P(ds, logits="f32")) == ds.E_UNSUPPORTED
+    assert draft(_P(ds, hidden="f32")) == ds.E_UNSUPPORTED
+    assert draft(_P(ds, d=4104)) == ds.E_UNSUPPORTED
+    assert draft(_P(ds, r=16)) == ds.E_UNSUPPORTED
+    assert draft(P, state=None) == ds.E_POINTER
+    assert draft(P, state=ctypes.c_void_p(0x10008)) == ds.E_POINTER
+    assert draft(P, wsb=ds.workspace_bytes(P)) == ds.E_WORKSPACE  # the Markov size lacks the gate region
+
+    def verify(P, state):
+        a = list(f[:8]) + [state] + list(f[8:14])
+        return lib.dspark_verify_rnn(ctypes.byref(P), *a, ws, ds.workspace_bytes(P), None)
+    assert verify(P, None) == ds.E_POINTER
+    assert verify(_P(ds, weights="f32"), f[20]) == ds.E_UNSUPPORTED
 
 
 def test_sts_validation(ds):
