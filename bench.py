@@ -428,6 +428,35 @@ def main() -> int:
                 "ece_raw_mean": float(np.nanmean(sts_out[3].cpu().numpy())),
                 "ece_fit_mean": float(np.nanmean(sts_out[2].cpu().numpy()))}
 
+    # the RNN head as the sequential block: whole cycles (draft_rnn, schedule,
+    # verify_rnn) on the same inputs, with seeded random GRU weights
+    w_rnn = synth.make_rnn_weights(cfg)
+    W_ih, W_hh = runner.to_device(w_rnn["W_ih"]), runner.to_device(w_rnn["W_hh"])
+    b_ih, b_hh = runner.to_device(w_rnn["b_ih"]), runner.to_device(w_rnn["b_hh"])
+    state = torch.empty((cfg.B, cfg.K, cfg.r), dtype=torch.float32, device="cuda")
+    ws_rnn = torch.empty(dspark.rnn_workspace_bytes(P), dtype=torch.uint8, device="cuda")
+
+    def rnn_cycle(xs):
+        dspark.draft_rnn(P, xs.Z, xs.E, xs.Wt, xs.h, W_ih, b_ih, W_hh, b_hh, xs.w_c, xs.b_c, xs.tau, xs.anchor,
+                         o.tok, o.logq, o.lse, o.conf, o.surv, state, ws_rnn)
+        dspark.schedule(P, o.surv, xs.T, o.n_sched, o.n_total, ws_rnn)
+        dspark.verify_rnn(P, xs.Zt, xs.Z, xs.E, xs.Wt, xs.anchor, o.tok, o.logq, o.lse, state, o.n_sched, o.out_tok,
+                          o.n_acc, o.next_anchor, o.logp, o.resid_mass, ws_rnn)
+
+    for i in range(args.warmup):
+        rnn_cycle(sets[i % 3])
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        rnn_cycle(sets[i % 3])
+    e1.record()
+    torch.cuda.synchronize()
+    ms_rnn = e0.elapsed_time(e1) / args.steps
+    h_rnn = o.host()
+    rnn_line = {"ms_per_step": ms_rnn, "positions_per_s": cfg.B * cfg.K / (ms_rnn / 1e3),
+                "scheduled_N": int(h_rnn["n_total"][0]), "mean_accepted": float(h_rnn["n_acc"].mean()),
+                "gate_gemm_gflop": 2.0 * cfg.B * cfg.K * 3 * cfg.r * cfg.d / 1e9}
+
     baselines = {
         f"fixed_gamma{cfg.K}": baseline_cycle(
             lambda xs: dspark.schedule_fixed(P, cfg.K, o.n_sched, o.n_total)),
@@ -491,6 +520,7 @@ def main() -> int:
         "ms_schedule_async": ms_async,
         "baselines": baselines,
         "sts_fit": sts_line,
+        "rnn_head": rnn_line,
         "scheduled_N": N,
         "mean_accepted": float(g["n_acc"].mean()),
         "roofline": {

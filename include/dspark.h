@@ -236,7 +236,7 @@ dspark_status dspark_schedule_threshold(const dspark_problem* P, const float* su
  *   W_hh  [3r][r] bf16        recurrent weights
  *   b_hh  [3r] float32
  *   state [B][K][r] float32   draft: out, s_k of every position; verify: in (the draft's)
- * Supported for bf16 logits, factors and hidden states with d a multiple of 32,
+ * Supported for bf16 logits, factors and hidden states with r a multiple of 32,
  * within the sizes the fragment-fed kernels address (DSPARK_E_UNSUPPORTED
  * otherwise).  Workspace: at least dspark_rnn_workspace_bytes(P) for the draft
  * (the draft's regions plus the hidden-state part of the input gates for all

@@ -146,10 +146,9 @@ def test_rnn_validation(ds):
     def draft(P, wsb=need, **kw):
         a = list(f[:9]) + [ctypes.c_float(0.0)] + list(f[9:16]) + [kw.get("state", f[17])]
         return lib.dspark_draft_rnn(ctypes.byref(P), *a, ws, wsb, None)
-    # fp32 logits or hidden states, or d not a multiple of 32: no RNN kernels
+    # fp32 logits or hidden states, or r not a multiple of 32: no RNN kernels
     assert draft(_P(ds, logits="f32")) == ds.E_UNSUPPORTED
     assert draft(_P(ds, hidden="f32")) == ds.E_UNSUPPORTED
-    assert draft(_P(ds, d=4104)) == ds.E_UNSUPPORTED
     assert draft(_P(ds, r=16)) == ds.E_UNSUPPORTED
     assert draft(P, state=None) == ds.E_POINTER
     assert draft(P, state=ctypes.c_void_p(0x10008)) == ds.E_POINTER

@@ -154,6 +154,8 @@ CASES = [
                            ttable=("linear", 5.0, 0.02))),
     ("rnn_k1_r32", dict(B=70, K=1, V=4104, r=32, d=64, seed=202, ew_std=0.25, wc_std=0.2,
                         ttable=("linear", 5.0, 0.02))),
+    ("rnn_ragged_d", dict(B=131, K=5, V=2056, r=128, d=200, seed=203, ew_std=0.25, wc_std=0.2,
+                          ttable=("linear", 5.0, 0.02))),
 ]
 
 
