@@ -14,9 +14,15 @@ namespace dspark {
 // Workgroups of the vocabulary-split stream kernel (one per CU on MI355X).
 constexpr int kStreamGridMax = 256;
 // Target-row segment of the verify log-partition pass.
-constexpr int kVlseSeg = 8192;
+#ifndef DSPARK_VLSE_SEG
+#define DSPARK_VLSE_SEG 8192
+#endif
+constexpr int kVlseSeg = DSPARK_VLSE_SEG;
 // Workgroups of the verify log-partition pass.
-constexpr int kVlseGrid = 1024;
+#ifndef DSPARK_VLSE_GRID
+#define DSPARK_VLSE_GRID 1024
+#endif
+constexpr int kVlseGrid = DSPARK_VLSE_GRID;
 
 inline int n_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 inline int stream_grid(int V) { const int nc = n_chunks(V); return nc < kStreamGridMax ? nc : kStreamGridMax; }
