@@ -187,9 +187,11 @@ def test_deterministic(lib):
             np.testing.assert_array_equal(runs[0][k], r[k], err_msg=k)
 
 
-@pytest.mark.parametrize("name,n_req", [("qwen3_4b", 6), ("high_concurrency", 6)])
+@pytest.mark.parametrize("name,n_req", [("qwen3_4b", 6), ("high_concurrency", 6), ("dsv4_vocab", 5), ("stress", 4)])
 def test_full_size_sampled(lib, name, n_req):
-    # the bench workload at full size; the oracle checks a sample of requests,
+    # every workload at full size (the bench's, and the larger-batch ones: two
+    # and four 256-row passes, 32,768 candidates in the scheduler, and a resample
+    # pass past the 32-bit buffer range); the oracle checks a sample of requests,
     # and the scheduler over the whole batch
     cfg = synth.get_config(name)
     _say(f"[gpu] full-size {name} B={cfg.B} K={cfg.K} V={cfg.V}")
