@@ -490,7 +490,8 @@ def main() -> int:
     positions = cfg.B * cfg.K
     value = positions / (ms_step / 1e3)
     alg_bytes = cycle_bytes(cfg, N, R)
-    G = min((cfg.V + 127) // 128, 256)
+    nc = (cfg.V + 127) // 128                     # the library's stream grid: fewest workgroups
+    G = -(-nc // -(-nc // 256))                    # with the busiest one's chunk count unchanged
     launch_bytes = stream_launch_bytes(cfg, G)
     achieved = launch_bytes / (k_ms / 1e3) / 1e9
     traffic = traffic_from_profile(cfg.name)

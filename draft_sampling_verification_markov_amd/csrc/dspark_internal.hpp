@@ -25,7 +25,15 @@ constexpr int kVlseSeg = DSPARK_VLSE_SEG;
 constexpr int kVlseGrid = DSPARK_VLSE_GRID;
 
 inline int n_chunks(int V) { return (V + kChunk - 1) / kChunk; }
-inline int stream_grid(int V) { const int nc = n_chunks(V); return nc < kStreamGridMax ? nc : kStreamGridMax; }
+// The smallest grid that gives no workgroup more chunks than an even split over
+// kStreamGridMax would (1,187 chunks: 238 workgroups of 4-5, not 256 of 4-5):
+// the step lasts as long as its busiest workgroup, and idle CUs take no share of
+// the per-step fill.
+inline int stream_grid(int V) {
+  const int nc = n_chunks(V);
+  const int per = (nc + kStreamGridMax - 1) / kStreamGridMax;
+  return (nc + per - 1) / per;
+}
 inline int vlse_segments(int V) { return (V + kVlseSeg - 1) / kVlseSeg; }
 
 // Byte offsets of the workspace regions (256-byte aligned each).
