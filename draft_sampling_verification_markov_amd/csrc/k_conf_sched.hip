@@ -245,6 +245,50 @@ __global__ __launch_bounds__(kGreedyThreads) void k_sched_greedy_global(const fl
   sched_greedy<kGreedyThreads>(sorted_s, sorted_i, T, B, K, n_sched, n_total, s_wsum, s_wmin, &s_stop);
 }
 
+// Candidate sets up to kSchedLdsMax: each candidate's rank is summed from the
+// partial ranks and the candidate is placed in schedule order in LDS by the
+// workgroup that runs the greedy pass (no ordering round trip through memory).
+constexpr int kSchedLdsMax = 8192;
+__global__ __launch_bounds__(kGreedyThreads) void k_sched_greedy_lds(const float* surv, const int32_t* part, int S,
+                                                                   const float* T, int B, int K, int32_t* n_sched,
+                                                                   int32_t* n_total) {
+  __shared__ float s_sorted_s[kSchedLdsMax];
+  __shared__ int32_t s_sorted_i[kSchedLdsMax];
+  __shared__ double s_wsum[kGreedyThreads / 64];
+  __shared__ int s_wmin[kGreedyThreads / 64];
+  __shared__ int s_stop;
+  const int n = B * K;
+  for (int b = threadIdx.x; b < B; b += kGreedyThreads) n_sched[b] = 0;
+  // kBatchC candidates per thread at a time, all their loads in flight before the
+  // first sum: kSchedSegMax segments each, unconditional (clamped) and masked after
+  constexpr int kBatchC = 4;
+  for (int u0 = 0; u0 * kGreedyThreads < n; u0 += kBatchC) {
+    int v[kBatchC][kSchedSegMax];
+    float sv[kBatchC];
+#pragma unroll
+    for (int u = 0; u < kBatchC; ++u) {
+      const int i = min((int)threadIdx.x + (u0 + u) * kGreedyThreads, n - 1);
+      sv[u] = surv[i];
+#pragma unroll
+      for (int q = 0; q < kSchedSegMax; ++q) v[u][q] = part[(size_t)(q < S ? q : 0) * n + i];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatchC; ++u) {
+      const int i = (int)threadIdx.x + (u0 + u) * kGreedyThreads;
+      if (i < n) {
+        int r = 0;
+#pragma unroll
+        for (int q = 0; q < kSchedSegMax; ++q) r += q < S ? v[u][q] : 0;
+        r = r < 0 ? 0 : (r >= n ? n - 1 : r);
+        s_sorted_s[r] = sv[u];
+        s_sorted_i[r] = i;
+      }
+    }
+  }
+  __syncthreads();
+  sched_greedy<kGreedyThreads>(s_sorted_s, s_sorted_i, T, B, K, n_sched, n_total, s_wsum, s_wmin, &s_stop);
+}
+
 // Asynchronous budget: the first M = lag_total - B candidates of the current
 // schedule order are taken; one workgroup.
 __global__ __launch_bounds__(kGreedyThreads) void k_sched_topk(const int32_t* sorted_i, const int32_t* lag_total,
@@ -318,6 +362,10 @@ hipError_t launch_schedule(const dspark_problem& P, const float* surv, const flo
   hipLaunchKernelGGL(k_sched_rank, dim3((n + 255) / 256, S), 256, 0, s, surv, n, S, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (n <= kSchedLdsMax) {
+    hipLaunchKernelGGL(k_sched_greedy_lds, 1, kGreedyThreads, 0, s, surv, part, S, T, P.B, P.K, n_sched, n_total);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_sched_scatter, (n + kScatterThreads - 1) / kScatterThreads, kScatterThreads, 0, s, surv, part, S, n, sorted_s, sorted_i);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
