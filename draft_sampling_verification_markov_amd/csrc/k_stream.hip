@@ -1336,8 +1336,6 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   const int K = a.K, V = a.V;
   __shared__ float s_m[4], s_s[4], s_best[4], s_ell[kChunk];
   __shared__ int s_c[4];
-  __shared__ float s_lse;
-  __shared__ int s_cstar;
 
   const int j = tid >> 1, h = tid & 1;
   // the partials first (G <= 256: at most one per thread), so that the merge
@@ -1351,47 +1349,36 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
     erow.load(static_cast<const WT*>(a.E) + (size_t)prev * R, h);
   }
 
-  // 1. merge the per-workgroup partials of row b
-  float m = -INFINITY, s = 0.f, best = -INFINITY;
+  // 1. the winning chunk of row b: argmax of the chunk scores over the partials
+  // (the log-partition, needed only for log q, is merged later, off this path)
+  float best = -INFINITY;
   int bc = 0x7fffffff;
   if (tid < a.G) {
-    lse2_merge(m, s, p.x, p.y);
     const int pc = __float_as_int(p.w);
     if (better(p.z, pc, best, bc)) {
       best = p.z;
       bc = pc;
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-    lse2_merge(m, s, m2, s2);
-  }
   wave_argmax(best, bc);
   if (lane == 0) {
-    s_m[wave] = m;
-    s_s[wave] = s;
     s_best[wave] = best;
     s_c[wave] = bc;
   }
   __syncthreads();
-  if (tid == 0) {
-    float M = s_m[0], S = s_s[0], B0 = s_best[0];
+  int cstar;
+  {
+    float B0 = s_best[0];
     int C0 = s_c[0];
     for (int w = 1; w < 4; ++w) {
-      lse2_merge(M, S, s_m[w], s_s[w]);
       if (better(s_best[w], s_c[w], B0, C0)) {
         B0 = s_best[w];
         C0 = s_c[w];
       }
     }
-    s_lse = (M + log2f(S)) * kLn2;
     // a row without any finite chunk score (non-finite logits) falls back to chunk 0
-    s_cstar = (C0 >= 0 && C0 * kChunk < V) ? C0 : 0;
+    cstar = (C0 >= 0 && C0 * kChunk < V) ? C0 : 0;
   }
-  __syncthreads();
-  const int cstar = s_cstar;
-  const float lse = s_lse;
 
   // 2. recompute the winning chunk's logits and draw the entry
   const int v = cstar * kChunk + j;
@@ -1400,6 +1387,23 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   wrow.load(static_cast<const WT*>(a.Wt) + (size_t)(inside ? v : 0) * R, h);
   const ZT* zrow = static_cast<const ZT*>(a.Z) + ((size_t)b * K + (a.k - 1)) * V;
   const float z = logit_at<ZT>(zrow, inside ? v : 0);
+  // the entry's Gumbel and the row's log-partition do not need the Wt rows:
+  // computed while they arrive
+  const float gum = gumbel_from_word(draw_word(a.key, (uint32_t)v, (uint32_t)b, (uint32_t)a.k, kDraftElem));
+  {
+    float m = -INFINITY, s = 0.f;
+    if (tid < a.G) lse2_merge(m, s, p.x, p.y);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+      lse2_merge(m, s, m2, s2);
+    }
+    if (lane == 0) {
+      s_m[wave] = m;
+      s_s[wave] = s;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   float dot = inside ? half_dot_regs<R>(erow, wrow) : 0.f;
   dot += __shfl_xor(dot, 1);
   float score = -INFINITY;
@@ -1407,7 +1411,7 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   if (h == 0 && inside) {
     const float ell = (z + dot) * a.inv_T;
     s_ell[j] = ell;
-    score = ell + gumbel_from_word(draw_word(a.key, (uint32_t)v, (uint32_t)b, (uint32_t)a.k, kDraftElem));
+    score = ell + gum;
     idx = v;
   }
   wave_argmax(score, idx);
@@ -1426,6 +1430,9 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
         X = s_c[w];
       }
     }
+    float M = s_m[0], S = s_s[0];
+    for (int w = 1; w < 4; ++w) lse2_merge(M, S, s_m[w], s_s[w]);
+    const float lse = (M + log2f(S)) * kLn2;
     const size_t o = (size_t)b * K + (a.k - 1);
     if (X < cstar * kChunk || X >= cstar * kChunk + kChunk || X >= V) X = cstar * kChunk;  // no finite score
     a.tok[o] = X;
