@@ -194,13 +194,13 @@ def _pmc_means(directory: str, counter: str):
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-PROFILE_COMMANDS = """cd /tmp && export TMPDIR=/tmp; R=<repository root>
-rocprofv3 --kernel-trace --stats -T -d $R/gpurun_out/prof/trace -o trace --output-format csv -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline
-rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/prof/fetch -o fetch --output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline
-rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/prof/write -o write --output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline
-rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/prof/cfetch -o cfetch --output-format csv -- python3 $R/bench.py --calibrate-copy
-rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/prof/cwrite -o cwrite --output-format csv -- python3 $R/bench.py --calibrate-copy
-python3 $R/bench.py --summarize-profiles $R/gpurun_out/prof"""
+PROFILE_COMMANDS = """cd /tmp && export TMPDIR=/tmp; R=<repository root>; OUT=<output directory>
+rocprofv3 --kernel-trace --stats -T -d $OUT/trace -o trace --output-format csv -- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline
+rocprofv3 --pmc FETCH_SIZE -d $OUT/fetch -o fetch --output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc WRITE_SIZE -d $OUT/write -o write --output-format csv -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc FETCH_SIZE -d $OUT/cfetch -o cfetch --output-format csv -- python3 $R/bench.py --calibrate-copy
+rocprofv3 --pmc WRITE_SIZE -d $OUT/cwrite -o cwrite --output-format csv -- python3 $R/bench.py --calibrate-copy
+python3 $R/bench.py --summarize-profiles $OUT"""
 
 
 def summarize_profiles(prof_dir: str, workload: str) -> None:
