@@ -341,6 +341,32 @@ def main() -> int:
     ms_step = start.elapsed_time(stop) / args.steps
     log(f"{args.steps} timed steps: {ms_step:.3f} ms/step")
 
+    # the same steps replayed from HIP graphs (one captured per input set, on the
+    # same stable output buffers): what a serving loop that captures the cycle sees
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        runner.run_cycle(P, sets[0], o)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for xs in sets:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            runner.run_cycle(P, xs, o)
+        graphs.append(gr)
+    for i in range(args.warmup):
+        graphs[i % 3].replay()
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        graphs[i % 3].replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_graph = start.elapsed_time(stop) / args.steps
+    log(f"{args.steps} graph replays: {ms_graph:.3f} ms/step")
+    del graphs
+
     # per-call split (a separate pass over the same steps)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     split = np.zeros(3)
@@ -518,6 +544,7 @@ def main() -> int:
         "algorithmic_bytes_per_step": alg_bytes,
         "logits_per_s": (positions + N) * cfg.V / (ms_step / 1e3),
         "ms_split": {"draft": split[0], "schedule": split[1], "verify": split[2]},
+        "ms_per_step_graph_replay": ms_graph,
         "ms_schedule_async": ms_async,
         "baselines": baselines,
         "sts_fit": sts_line,
