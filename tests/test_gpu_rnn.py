@@ -1,5 +1,6 @@
 """RNN head on the GPU (dspark_draft_rnn, dspark_schedule, dspark_verify_rnn
-through the C ABI) against the oracle, stage by stage.
+through the C ABI) against the oracle's own RNN-head cycle on the same inputs
+(nothing the GPU produced is fed to the oracle), stage by stage.
 
 Tolerances.  The GPU state is fp32 (gate inputs from bf16 MFMA products with
 fp32 accumulation); the oracle's is fp64.  Both round the state to bf16 for the
@@ -11,7 +12,7 @@ whose codes do differ is bounded by
 (step_j the bf16 spacing at the entry, doubled to cover a binade edge),
 and every comparison downstream of the projection widens by it: a decision may
 differ only where its oracle margin is below 1e-4 + 2 amb; log q within 1e-5
-relative plus 2 amb; the residual mass within 1e-5 relative plus 2 amb.  Where
+relative plus 2 amb; the residual mass within 1e-5 relative plus 4e-6 plus 2 amb.  Where
 no code differs (amb = 0) these are the Markov head's bounds.  States are
 compared to STATE_ATOL absolute (about three times the largest error seen:
 3.3e-6); confidences and survivals to 1e-6."""
@@ -23,12 +24,10 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import conf as oconf
+from oracle import cycle as ocycle
 from oracle import rnn as ornn
-from oracle import sched as osched
-from oracle import verify as overify
 from oracle.io import f64
-from parity_util import CONF_ATOL, MARGIN, check_abs
+from parity_util import PROB_RTOL, cycle_check
 
 pytestmark = pytest.mark.gpu
 
@@ -71,80 +70,43 @@ def gpu_rnn_cycle(lib, cfg, inp, w):
     return g
 
 
-def ambiguity(state, gpu_state, Wt, T_s, atol=STATE_ATOL):
+def ambiguity(state, gpu_state, Wt, T_s, where=None, atol=STATE_ATOL):
     """Per (request, position): bound on the logit shift from the entries whose bf16
     codes differ between the GPU's fp32 state and the oracle's fp64 one; each such
-    entry must lie within atol of a rounding midpoint."""
+    entry must lie within atol of a rounding midpoint.  ``where`` (B x K) limits the
+    check to positions whose states are comparable (zero slack elsewhere)."""
     code = ornn.bf16_round(state)
     _, e = np.frexp(state)
     step = np.ldexp(1.0, e - 8)                      # bf16 spacing at the value
     near = np.minimum(np.abs(state - (code + step / 2)), np.abs(state - (code - step / 2))) < atol
     flipped = ornn.bf16_round(np.asarray(gpu_state, np.float64)) != code
+    if where is not None:
+        flipped &= where[..., None]
     assert not (flipped & ~near).any(), "a bf16 code differs away from a rounding midpoint"
     wmax = np.abs(f64(Wt)).max(axis=0)               # (r,)
     return (flipped * 2 * step * wmax).sum(axis=-1) / float(T_s)
 
 
-def _decisions(kind, gpu, ref, margin, slack):
-    gpu, ref, margin, slack = (np.asarray(a).ravel() for a in (gpu, ref, margin, slack))
-    mism = gpu != ref
-    bad = mism & ~(margin < MARGIN + 2 * slack)
-    assert not bad.any(), (f"{kind}: mismatches beyond margin: idx {np.flatnonzero(bad)[:8]}, "
-                           f"margin {margin[bad][:8]}, slack {slack[bad][:8]}")
-    return int(mism.sum())
-
-
-def staged_rnn_check(cfg, inp, w, g, requests=None):
-    B, K = cfg.B, cfg.K
-    reqs = np.arange(B) if requests is None else np.asarray(requests)
-    counts = {}
-    d = ornn.rnn_draft(inp["Z"], inp["E"], inp["Wt"], inp["h"], inp["anchor"], w["W_ih"], w["b_ih"], w["W_hh"],
-                       w["b_hh"], cfg.T_s, cfg.seed, teacher_x=g["tok"], requests=reqs)
-    counts["state_err"] = check_abs("state", g["state"][reqs], d["state"], STATE_ATOL)
-    amb = ambiguity(d["state"], g["state"][reqs], inp["Wt"], cfg.T_s)
-    counts["draft"] = _decisions("draft token", g["tok"][reqs], d["x"], d["margin"], amb)
-    same = g["tok"][reqs] == d["x"]
-    rel = np.abs(np.expm1(g["logq"][reqs].astype(np.float64) - d["logq"]))
-    assert (rel[same] <= 1e-5 + 2 * amb[same]).all(), f"draft q(x): worst {rel[same].max():.3e}"
-    counts["logq_err"] = float(rel[same].max())
-    counts["codes_differ"] = int((ornn.bf16_round(g["state"][reqs].astype(np.float64)) !=
-                                  ornn.bf16_round(d["state"])).sum())
-    counts["logq_err_clean"] = float(rel[same & (amb == 0)].max()) if (same & (amb == 0)).any() else 0.0
-    assert counts["logq_err_clean"] <= 1e-5
-    c, S = oconf.confidence(inp["h"][reqs], inp["E"], inp["w_c"], inp["b_c"], inp["tau"], inp["anchor"][reqs],
-                            g["tok"][reqs])
-    check_abs("confidence", g["conf"][reqs], c, CONF_ATOL)
-    check_abs("survival", g["surv"][reqs], S, CONF_ATOL)
-    sc = osched.schedule(g["surv"].astype(np.float64), inp["T"])
-    assert (g["n_sched"] == np.array(sc["n"])).all() or sc["margin"] < MARGIN
-    # verification on the GPU's tokens and schedule, with the oracle's own state codes
-    vec = np.zeros((B, K, cfg.r))
-    vec[reqs] = ornn.bf16_round(d["state"])
-    ver = overify.verify(inp["Zt"], inp["Z"], inp["E"], inp["Wt"], inp["anchor"], g["tok"], g["n_sched"], cfg.T_s,
-                         cfg.seed, requests=reqs, vec=vec)
-    amb_row = amb.max(axis=1)
-    acc_ref = np.array([v["accepted"] for v in ver])
-    counts["accept"] = _decisions("accepted length", g["n_acc"][reqs], acc_ref,
-                                  np.array([v["accept_margin"] for v in ver]), amb_row)
-    same_acc = g["n_acc"][reqs] == acc_ref
-    y_ref = np.array([v["y"] for v in ver])
-    counts["emit"] = _decisions("emitted token", g["next_anchor"][reqs][same_acc], y_ref[same_acc],
-                                np.array([v["token_margin"] for v in ver])[same_acc], amb_row[same_acc])
-    for i, b in enumerate(reqs):
-        v = ver[i]
-        if not same_acc[i]:
-            continue
-        if g["next_anchor"][b] == v["y"]:
-            row = np.full(K + 1, -1)
-            row[:len(v["tokens"])] = v["tokens"]
-            assert (g["out_tok"][b] == row).all(), (b, g["out_tok"][b], row)
-        if v["kind"] == "bonus":
-            assert np.isnan(g["resid_mass"][b])
-        else:
-            ks = v["k_star"]
-            tol = 1e-5 * abs(v["mass"]) + 2 * amb[i, ks - 1]
-            assert abs(g["resid_mass"][b] - v["mass"]) <= tol, (b, g["resid_mass"][b], v["mass"], tol)
-    counts["ambiguous_positions"] = int((amb > 0).sum())
+def rnn_check(cfg, inp, w, g):
+    """The GPU RNN-head cycle against the oracle's own RNN-head cycle (nothing of the
+    GPU's fed to the oracle), stage by stage; states where the preceding tokens agree."""
+    ref = ocycle.run_cycle_rnn(inp, w)
+    d = ref["draft"]
+    same = g["tok"] == d["x"]
+    prefix = np.cumprod(same, axis=1).astype(bool)
+    prev_ok = np.concatenate([np.ones((cfg.B, 1), bool), prefix[:, :-1]], axis=1)
+    err = np.abs(g["state"].astype(np.float64) - d["state"])[prev_ok]
+    assert (err <= STATE_ATOL).all(), f"state: worst {err.max():.3e}"
+    slack = ambiguity(d["state"], g["state"], inp["Wt"], cfg.T_s, where=prev_ok)
+    counts = cycle_check(cfg, g, ref, slack)
+    counts["state_err"] = float(err.max())
+    counts["codes_differ"] = int((ornn.bf16_round(g["state"].astype(np.float64)) !=
+                                  ornn.bf16_round(d["state"]))[prev_ok].sum())
+    rel = np.abs(np.expm1(g["logq"].astype(np.float64) - d["logq"]))
+    clean = prefix & (slack == 0)
+    counts["logq_err_clean"] = float(rel[clean].max()) if clean.any() else 0.0
+    assert counts["logq_err_clean"] <= PROB_RTOL
+    counts["positions_with_flips"] = int((slack > 0).sum())
     return counts
 
 
@@ -167,35 +129,13 @@ def _config(name, over):
 
 
 @pytest.mark.parametrize("name,over", CASES, ids=[c[0] for c in CASES])
-def test_rnn_staged_parity(lib, name, over):
+def test_rnn_parity(lib, name, over):
     cfg = _config(name, over)
-    _say(f"[gpu] rnn staged parity {name} B={cfg.B} K={cfg.K} V={cfg.V} r={cfg.r} d={cfg.d}")
+    _say(f"[gpu] rnn parity {name} B={cfg.B} K={cfg.K} V={cfg.V} r={cfg.r} d={cfg.d}")
     inp = synth.make_inputs(cfg)
     w = synth.make_rnn_weights(cfg)
     g = gpu_rnn_cycle(lib, cfg, inp, w)
-    counts = staged_rnn_check(cfg, inp, w, g)
-    _say(f"[gpu]   {counts}")
-
-
-def test_rnn_end_to_end(lib):
-    from oracle import cycle as ocycle
-    cfg = synth.get_config("tbias_bf16")
-    _say(f"[gpu] rnn end-to-end {cfg.name}")
-    inp = synth.make_inputs(cfg)
-    w = synth.make_rnn_weights(cfg)
-    g = gpu_rnn_cycle(lib, cfg, inp, w)
-    ref = ocycle.run_cycle_rnn(inp, w)
-    d = ref["draft"]
-    amb = ambiguity(d["state"], g["state"], inp["Wt"], cfg.T_s) if (g["tok"] == d["x"]).all() else \
-        np.full(g["tok"].shape, np.inf)
-    diff = g["tok"] != d["x"]
-    assert (d["margin"][diff] < MARGIN + 2 * amb[diff]).all()
-    if not diff.any():
-        assert (g["n_sched"] == np.array(ref["sched"]["n"])).all()
-        ok = g["n_acc"] == ref["n_accepted"]
-        assert ok.mean() > 0.9
-        assert (g["out_tok"][ok & (g["next_anchor"] == ref["next_anchor"])] ==
-                ref["out_tok"][ok & (g["next_anchor"] == ref["next_anchor"])]).all()
+    _say(f"[gpu]   {rnn_check(cfg, inp, w, g)}")
 
 
 def test_rnn_deterministic(lib):
@@ -209,12 +149,11 @@ def test_rnn_deterministic(lib):
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
 
 
-def test_rnn_full_size_sampled(lib):
+def test_rnn_full_size(lib):
     cfg = synth.get_config("high_concurrency")
     _say(f"[gpu] rnn full-size {cfg.name} B={cfg.B} K={cfg.K} V={cfg.V} d={cfg.d}")
     inp = synth.make_inputs(cfg)
     w = synth.make_rnn_weights(cfg)
     g = gpu_rnn_cycle(lib, cfg, inp, w)
-    reqs = np.random.default_rng(1).choice(cfg.B, 4, replace=False)
-    counts = staged_rnn_check(cfg, inp, w, g, requests=reqs)
-    _say(f"[gpu]   {counts}; N = {int(g['n_total'][0])}")
+    _say("[gpu]   GPU cycle done; oracle cycle running")
+    _say(f"[gpu]   {rnn_check(cfg, inp, w, g)}; N = {int(g['n_total'][0])}")
