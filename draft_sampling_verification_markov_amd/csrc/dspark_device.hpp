@@ -90,6 +90,12 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+// Workgroup barrier ordering LDS only: this wave's LDS operations complete
+// first; vector-memory operations (LDS DMA included) are the caller's to wait
+// for.  __syncthreads() carries a release fence that drains every load of the
+// wave, prefetches meant to stay in flight included.  The memory clobber keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds_only() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // float -> bfloat16 bits, round to nearest, ties to even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);

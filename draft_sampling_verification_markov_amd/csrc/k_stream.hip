@@ -418,12 +418,6 @@ __device__ __forceinline__ void chunk_range(int g, int G, int nchunks, int& c_be
 
 // waits until every vector-memory operation of this wave has completed
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// Workgroup barrier ordering LDS only: this wave's LDS operations complete
-// first; vector-memory operations (LDS DMA included) are the caller's to wait
-// for.  __syncthreads() carries a release fence that drains every load of the
-// wave, prefetches meant to stay in flight included.  The memory clobber keeps
-// the compiler from moving memory accesses across it.
-__device__ __forceinline__ void barrier_lds_only() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // wait until at most N vector-memory operations of this wave are outstanding
 // (they complete in issue order), lgkm and export counters untouched
 template <int N>

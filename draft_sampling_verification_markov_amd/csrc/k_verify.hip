@@ -109,7 +109,8 @@ __device__ __forceinline__ const ZT* vlse_row(const VerifyArgs& a, int w, int& b
 }
 
 // (row, segment) items, round-robin over the workgroups; the loads of the next
-// item are in flight while the current one is reduced.
+// item are in flight while the current one is reduced (the workgroup joins its
+// waves with LDS-only barriers, which leave those loads in flight).
 template <typename ZT>
 __global__ __launch_bounds__(256) void k_vlse(VerifyArgs a) {
   using Vec = Vec16<ZT>;
@@ -133,31 +134,36 @@ __global__ __launch_bounds__(256) void k_vlse(VerifyArgs a) {
       const ZT* rown = vlse_row<ZT>(a, wn, bn, kn, segn);
       nxt.load(rown, segn * kVlseSeg, a.V, tid);
     }
+    // VALU-bound (one transcendental per entry): the max is taken on the raw
+    // logits, the temperature folds into one fma per entry, and only the last
+    // segment of a row masks entries past V (V is a multiple of 8: a 16-byte
+    // piece is wholly inside or outside)
     const int lo = seg * kVlseSeg;
+    const bool full = lo + kVlseSeg <= a.V;
     float x[kPer];
     float m = -INFINITY;
 #pragma unroll
     for (int l = 0; l < It::kLoads; ++l) {
-      const int v = lo + (l * 256 + tid) * Vec::N;
       Vec::load(reinterpret_cast<const ZT*>(&cur.raw[l]), x + l * Vec::N);
+      if (!full && lo + (l * 256 + tid) * Vec::N >= a.V) {
 #pragma unroll
-      for (int i = 0; i < Vec::N; ++i) {
-        x[l * Vec::N + i] = v < a.V ? x[l * Vec::N + i] * a.scale2 : -INFINITY;
-        m = fmaxf(m, x[l * Vec::N + i]);
+        for (int i = 0; i < Vec::N; ++i) x[l * Vec::N + i] = -INFINITY;
       }
+#pragma unroll
+      for (int i = 0; i < Vec::N; ++i) m = fmaxf(m, x[l * Vec::N + i]);
     }
     m = wave_max(m);
     if (lane == 0) s_m[wave] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    barrier_lds_only();
+    m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3])) * a.scale2;  // base-2 units
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) s += exp2f(x[i] - m);
+    for (int i = 0; i < kPer; ++i) s += exp2f(fmaf(x[i], a.scale2, -m));
     s = wave_sum(s);
     if (lane == 0) s_s[wave] = s;
-    __syncthreads();
+    barrier_lds_only();
     if (tid == 0) a.vlse[((size_t)b * a.K + k0) * a.nseg + seg] = make_float2(m, s_s[0] + s_s[1] + s_s[2] + s_s[3]);
-    __syncthreads();
+    barrier_lds_only();
     cur = nxt;
     b = bn;
     k0 = kn;
