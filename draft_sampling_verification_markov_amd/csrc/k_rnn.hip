@@ -124,16 +124,20 @@ __global__ __launch_bounds__(256) void k_rnn_gemm(const uint16_t* __restrict__ H
 }
 
 // ------------------------------------------------------------------ one step
-// One workgroup of four waves per (32 requests, 32 state entries).  Three MFMA
-// tiles per product (gates r, z, n of the same 32 entries): A = rows of W
-// (bf16), B = the requests' operands.  The embedding operand E[x_{k-1}] is exact
-// in bf16; the fp32 state enters the recurrent product as hi + lo, two bf16
-// terms (hi = bf16(s), lo = bf16(s - hi)), which leaves a relative error of at
-// most 2^-18 per entry.  Wave w takes a quarter of the K-steps; the partial
-// accumulators are summed through LDS in wave order, and wave w then finishes
-// the cell for accumulator entries 4w..4w+3 (four of the 16 entries of each lane).
+// One workgroup of four waves per (16 requests, 16 state entries): 256
+// workgroups at B = r = 256, so each CU takes in only its 48 weight rows and
+// 16 requests' operands.  v_mfma_f32_16x16x32_bf16 tiles, three per product
+// (gates r, z, n of the same 16 entries): A = rows of W (bf16), B = the
+// requests' operands.  The embedding operand E[x_{k-1}] is exact in bf16; the
+// fp32 state enters the recurrent product as hi + lo, two bf16 terms
+// (hi = bf16(s), lo = bf16(s - hi)), which leaves a relative error of at most
+// 2^-18 per entry.  Wave w takes a quarter of the K-steps of each product; the
+// partial accumulators are summed through LDS in wave order, and wave w then
+// finishes the cell for accumulator row w of every lane (one entry per lane).
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 constexpr int kStepWaves = 4;
-constexpr int kStepUnroll = 4;  // K-steps per wave at r = 256, all loads in flight together
+constexpr int kStepTile = 16;   // requests and state entries per workgroup
+constexpr int kStepMaxK = 2;    // K-steps of 32 per wave and product at r = 256 (held in registers)
 
 struct RnnStepArgs {
   const float* Gh;          // [B*K][3r]: hidden-state part of a, with b_ih
@@ -163,133 +167,117 @@ __device__ __forceinline__ void split_bf16x8(const float4 x0, const float4 x1, b
 }
 
 struct StepLds {
-  float acc[kStepWaves][6][16][64];  // partial accumulators: [wave][a_r a_z a_n c_r c_z c_n][entry][lane]
-  float sk[32][33];                  // s_k of the block: [request][entry]
+  float acc[kStepWaves][6][4][64];      // partials: [wave][a_r a_z a_n c_r c_z c_n][row][lane]
+  float sk[kStepTile][kStepTile + 1];   // s_k of the block: [request][entry]
 };
 
-__global__ __launch_bounds__(256) void k_rnn_step(RnnStepArgs a) {
+__global__ __launch_bounds__(64 * kStepWaves) void k_rnn_step(RnnStepArgs a) {
   __shared__ StepLds L;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31, half = lane >> 5;
-  const int b0 = blockIdx.x * 32, j0 = blockIdx.y * 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, quad = lane >> 4;  // MFMA column (request) and k-group
+  const int b0 = blockIdx.x * kStepTile, j0 = blockIdx.y * kStepTile;
   const int R = a.r, K = a.K, k = a.k, ldw = a.d + R;
   const int b = b0 + col;
   const bool live = b < a.B;
   const bool has_prev_state = live && k >= 2;
 
-  // the epilogue's operands first (they do not depend on the products): entries
-  // jj = 8*(e/4) + 4*half + e%4 for e = 4*wave .. 4*wave + 3, i.e. 8*wave + 4*half + 0..3
-  const int jb = j0 + 8 * wave + 4 * half;
-  float ghv[3][4], bhv[3][4], spv[4];
+  // the epilogue's operands first (they do not depend on the products):
+  // accumulator row `wave` of this lane is state entry j0 + 4*quad + wave
+  const int je = j0 + 4 * quad + wave;
+  float ghv[3] = {0.f, 0.f, 0.f}, bhv[3] = {0.f, 0.f, 0.f}, spv = 0.f;
   if (live) {
     const float* gh = a.Gh + ((size_t)b * K + (k - 1)) * (3 * R);
-    const float* sp = a.state + ((size_t)b * K + (k >= 2 ? k - 2 : 0)) * R;
 #pragma unroll
     for (int g = 0; g < 3; ++g) {
-      const float4 x = *reinterpret_cast<const float4*>(gh + g * R + jb);
-      const float4 y = *reinterpret_cast<const float4*>(a.b_hh + g * R + jb);
-      ghv[g][0] = x.x; ghv[g][1] = x.y; ghv[g][2] = x.z; ghv[g][3] = x.w;
-      bhv[g][0] = y.x; bhv[g][1] = y.y; bhv[g][2] = y.z; bhv[g][3] = y.w;
+      ghv[g] = gh[g * R + je];
+      bhv[g] = a.b_hh[g * R + je];
     }
-    const float4 z = k >= 2 ? *reinterpret_cast<const float4*>(sp + jb) : make_float4(0.f, 0.f, 0.f, 0.f);
-    spv[0] = z.x; spv[1] = z.y; spv[2] = z.z; spv[3] = z.w;
+    if (k >= 2) spv = a.state[((size_t)b * K + (k - 2)) * R + je];
   }
 
-  // products over this wave's K-steps
-  const int prev = live ? clamp_id(k == 1 ? a.anchor[b] : a.tok[(size_t)b * K + k - 2], a.V) : 0;
-  const uint16_t* erow = a.E + (size_t)prev * R + 8 * half;  // its loads are issued after the weights'
-  const float* srow = a.state + ((size_t)(live ? b : 0) * K + (k >= 2 ? k - 2 : 0)) * R + 8 * half;
-  const uint16_t* wi[3];
-  const uint16_t* wh[3];
+  // products over this wave's K-steps (32 wide): weights and states first, the
+  // token-dependent embedding row last
+  const int nt = R / 32, per = (nt + kStepWaves - 1) / kStepWaves;
+  const int t0 = wave * per, t1 = min(nt, t0 + per);
+  const float* srow = a.state + ((size_t)(live ? b : 0) * K + (k >= 2 ? k - 2 : 0)) * R + 8 * quad;
+  bf16x8_t aw[kStepMaxK][3], hw[kStepMaxK][3], bh[kStepMaxK], bl[kStepMaxK], be[kStepMaxK];
 #pragma unroll
-  for (int g = 0; g < 3; ++g) {
-    const size_t row = (size_t)g * R + j0 + col;
-    wi[g] = a.W_ih + row * ldw + a.d + 8 * half;
-    wh[g] = a.W_hh + row * R + 8 * half;
+  for (int u = 0; u < kStepMaxK; ++u) {
+    const int t = t0 + u;
+    if (t >= t1) break;
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+      const size_t row = (size_t)g * R + j0 + col;
+      aw[u][g] = *reinterpret_cast<const bf16x8_t*>(a.W_ih + row * ldw + a.d + 32 * t + 8 * quad);
+      hw[u][g] = *reinterpret_cast<const bf16x8_t*>(a.W_hh + row * R + 32 * t + 8 * quad);
+    }
+    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+    if (has_prev_state) {
+      x0 = *reinterpret_cast<const float4*>(srow + 32 * t);
+      x1 = *reinterpret_cast<const float4*>(srow + 32 * t + 4);
+    }
+    split_bf16x8(x0, x1, bh[u], bl[u]);
   }
-  f32x16_t acc_a[3], acc_c[3];
+  const int prev = live ? clamp_id(k == 1 ? a.anchor[b] : a.tok[(size_t)b * K + k - 2], a.V) : 0;
+  const uint16_t* erow = a.E + (size_t)prev * R + 8 * quad;
 #pragma unroll
-  for (int g = 0; g < 3; ++g) { acc_a[g] = f32x16_t{}; acc_c[g] = f32x16_t{}; }
-  const int nt = R / 16, per = (nt + kStepWaves - 1) / kStepWaves;
-  const int t_begin = wave * per, t_end = min(nt, t_begin + per);
-  for (int t0 = t_begin; t0 < t_end; t0 += kStepUnroll) {
-    bf16x8_t be[kStepUnroll], bh[kStepUnroll], bl[kStepUnroll], aw[kStepUnroll][3], hw[kStepUnroll][3];
+  for (int u = 0; u < kStepMaxK; ++u) {
+    const int t = t0 + u;
+    if (t >= t1) break;
+    be[u] = live ? *reinterpret_cast<const bf16x8_t*>(erow + 32 * t) : bf16x8_t{};
+  }
+  f32x4_t acc_a[3], acc_c[3];
 #pragma unroll
-    for (int u = 0; u < kStepUnroll; ++u) {  // weights and states: independent of the previous token
-      const int t = t0 + u;
-      if (t >= t_end) break;
+  for (int g = 0; g < 3; ++g) { acc_a[g] = f32x4_t{}; acc_c[g] = f32x4_t{}; }
 #pragma unroll
-      for (int g = 0; g < 3; ++g) {
-        aw[u][g] = *reinterpret_cast<const bf16x8_t*>(wi[g] + 16 * t);
-        hw[u][g] = *reinterpret_cast<const bf16x8_t*>(wh[g] + 16 * t);
-      }
-      float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-      if (has_prev_state) {
-        x0 = *reinterpret_cast<const float4*>(srow + 16 * t);
-        x1 = *reinterpret_cast<const float4*>(srow + 16 * t + 4);
-      }
-      split_bf16x8(x0, x1, bh[u], bl[u]);
+  for (int u = 0; u < kStepMaxK; ++u) {
+    if (t0 + u >= t1) break;
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+      acc_a[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[u][g], be[u], acc_a[g], 0, 0, 0);
+      acc_c[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hw[u][g], bh[u], acc_c[g], 0, 0, 0);
+      acc_c[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hw[u][g], bl[u], acc_c[g], 0, 0, 0);
     }
-#pragma unroll
-    for (int u = 0; u < kStepUnroll; ++u) {
-      const int t = t0 + u;
-      if (t >= t_end) break;
-      be[u] = live ? *reinterpret_cast<const bf16x8_t*>(erow + 16 * t) : bf16x8_t{};
-    }
-#pragma unroll
-    for (int u = 0; u < kStepUnroll; ++u)
-#pragma unroll
-      for (int g = 0; g < 3; ++g) {
-        if (t0 + u >= t_end) break;
-        acc_a[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[u][g], be[u], acc_a[g], 0, 0, 0);
-        acc_c[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hw[u][g], bh[u], acc_c[g], 0, 0, 0);
-        acc_c[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hw[u][g], bl[u], acc_c[g], 0, 0, 0);
-      }
   }
 #pragma unroll
   for (int g = 0; g < 3; ++g)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < 4; ++e) {
       L.acc[wave][g][e][lane] = acc_a[g][e];
       L.acc[wave][3 + g][e][lane] = acc_c[g][e];
     }
   __syncthreads();
 
-  // wave w: entries e = 4w..4w+3 of every lane, partials summed in wave order
+  // wave w: accumulator row w of every lane, partials summed in wave order
   if (live) {
-    float* so = a.state + ((size_t)b * K + (k - 1)) * R;
-    float sv[4];
+    float v[6];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = 4 * wave + q;
-      float v[6];
+    for (int m = 0; m < 6; ++m) {
+      float t = L.acc[0][m][wave][lane];
 #pragma unroll
-      for (int m = 0; m < 6; ++m) {
-        float t = L.acc[0][m][e][lane];
-#pragma unroll
-        for (int w = 1; w < kStepWaves; ++w) t += L.acc[w][m][e][lane];
-        v[m] = t;
-      }
-      const float ar = ghv[0][q] + v[0], az = ghv[1][q] + v[1], an = ghv[2][q] + v[2];
-      const float cr = bhv[0][q] + v[3], cz = bhv[1][q] + v[4], cn = bhv[2][q] + v[5];
-      const float rho = 1.f / (1.f + expf(-(ar + cr)));
-      const float z = 1.f / (1.f + expf(-(az + cz)));
-      const float n = tanhf(an + rho * cn);
-      sv[q] = (1.f - z) * n + z * spv[q];
-      L.sk[col][jb - j0 + q] = sv[q];
+      for (int q = 1; q < kStepWaves; ++q) t += L.acc[q][m][wave][lane];
+      v[m] = t;
     }
-    *reinterpret_cast<float4*>(so + jb) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+    const float ar = ghv[0] + v[0], az = ghv[1] + v[1], an = ghv[2] + v[2];
+    const float cr = bhv[0] + v[3], cz = bhv[1] + v[4], cn = bhv[2] + v[5];
+    const float rho = 1.f / (1.f + expf(-(ar + cr)));
+    const float z = 1.f / (1.f + expf(-(az + cz)));
+    const float n = tanhf(an + rho * cn);
+    const float sv = (1.f - z) * n + z * spv;
+    a.state[((size_t)b * K + (k - 1)) * R + je] = sv;
+    L.sk[col][je - j0] = sv;
   }
   if (!a.efrag) return;
   __syncthreads();
-  // bf16(s_k) in B-fragment order: per request of the block 4 pieces of 8 entries
-  if (tid < 128) {
-    const int qq = tid >> 2, piece = tid & 3, bb = b0 + qq;
+  // bf16(s_k) in B-fragment order: per request of the block 2 pieces of 8 entries
+  if (tid < kStepTile * 2) {
+    const int qq = tid >> 1, piece = tid & 1, bb = b0 + qq;
     if (bb < a.B) {
       const float* src = &L.sk[qq][8 * piece];
-      const uint4 v = make_uint4(pack_bf16x2(src[0], src[1]), pack_bf16x2(src[2], src[3]),
-                                 pack_bf16x2(src[4], src[5]), pack_bf16x2(src[6], src[7]));
+      const uint4 val = make_uint4(pack_bf16x2(src[0], src[1]), pack_bf16x2(src[2], src[3]),
+                                   pack_bf16x2(src[4], src[5]), pack_bf16x2(src[6], src[7]));
       const int p = (j0 >> 3) + piece;  // 8-entry piece index within the row
-      a.efrag[((size_t)(bb >> 5) * (R >> 4) + (p >> 1)) * 64 + (bb & 31) + 32 * (p & 1)] = v;
+      a.efrag[((size_t)(bb >> 5) * (R >> 4) + (p >> 1)) * 64 + (bb & 31) + 32 * (p & 1)] = val;
     }
   }
 }
@@ -329,7 +317,7 @@ hipError_t launch_rnn_step(const dspark_problem& P, const float* Gh, const void*
   a.state = state;
   a.efrag = efrag;
   a.B = P.B; a.K = P.K; a.V = P.V; a.d = P.d; a.r = P.r; a.k = k;
-  dim3 grid((P.B + 31) / 32, P.r / 32);
+  dim3 grid((P.B + kStepTile - 1) / kStepTile, P.r / kStepTile);
   hipLaunchKernelGGL(k_rnn_step, grid, 64 * kStepWaves, 0, s, a);
   return hipGetLastError();
 }
