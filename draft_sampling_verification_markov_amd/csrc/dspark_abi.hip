@@ -161,12 +161,12 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
   if (rnn) {
     se.state = rnn->state;
     if (launch_rnn_gemm(p, h, rnn->W_ih, rnn->b_ih, Gh, stream) != hipSuccess) return DSPARK_E_LAUNCH;
-  } else if (use_efrag && launch_efrag_gather(p, E, anchor, efrag, stream) != hipSuccess) {
-    return DSPARK_E_LAUNCH;
   }
   for (int k = 1; k <= p.K; ++k) {
     sa.k = k;
     se.k = k;
+    // Markov head: step 1 gathers the anchors' E rows itself
+    sa.first_from_anchor = !rnn && use_efrag && k == 1;
     // Markov head: the select kernel stores the fragments of position k for step k + 1;
     // RNN head: the step kernel stores those of the state of position k before step k
     se.efrag = !rnn && use_efrag && k < p.K ? efrag : nullptr;

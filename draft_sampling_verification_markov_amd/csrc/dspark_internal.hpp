@@ -70,6 +70,7 @@ struct StreamArgs {
   const int32_t* n_sched;// [B] (verify)
   float4* part;          // [B][G]
   const uint4* efrag;    // B fragments of the previous tokens (draft kernel with bf16 logits and factors)
+  int first_from_anchor; // draft kernel with bf16 logits and factors: B fragments gathered from E[anchor]
   int B, K, V, k;        // k: 1-based draft position (draft mode)
   int nchunks;
   float scale2;          // log2(e) / T_s
@@ -160,11 +161,9 @@ hipError_t launch_rnn_step(const dspark_problem& P, const float* Gh, const void*
 // Launchers; each returns hipSuccess or the launch error.
 hipError_t launch_stream_draft(const dspark_problem& P, const StreamArgs& a, int G, hipStream_t s);
 // true when the draft step runs the buffer-DMA kernel, which takes its B
-// fragments from the efrag region (filled by launch_efrag_gather for the
-// anchors and by the select kernel for later positions)
+// fragments from the efrag region (filled by the select kernel of the previous
+// position; position 1 gathers the anchors' E rows itself)
 bool draft_uses_efrag(const dspark_problem& P);
-hipError_t launch_efrag_gather(const dspark_problem& P, const void* E, const int32_t* tok, uint4* efrag,
-                               hipStream_t s);
 hipError_t launch_stream_verify(const dspark_problem& P, const StreamArgs& a, int G, hipStream_t s);
 // true when the verify resample pass runs the buffer-DMA kernel, which takes
 // its B fragments from the efrag region (filled by k_accept)

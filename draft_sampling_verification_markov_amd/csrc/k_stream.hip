@@ -416,6 +416,7 @@ __device__ __forceinline__ void chunk_range(int g, int G, int nchunks, int& c_be
   c_end = c_begin + (int)q + (ug < rem ? 1 : 0);
 }
 
+
 // waits until every vector-memory operation of this wave has completed
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // wait until at most N vector-memory operations of this wave are outstanding
@@ -512,6 +513,8 @@ struct DraftDma {
     }
   }
 };
+
+
 
 // 128-bit buffer descriptor over [base, base + bytes) (raw; reads past the end return 0)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -875,15 +878,16 @@ struct ChunkGumbels {
   }
 };
 
-template <int R>
-__global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
+// FIRST (position 1 of the Markov head): the B fragments are the E rows of the
+// anchors, gathered straight from E (two lanes per row, one 16-byte piece per
+// K-step each) instead of from the fragment-ordered region a select kernel
+// wrote.  buf0 / buf1: the two LDS stages, distinct __shared__ objects of the
+// kernel (the compiler gives them separate alias scopes, so reads of one stage
+// need not wait for the DMA still landing in the other).
+template <int R, bool FIRST>
+__device__ __forceinline__ void draft_step(const StreamArgs& a, unsigned char* buf0, unsigned char* buf1) {
   using T = DraftTiles<R>;
   using D = DraftUnit<R>;
-  // Two distinct LDS objects: the compiler gives them separate alias scopes, so
-  // reads of one stage need not wait for the DMA still landing in the other.
-  __shared__ __attribute__((aligned(1024))) unsigned char buf0[T::kStage];
-  __shared__ __attribute__((aligned(1024))) unsigned char buf1[T::kStage];
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x, g = blockIdx.x;
   int c_begin, c_end;
@@ -912,11 +916,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
     // previous tokens, stored in fragment order so that each K-step is one
     // contiguous 1 KB block), then the second unit's tiles.  Compute starts
     // when all but the second unit have landed; the first chunk Gumbels are
-    // drawn in the meantime.
+    // drawn in the meantime.  (FIRST: the anchor is loaded ahead of the first
+    // stage, so waiting for it leaves that stage in flight.)
+    int anc = 0;
+    if (FIRST) anc = a.anchor[rv ? b : B - 1];
+    __builtin_amdgcn_sched_barrier(0);
     dma.stage(buf0, zr, wr, vb, wave);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8_t bfrag[T::kSteps];
-    {
+    if (FIRST) {
+      const bf16x8_t* src =
+          reinterpret_cast<const bf16x8_t*>(static_cast<const uint16_t*>(a.E) + (size_t)clamp_id(anc, V) * R + 8 * h);
+#pragma unroll
+      for (int t = 0; t < T::kSteps; ++t) bfrag[t] = src[2 * t];
+    } else {
       const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(a.efrag) + (size_t)((base >> 5) + wave) * T::kSteps * 64 + lane;
 #pragma unroll
       for (int t = 0; t < T::kSteps; ++t) bfrag[t] = src[t * 64];  // rows past B: unwritten slots, own column only
@@ -1003,6 +1016,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
     __syncthreads();  // the next pass restages buf0
     if (rv && lane < 32) a.part[(size_t)b * G + g] = make_float4(st.run_m, st.run_s, st.best, __int_as_float(st.best_c));
   }
+}
+
+template <int R>
+__global__ __launch_bounds__(kThreads, 1) void k_draft(StreamArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[DraftTiles<R>::kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[DraftTiles<R>::kStage];
+  draft_step<R, false>(a, buf0, buf1);
+}
+
+template <int R>
+__global__ __launch_bounds__(kThreads, 1) void k_draft_first(StreamArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[DraftTiles<R>::kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[DraftTiles<R>::kStage];
+  draft_step<R, true>(a, buf0, buf1);
 }
 
 
@@ -1309,17 +1336,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify_stream(StreamArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- B fragments
-// One thread per 16-byte piece: the fragments of tok[b] for every row b.
-__global__ __launch_bounds__(256) void k_efrag_gather(const uint16_t* E, const int32_t* tok, uint4* efrag, int B,
-                                                      int V, int r) {
-  const int per = r >> 3;
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (long long)B * per) return;
-  const int b = (int)(i / per), p = (int)(i % per);
-  efrag_store_piece(efrag, E, clamp_id(tok[b], V), b, r, p);
-}
-
 // ---------------------------------------------------------------- select kernel
 // One workgroup per row.  The loads that do not depend on the winning chunk
 // (the previous token, then its E half row) are issued before the partials
@@ -1466,13 +1482,16 @@ constexpr int kVerifyStages = DSPARK_VERIFY_STAGES;
     case 256: hipLaunchKernelGGL((k_verify_stream<256, kVerifyStages>), G, kThreads, 0, s, a); break;   \
     default: return hipErrorInvalidValue;                                              \
   }
+#define DSPARK_DRAFT_K(R)                                                              \
+  if (a.first_from_anchor) hipLaunchKernelGGL((k_draft_first<R>), G, kThreads, 0, s, a); \
+  else hipLaunchKernelGGL((k_draft<R>), G, kThreads, 0, s, a);
 #define DSPARK_R_CASES_DRAFT16                                                         \
   switch (P.r) {                                                                       \
-    case 16: hipLaunchKernelGGL((k_draft<16>), G, kThreads, 0, s, a); break;             \
-    case 32: hipLaunchKernelGGL((k_draft<32>), G, kThreads, 0, s, a); break;             \
-    case 64: hipLaunchKernelGGL((k_draft<64>), G, kThreads, 0, s, a); break;             \
-    case 128: hipLaunchKernelGGL((k_draft<128>), G, kThreads, 0, s, a); break;           \
-    case 256: hipLaunchKernelGGL((k_draft<256>), G, kThreads, 0, s, a); break;           \
+    case 16: DSPARK_DRAFT_K(16) break;                                                 \
+    case 32: DSPARK_DRAFT_K(32) break;                                                 \
+    case 64: DSPARK_DRAFT_K(64) break;                                                 \
+    case 128: DSPARK_DRAFT_K(128) break;                                               \
+    case 256: DSPARK_DRAFT_K(256) break;                                               \
     default: return hipErrorInvalidValue;                                              \
   }
 #define DSPARK_R_CASES_GENERIC(ZT, WT, MODE)                                                      \
@@ -1541,14 +1560,6 @@ bool verify_uses_efrag(const dspark_problem& P) {
   return P.logits_dtype == DSPARK_BF16 && P.weight_dtype == DSPARK_BF16 &&
          (unsigned long long)kRowsPerPass * (P.K + 1) * (unsigned long long)P.V * 2ull < (1ull << 31) &&
          (unsigned long long)P.V * (unsigned long long)P.r * 2ull < (1ull << 31);
-}
-
-hipError_t launch_efrag_gather(const dspark_problem& P, const void* E, const int32_t* tok, uint4* efrag,
-                               hipStream_t s) {
-  const long long n = (long long)P.B * (P.r / 8);
-  hipLaunchKernelGGL(k_efrag_gather, (unsigned)((n + 255) / 256), 256, 0, s, static_cast<const uint16_t*>(E), tok,
-                     efrag, P.B, P.V, P.r);
-  return hipGetLastError();
 }
 
 hipError_t launch_stream_draft(const dspark_problem& P, const StreamArgs& a, int G, hipStream_t s) {
