@@ -121,6 +121,16 @@ def traffic_from_profile(workload: str):
     return float(rec["hbm_bytes_per_launch"])
 
 
+def mfma_from_profile(workload: str):
+    """MFMA counters of the draft-step kernel (bf16 MFMA flops per launch, MFMA busy
+    share of the SIMD cycles) from the committed profile record, if it was taken on
+    the current kernel source; else None."""
+    rec = _profile_record(workload)
+    if rec is None or rec.get("kernel_source_sha256") != kernel_source_hash() or not rec.get("mfma"):
+        return None
+    return rec["mfma"].get(DOMINANT)
+
+
 def step_kernels(cfg) -> dict:
     """The kernels of one step of the first-drop cycle (dspark_draft, dspark_schedule,
     dspark_verify with bf16 logits and factors) and how often each runs per step."""
@@ -198,13 +208,17 @@ def _csv_rows(directory: str, suffix: str):
 
 
 def _pmc_means(directory: str, counter: str):
-    """Mean counter value (KiB) per dispatch, by short kernel name."""
-    acc = {}
+    """Mean counter value per dispatch, by short kernel name (rows of one dispatch,
+    if the counter is reported per hardware instance, are summed first)."""
+    per_dispatch = {}
     for r in _csv_rows(directory, "counter_collection.csv"):
         if r["Counter_Name"] != counter:
             continue
-        k = _short_kernel_name(r["Kernel_Name"])
-        acc.setdefault(k, []).append(float(r["Counter_Value"]))
+        key = (_short_kernel_name(r["Kernel_Name"]), r.get("Dispatch_Id", id(r)))
+        per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    acc = {}
+    for (k, _), v in per_dispatch.items():
+        acc.setdefault(k, []).append(v)
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
@@ -214,6 +228,7 @@ rocprofv3 --pmc FETCH_SIZE -d $OUT/fetch -o fetch --output-format csv -- python3
 rocprofv3 --pmc WRITE_SIZE -d $OUT/write -o write --output-format csv -- python3 $R/bench.py --main-only --steps 2 --warmup 1 --no-cpu-baseline
 rocprofv3 --pmc FETCH_SIZE -d $OUT/cfetch -o cfetch --output-format csv -- python3 $R/bench.py --calibrate-copy
 rocprofv3 --pmc WRITE_SIZE -d $OUT/cwrite -o cwrite --output-format csv -- python3 $R/bench.py --calibrate-copy
+rocprofv3 --pmc MfmaFlopsBF16 MfmaUtil -d $OUT/mfma -o mfma --output-format csv -- python3 $R/bench.py --main-only --steps 2 --warmup 1 --no-cpu-baseline
 python3 $R/bench.py --summarize-profiles $OUT"""
 
 
@@ -258,6 +273,24 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
             continue
         w = write.get(k, 0.0)
         lines.append(f"| {k} | {fetch[k]:.1f} | {w:.1f} | {(fetch[k] * fscale + w * wscale) * 1024 / 1e6:.1f} |")
+    # MFMA work of the kernels that use the matrix cores: bf16 MFMA flops per
+    # dispatch, and the MFMA busy cycles over the active cycles of all SIMDs
+    mfma = None
+    if os.path.isdir(os.path.join(prof_dir, "mfma")):
+        flops = _pmc_means(os.path.join(prof_dir, "mfma"), "MfmaFlopsBF16")
+        util = _pmc_means(os.path.join(prof_dir, "mfma"), "MfmaUtil")
+        avg_us = {_short_kernel_name(r["Name"]): float(r["AverageNs"]) / 1e3 for r in rows}
+        mfma = {}
+        lines += ["", "## MFMA work (bf16), per dispatch", "",
+                  "| kernel | MFMA GFLOP | MFMA busy % of SIMD cycles | TFLOP/s over the traced average | "
+                  "% of the 2.5 PFLOP/s bf16 peak |", "|---|---:|---:|---:|---:|"]
+        for k in sorted(flops, key=lambda k: -flops[k]):
+            if flops[k] <= 0 or not k.startswith("k_"):
+                continue
+            tf = flops[k] / (avg_us[k] * 1e-6) / 1e12 if k in avg_us else float("nan")
+            mfma[k] = {"gflop": flops[k] / 1e9, "busy_pct": util.get(k), "tflops": tf}
+            lines.append(f"| {k} | {flops[k] / 1e9:.2f} | {util.get(k, float('nan')):.1f} | {tf:.0f} | "
+                         f"{100 * tf / 2500:.1f} |")
     lines += ["", f"Library source: commit {commit} (kernel sources sha256 {src[:16]}...)."]
     with open(os.path.join(PROFILE_DIR, f"cycle_{workload}_hbm_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -268,6 +301,7 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
            "fetch_kib_per_launch": fetch[DOMINANT], "write_kib_per_launch": write.get(DOMINANT, 0.0),
            "fetch_scale": fscale, "write_scale": wscale,
            "hbm_bytes_per_launch": (fetch[DOMINANT] * fscale + write.get(DOMINANT, 0.0) * wscale) * 1024,
+           "mfma": mfma,
            "source": f"profiles/cycle_{workload}_hbm_counters.md"}
     with open(os.path.join(PROFILE_DIR, f"{DOMINANT}_{workload}_pmc.json"), "w") as f:
         json.dump(rec, f, indent=1)
@@ -548,6 +582,7 @@ def main() -> int:
     achieved = launch_bytes / (k_ms / 1e3) / 1e9
     traffic = traffic_from_profile(cfg.name)
     step_traffic = step_traffic_from_profile(cfg)
+    mfma = mfma_from_profile(cfg.name)
 
     line = {
         "metric": METRIC,
@@ -579,6 +614,14 @@ def main() -> int:
         "rnn_head": rnn_line,
         "scheduled_N": N,
         "mean_accepted": float(g["n_acc"].mean()),
+        "mfma_bias": None if mfma is None else {
+            "kernel": f"{DOMINANT} (bias contraction E[x]·Wt^T on v_mfma_f32_32x32x16_bf16)",
+            "gflop_per_launch_counted": mfma["gflop"],
+            "gflop_per_launch_algorithmic": 2.0 * cfg.B * cfg.r * cfg.V / 1e9,
+            "tflops": mfma["gflop"] / k_ms,
+            "frac_of_bf16_peak": mfma["gflop"] / k_ms / 2500.0,
+            "mfma_busy_pct": mfma["busy_pct"],
+            "source": f"profiles/cycle_{cfg.name}_hbm_counters.md"},
         "roofline": {
             "kernel": f"{DOMINANT} (draft steps 2..K)",
             "bound": "hbm",
