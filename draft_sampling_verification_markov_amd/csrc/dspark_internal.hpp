@@ -171,7 +171,10 @@ bool verify_uses_efrag(const dspark_problem& P);
 hipError_t launch_select(const dspark_problem& P, const SelectArgs& a, hipStream_t s);
 hipError_t launch_conf(const dspark_problem& P, const ConfArgs& a, hipStream_t s);
 // Segments of the candidate range that the partial-rank kernel splits the comparisons into.
-constexpr int kSchedSegMax = 16;
+#ifndef DSPARK_SCHED_SEG_MAX
+#define DSPARK_SCHED_SEG_MAX 16
+#endif
+constexpr int kSchedSegMax = DSPARK_SCHED_SEG_MAX;
 int sched_segments(int n);
 hipError_t launch_schedule(const dspark_problem& P, const float* surv, const float* T, int32_t* n_sched,
                            int32_t* n_total, int32_t* part, float* sorted_s, int32_t* sorted_i, hipStream_t s);

@@ -1457,6 +1457,179 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   }
 }
 
+// Select kernel for bf16 factors.  The winning chunk's Wt rows form one
+// contiguous block (128 rows x R); the 256 threads read it in 16-byte pieces,
+// consecutive threads on consecutive pieces, so every wave instruction reads
+// 1 KB of contiguous memory.  Thread t then holds column piece t % PR of rows
+// i * (256 / PR) + t / PR (i < PR / 2; PR = R / 8 pieces per row) and the
+// matching piece of the Markov operand (E[x_{k-1}], or the RNN state rounded
+// to bf16), one 16-byte load per thread instead of a half row per thread.  The
+// partial dot products go through LDS once: thread r < 128 sums the PR
+// partials of row r in column order (a cross-lane shuffle tree costs more).
+__device__ __forceinline__ float dot_bf16x8(uint4 e, uint4 w) {
+  float acc = 0.f;
+  acc = fmaf(bf16_lo(e.x), bf16_lo(w.x), acc);
+  acc = fmaf(bf16_hi(e.x), bf16_hi(w.x), acc);
+  acc = fmaf(bf16_lo(e.y), bf16_lo(w.y), acc);
+  acc = fmaf(bf16_hi(e.y), bf16_hi(w.y), acc);
+  acc = fmaf(bf16_lo(e.z), bf16_lo(w.z), acc);
+  acc = fmaf(bf16_hi(e.z), bf16_hi(w.z), acc);
+  acc = fmaf(bf16_lo(e.w), bf16_lo(w.w), acc);
+  acc = fmaf(bf16_hi(e.w), bf16_hi(w.w), acc);
+  return acc;
+}
+
+template <typename ZT, int R>
+__global__ __launch_bounds__(256) void k_select_b16(SelectArgs a) {
+  constexpr int PR = R / 8;                         // 16-byte pieces per Wt row (2..32)
+  constexpr int NP = PR / 2;                        // pieces per thread (1..16)
+  constexpr int RG = 256 / PR;                      // rows per piece step
+  constexpr int STR = PR % 4 == 0 ? PR + 4 : PR;    // LDS row stride of the partials (floats)
+  static_assert(NP * RG == kChunk, "one chunk of rows over the workgroup");
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, V = a.V;
+  __shared__ float s_m[4], s_s[4], s_best[4], s_ell[kChunk];
+  __shared__ __attribute__((aligned(16))) float s_part[kChunk * STR];
+  __shared__ int s_c[4];
+  const int c = tid % PR, grp = tid / PR;
+
+  // the previous token and the partials (G <= 256: at most one per thread);
+  // the piece of the Markov operand is requested with the Wt block below, so
+  // that the merge waits for nothing else.  (Unconditional loads, values past
+  // G masked: a branch around a load makes the compiler wait for every load in
+  // flight before later ones.)
+  const int prev_raw = a.k == 1 ? a.anchor[b] : a.tok[(size_t)b * K + a.k - 2];
+  float4 p = a.part[(size_t)b * a.G + (tid < a.G ? tid : 0)];
+  if (tid >= a.G) p = make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
+
+  // 1. the winning chunk of row b: argmax of the chunk scores over the partials
+  float best = -INFINITY;
+  int bc = 0x7fffffff;
+  if (tid < a.G) {
+    const int pc = __float_as_int(p.w);
+    if (better(p.z, pc, best, bc)) {
+      best = p.z;
+      bc = pc;
+    }
+  }
+  wave_argmax(best, bc);
+  if (lane == 0) {
+    s_best[wave] = best;
+    s_c[wave] = bc;
+  }
+  __syncthreads();
+  int cstar;
+  {
+    float B0 = s_best[0];
+    int C0 = s_c[0];
+    for (int w = 1; w < 4; ++w) {
+      if (better(s_best[w], s_c[w], B0, C0)) {
+        B0 = s_best[w];
+        C0 = s_c[w];
+      }
+    }
+    // a row without any finite chunk score (non-finite logits) falls back to chunk 0
+    cstar = (C0 >= 0 && C0 * kChunk < V) ? C0 : 0;
+  }
+
+  // 2. the chunk's Wt block, coalesced, and this thread's operand piece; for
+  // thread r < 128 the logit and Gumbel of entry r; the row's log-partition
+  const int v0 = cstar * kChunk;
+  const int nrow = V - v0 < kChunk ? V - v0 : kChunk;
+  const uint16_t* blk = static_cast<const uint16_t*>(a.Wt) + (size_t)v0 * R;
+  uint4 w[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int row = i * RG + grp;
+    w[i] = *reinterpret_cast<const uint4*>(blk + (size_t)(row < nrow ? row : 0) * R + 8 * c);
+  }
+  // both operand loads unconditional (the state's from E's first bytes when
+  // there is no state)
+  uint4 ep = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.E) + (size_t)clamp_id(prev_raw, V) * R + 8 * c);
+  const float4* sp = a.state ? reinterpret_cast<const float4*>(a.state + ((size_t)b * K + (a.k - 1)) * R + 8 * c)
+                             : static_cast<const float4*>(a.E);
+  const float4 sf0 = sp[0], sf1 = sp[1];
+  const int r = tid & (kChunk - 1);
+  const int v = v0 + r;
+  const bool inside = tid < kChunk && r < nrow;
+  const ZT* zrow = static_cast<const ZT*>(a.Z) + ((size_t)b * K + (a.k - 1)) * V;
+  const float z = logit_at<ZT>(zrow, r < nrow ? v : v0);
+  const float gum = gumbel_from_word(draw_word(a.key, (uint32_t)v, (uint32_t)b, (uint32_t)a.k, kDraftElem));
+  {
+    float m = -INFINITY, sm = 0.f;
+    if (tid < a.G) lse2_merge(m, sm, p.x, p.y);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(sm, o);
+      lse2_merge(m, sm, m2, s2);
+    }
+    if (lane == 0) {
+      s_m[wave] = m;
+      s_s[wave] = sm;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (a.state)
+    ep = make_uint4(pack_bf16x2(sf0.x, sf0.y), pack_bf16x2(sf0.z, sf0.w), pack_bf16x2(sf1.x, sf1.y),
+                    pack_bf16x2(sf1.z, sf1.w));
+#pragma unroll
+  for (int i = 0; i < NP; ++i) s_part[(i * RG + grp) * STR + c] = dot_bf16x8(ep, w[i]);
+  __syncthreads();
+  float score = -INFINITY;
+  int idx = 0x7fffffff;
+  if (inside) {
+    float dot = 0.f;
+    if constexpr (STR != PR) {
+      const float4* q = reinterpret_cast<const float4*>(s_part + r * STR);
+#pragma unroll
+      for (int j = 0; j < PR / 4; ++j) {
+        const float4 x = q[j];
+        dot += x.x;
+        dot += x.y;
+        dot += x.z;
+        dot += x.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PR; ++j) dot += s_part[r * STR + j];
+    }
+    const float ell = (z + dot) * a.inv_T;
+    s_ell[r] = ell;
+    score = ell + gum;
+    idx = v;
+  }
+  wave_argmax(score, idx);
+  if (lane == 0) {
+    s_best[wave] = score;
+    s_c[wave] = idx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float B0 = s_best[0];
+    int X = s_c[0];
+    for (int ww = 1; ww < 4; ++ww) {
+      if (better(s_best[ww], s_c[ww], B0, X)) {
+        B0 = s_best[ww];
+        X = s_c[ww];
+      }
+    }
+    float M = s_m[0], S = s_s[0];
+    for (int ww = 1; ww < 4; ++ww) lse2_merge(M, S, s_m[ww], s_s[ww]);
+    const float lse = (M + log2f(S)) * kLn2;
+    const size_t o = (size_t)b * K + (a.k - 1);
+    if (X < v0 || X >= v0 + kChunk || X >= V) X = v0;  // no finite score
+    a.tok[o] = X;
+    a.logq[o] = s_ell[X - v0] - lse;
+    a.lse[o] = lse;
+    s_c[0] = X;
+  }
+  if (a.efrag) {  // the next draft step's B fragments
+    __syncthreads();
+    const int X = s_c[0];
+    if (tid < (R >> 3)) efrag_store_piece(a.efrag, static_cast<const uint16_t*>(a.E), X, b, R, tid);
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- dispatch
@@ -1573,15 +1746,6 @@ hipError_t launch_stream_verify(const dspark_problem& P, const StreamArgs& a, in
 hipError_t launch_select(const dspark_problem& P, const SelectArgs& a, hipStream_t s) {
   const bool zb = P.logits_dtype == DSPARK_BF16, wb = P.weight_dtype == DSPARK_BF16;
 #define DSPARK_SEL(ZT, WT, R) hipLaunchKernelGGL((k_select<ZT, WT, R>), P.B, 256, 0, s, a)
-#define DSPARK_SEL_R(ZT, WT)                  \
-  switch (P.r) {                              \
-    case 16: DSPARK_SEL(ZT, WT, 16); break;   \
-    case 32: DSPARK_SEL(ZT, WT, 32); break;   \
-    case 64: DSPARK_SEL(ZT, WT, 64); break;   \
-    case 128: DSPARK_SEL(ZT, WT, 128); break; \
-    case 256: DSPARK_SEL(ZT, WT, 256); break; \
-    default: return hipErrorInvalidValue;     \
-  }
 #define DSPARK_SEL_R32(ZT)                        \
   switch (P.r) {                                  \
     case 16: DSPARK_SEL(ZT, float, 16); break;    \
@@ -1589,12 +1753,21 @@ hipError_t launch_select(const dspark_problem& P, const SelectArgs& a, hipStream
     case 64: DSPARK_SEL(ZT, float, 64); break;    \
     default: return hipErrorInvalidValue;         \
   }
-  if (zb && wb) { DSPARK_SEL_R(uint16_t, uint16_t) }
+#define DSPARK_SELB(ZT)                                                                 \
+  switch (P.r) {                                                                        \
+    case 16: hipLaunchKernelGGL((k_select_b16<ZT, 16>), P.B, 256, 0, s, a); break;       \
+    case 32: hipLaunchKernelGGL((k_select_b16<ZT, 32>), P.B, 256, 0, s, a); break;       \
+    case 64: hipLaunchKernelGGL((k_select_b16<ZT, 64>), P.B, 256, 0, s, a); break;       \
+    case 128: hipLaunchKernelGGL((k_select_b16<ZT, 128>), P.B, 256, 0, s, a); break;     \
+    case 256: hipLaunchKernelGGL((k_select_b16<ZT, 256>), P.B, 256, 0, s, a); break;     \
+    default: return hipErrorInvalidValue;                                               \
+  }
+  if (zb && wb) { DSPARK_SELB(uint16_t) }
   else if (zb) { DSPARK_SEL_R32(uint16_t) }
-  else if (wb) { DSPARK_SEL_R(float, uint16_t) }
+  else if (wb) { DSPARK_SELB(float) }
   else { DSPARK_SEL_R32(float) }
+#undef DSPARK_SELB
 #undef DSPARK_SEL_R32
-#undef DSPARK_SEL_R
 #undef DSPARK_SEL
   return hipGetLastError();
 }
