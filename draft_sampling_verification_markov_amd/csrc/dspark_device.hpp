@@ -131,28 +131,103 @@ __device__ __forceinline__ float2 halves32(float x) {
 __device__ __forceinline__ float halves32_max(float x) { const float2 h = halves32(x); return fmaxf(h.x, h.y); }
 __device__ __forceinline__ float halves32_sum(float x) { const float2 h = halves32(x); return h.x + h.y; }
 
+// Whole-wave reductions on the VALU cross-lane paths instead of the LDS
+// crossbar (ds_bpermute, which __shfl_xor becomes, costs a round trip through
+// the LDS unit per step): DPP quad permutes pair lanes i and i ^ 1, then i and
+// i ^ 2; once every lane of a quad holds the quad's value, row_half_mirror
+// (i <-> 7 - i) joins the two quads of an octet and row_mirror (i <-> 15 - i)
+// the two octets of a row; v_permlane16_swap and v_permlane32_swap join rows.
+// Each step combines a lane's value with its partner's by a commutative
+// operation (or takes the two swapped values in a fixed order), so every lane
+// ends with the same bitwise result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+// {x of the lane with bit 4 clear, x of the lane with bit 4 set}, from either
+__device__ __forceinline__ float2 rows16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ int2 rows16_i(int x) {
+  const auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  return make_int2((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ int2 halves32_i(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return make_int2((int)r[0], (int)r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  float2 h = rows16(v);
+  v = fmaxf(h.x, h.y);
+  h = halves32(v);
+  return fmaxf(h.x, h.y);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  float2 h = rows16(v);
+  v = h.x + h.y;
+  h = halves32(v);
+  return h.x + h.y;
 }
 
-__device__ __forceinline__ void wave_argmax(float& s, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float so = __shfl_xor(s, o);
-    const int io = __shfl_xor(i, o);
-    if (better(so, io, s, i)) {
-      s = so;
-      i = io;
-    }
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<kDppXor1>(v));
+  v = min(v, dpp_i<kDppXor2>(v));
+  v = min(v, dpp_i<kDppHalfMirror>(v));
+  v = min(v, dpp_i<kDppMirror>(v));
+  int2 h = rows16_i(v);
+  v = min(h.x, h.y);
+  h = halves32_i(v);
+  return min(h.x, h.y);
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_i<kDppXor1>(v);
+  v += dpp_i<kDppXor2>(v);
+  v += dpp_i<kDppHalfMirror>(v);
+  v += dpp_i<kDppMirror>(v);
+  int2 h = rows16_i(v);
+  v = h.x + h.y;
+  h = halves32_i(v);
+  return h.x + h.y;
+}
+
+__device__ __forceinline__ void argmax_step(float& s, int& i, float so, int io) {
+  if (better(so, io, s, i)) {
+    s = so;
+    i = io;
   }
+}
+__device__ __forceinline__ void wave_argmax(float& s, int& i) {
+  argmax_step(s, i, dpp_f<kDppXor1>(s), dpp_i<kDppXor1>(i));
+  argmax_step(s, i, dpp_f<kDppXor2>(s), dpp_i<kDppXor2>(i));
+  argmax_step(s, i, dpp_f<kDppHalfMirror>(s), dpp_i<kDppHalfMirror>(i));
+  argmax_step(s, i, dpp_f<kDppMirror>(s), dpp_i<kDppMirror>(i));
+  float2 hs = rows16(s);
+  int2 hi = rows16_i(i);
+  s = hs.x;
+  i = hi.x;
+  argmax_step(s, i, hs.y, hi.y);
+  hs = halves32(s);
+  hi = halves32_i(i);
+  s = hs.x;
+  i = hi.x;
+  argmax_step(s, i, hs.y, hi.y);
 }
 
 // Combine two (max, sum of 2^(x - max)) pairs in base 2.
@@ -161,6 +236,25 @@ __device__ __forceinline__ void lse2_merge(float& m, float& s, float m2, float s
   if (mn == -INFINITY) return;
   s = s * exp2f(m - mn) + s2 * exp2f(m2 - mn);
   m = mn;
+}
+
+// lse2_merge over the whole wave, on the same cross-lane paths as wave_sum
+// (the merge is symmetric in its two operands up to the order of one addition,
+// which is commutative, so every lane ends with the same result)
+__device__ __forceinline__ void wave_lse2_merge(float& m, float& s) {
+  lse2_merge(m, s, dpp_f<kDppXor1>(m), dpp_f<kDppXor1>(s));
+  lse2_merge(m, s, dpp_f<kDppXor2>(m), dpp_f<kDppXor2>(s));
+  lse2_merge(m, s, dpp_f<kDppHalfMirror>(m), dpp_f<kDppHalfMirror>(s));
+  lse2_merge(m, s, dpp_f<kDppMirror>(m), dpp_f<kDppMirror>(s));
+  float2 hm = rows16(m), hs = rows16(s);
+  m = hm.x;
+  s = hs.x;
+  lse2_merge(m, s, hm.y, hs.y);
+  hm = halves32(m);
+  hs = halves32(s);
+  m = hm.x;
+  s = hs.x;
+  lse2_merge(m, s, hm.y, hs.y);
 }
 
 

@@ -189,8 +189,7 @@ __device__ __forceinline__ void sched_greedy(const SS* sorted_s, const SI* sorte
       }
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o));
+  first = wave_min_i(first);
   if (lane == 0) s_wmin[wave] = first;
   __syncthreads();
   if (tid == 0) {
@@ -322,8 +321,7 @@ __global__ __launch_bounds__(kGreedyThreads) void k_sched_static(const float* su
     n_sched[b] = nb;
     total += nb;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) total += __shfl_xor(total, o);
+  total = wave_sum_i(total);
   if (lane == 0) s_sum[wave] = total;
   __syncthreads();
   if (tid == 0) {

@@ -1403,11 +1403,7 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   {
     float m = -INFINITY, s = 0.f;
     if (tid < a.G) lse2_merge(m, s, p.x, p.y);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-      lse2_merge(m, s, m2, s2);
-    }
+    wave_lse2_merge(m, s);
     if (lane == 0) {
       s_m[wave] = m;
       s_s[wave] = s;
@@ -1415,7 +1411,7 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
   float dot = inside ? half_dot_regs<R>(erow, wrow) : 0.f;
-  dot += __shfl_xor(dot, 1);
+  dot += dpp_f<kDppXor1>(dot);
   float score = -INFINITY;
   int idx = 0x7fffffff;
   if (h == 0 && inside) {
@@ -1558,11 +1554,7 @@ __global__ __launch_bounds__(256) void k_select_b16(SelectArgs a) {
   {
     float m = -INFINITY, sm = 0.f;
     if (tid < a.G) lse2_merge(m, sm, p.x, p.y);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(sm, o);
-      lse2_merge(m, sm, m2, s2);
-    }
+    wave_lse2_merge(m, sm);
     if (lane == 0) {
       s_m[wave] = m;
       s_s[wave] = sm;

@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256) void k_finish(VerifyArgs a) {
           dot = half_dot<WT>(static_cast<const WT*>(a.E), static_cast<const WT*>(a.Wt), prev, v, a.r, h);
         }
       }
-      dot += __shfl_xor(dot, 1);
+      dot += dpp_f<kDppXor1>(dot);
       float sc = -INFINITY;
       int idx = 0x7fffffff;
       if (h == 0 && inside) {
