@@ -96,6 +96,19 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_floa
 // wave, prefetches meant to stay in flight included.  The memory clobber keeps
 // the compiler from moving memory accesses across it.
 __device__ __forceinline__ void barrier_lds_only() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// waits until every vector-memory operation of this wave has completed
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order), lgkm and export counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+// 128-bit buffer descriptor over [base, base + bytes) (raw; reads past the end return 0)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 // float -> bfloat16 bits, round to nearest, ties to even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);

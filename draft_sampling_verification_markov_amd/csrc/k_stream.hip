@@ -417,16 +417,6 @@ __device__ __forceinline__ void chunk_range(int g, int G, int nchunks, int& c_be
 }
 
 
-// waits until every vector-memory operation of this wave has completed
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// wait until at most N vector-memory operations of this wave are outstanding
-// (they complete in issue order), lgkm and export counters untouched
-template <int N>
-__device__ __forceinline__ void wait_vmem_n() {
-  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
 // Tiles of the draft step (bf16 logits): per stage a logits tile (256 requests
 // x 64 entries, 128-byte rows, 16-byte slots XOR-swizzled by the row) and a Wt
 // tile (64 vocabulary rows x r) whose rows are padded to 2r + 16 bytes and
@@ -514,12 +504,6 @@ struct DraftDma {
   }
 };
 
-
-
-// 128-bit buffer descriptor over [base, base + bytes) (raw; reads past the end return 0)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 
 // 16 consecutive logits of one request from a tile row (two or four 16-byte slots)
