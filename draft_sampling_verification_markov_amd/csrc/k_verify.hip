@@ -9,6 +9,8 @@
 // scheduled positions pass, draw a bonus token from the next target row.
 //
 //   k_rowlist  one workgroup: compact list of the rows (b, k <= n_b) to test
+//              (batches up to 1,024 requests and 8,192 candidates: every k_vlse
+//              workgroup builds it in LDS instead)
 //   k_vlse     (row, 8192-entry segment) items: base-2 (max, sum) of target/T_s
 //   k_accept   one wave per request: log-partition of each tested row,
 //              log p_k(x_k), the accept draw, the first rejection
@@ -98,32 +100,79 @@ struct VlseItem {
   }
 };
 
-template <typename ZT>
-__device__ __forceinline__ const ZT* vlse_row(const VerifyArgs& a, int w, int& b, int& k0, int& seg) {
+// Row code of item w: from the list in LDS (LOCAL) or the one k_rowlist wrote.
+template <typename ZT, bool LOCAL>
+__device__ __forceinline__ const ZT* vlse_row(const VerifyArgs& a, const int* s_rows, int w, int& b, int& k0,
+                                              int& seg) {
   const int j = w / a.nseg;
   seg = w - j * a.nseg;
-  const int code = a.rows[j];
+  const int code = LOCAL ? s_rows[j] : a.rows[j];
   b = code >> 6;
   k0 = code & 63;
   return static_cast<const ZT*>(a.Zt) + ((size_t)b * (a.K + 1) + k0) * a.V;
 }
 
+// With LOCAL (B <= kVlseListB, B*K <= kVlseListMax) every workgroup builds the
+// compact list of the rows to test in LDS from n_sched (request b's positions
+// 1..n_b, requests in order: the list k_rowlist writes), so no separate launch
+// precedes this pass.
+constexpr int kVlseListMax = 8192;
+constexpr int kVlseListB = 1024;
+
 // (row, segment) items, round-robin over the workgroups; the loads of the next
 // item are in flight while the current one is reduced (the workgroup joins its
 // waves with LDS-only barriers, which leave those loads in flight).
-template <typename ZT>
+template <typename ZT, bool LOCAL>
 __global__ __launch_bounds__(256) void k_vlse(VerifyArgs a) {
   using Vec = Vec16<ZT>;
   using It = VlseItem<ZT>;
   constexpr int kPer = kVlseSeg / 256;  // entries per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float s_m[4], s_s[4];
-  const int M = *a.nrows;
+  __shared__ int s_rows[LOCAL ? kVlseListMax : 1];
+  __shared__ int s_wsum[4];
+  int M;
+  if (LOCAL) {
+    // n_b of requests tid, tid + 256, ... (at most four per thread), then one
+    // scan per 256 requests: wave inclusive scans, the waves' totals in LDS
+    const int B = a.B, K = a.K;
+    int nbv[kVlseListB / 256];
+#pragma unroll
+    for (int q = 0; q < kVlseListB / 256; ++q) {
+      const int b = tid + 256 * q;
+      const int v = a.n_sched[b < B ? b : 0];
+      nbv[q] = b < B ? (v < 0 ? 0 : (v > K ? K : v)) : 0;
+    }
+    int base = 0;
+#pragma unroll
+    for (int q = 0; q < kVlseListB / 256; ++q) {
+      if (256 * q >= B) break;
+      const int nb = nbv[q];
+      int incl = nb;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      if (lane == 63) s_wsum[wave] = incl;
+      __syncthreads();
+      int off = base;
+      for (int w2 = 0; w2 < wave; ++w2) off += s_wsum[w2];
+      off += incl - nb;
+      const int b = tid + 256 * q;
+      for (int j = 0; j < nb; ++j) s_rows[off + j] = b * 64 + j;
+      base += s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+      __syncthreads();
+    }
+    M = base;
+  } else {
+    M = *a.nrows;
+  }
   const int items = M * a.nseg;
   int w = blockIdx.x;
   if (w >= items) return;
   int b, k0, seg;
-  const ZT* row = vlse_row<ZT>(a, w, b, k0, seg);
+  const ZT* row = vlse_row<ZT, LOCAL>(a, s_rows, w, b, k0, seg);
   It cur;
   cur.load(row, seg * kVlseSeg, a.V, tid);
   for (; w < items; w += gridDim.x) {
@@ -131,7 +180,7 @@ __global__ __launch_bounds__(256) void k_vlse(VerifyArgs a) {
     int bn = 0, kn = 0, segn = 0;
     It nxt;
     if (wn < items) {
-      const ZT* rown = vlse_row<ZT>(a, wn, bn, kn, segn);
+      const ZT* rown = vlse_row<ZT, LOCAL>(a, s_rows, wn, bn, kn, segn);
       nxt.load(rown, segn * kVlseSeg, a.V, tid);
     }
     // VALU-bound (one transcendental per entry): the max is taken on the raw
@@ -418,12 +467,18 @@ __global__ __launch_bounds__(256) void k_finish(VerifyArgs a) {
 }  // namespace
 
 hipError_t launch_verify_pre(const dspark_problem& P, const VerifyArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_rowlist, 1, kListThreads, 0, s, a.n_sched, P.B, P.K, a.rows, a.nrows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const bool local = P.B <= kVlseListB && (long long)P.B * P.K <= kVlseListMax;
+  hipError_t e;
+  if (!local) {
+    hipLaunchKernelGGL(k_rowlist, 1, kListThreads, 0, s, a.n_sched, P.B, P.K, a.rows, a.nrows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const bool zb = P.logits_dtype == DSPARK_BF16;
-  if (zb) hipLaunchKernelGGL(k_vlse<uint16_t>, kVlseGrid, 256, 0, s, a);
-  else hipLaunchKernelGGL(k_vlse<float>, kVlseGrid, 256, 0, s, a);
+  if (zb && local) hipLaunchKernelGGL((k_vlse<uint16_t, true>), kVlseGrid, 256, 0, s, a);
+  else if (zb) hipLaunchKernelGGL((k_vlse<uint16_t, false>), kVlseGrid, 256, 0, s, a);
+  else if (local) hipLaunchKernelGGL((k_vlse<float, true>), kVlseGrid, 256, 0, s, a);
+  else hipLaunchKernelGGL((k_vlse<float, false>), kVlseGrid, 256, 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (zb) hipLaunchKernelGGL(k_accept<uint16_t>, P.B, 64, 0, s, a);
