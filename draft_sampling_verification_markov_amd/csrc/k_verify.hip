@@ -464,6 +464,184 @@ __global__ __launch_bounds__(256) void k_finish(VerifyArgs a) {
   }
 }
 
+// Finishing kernel for bf16 logits and factors with the fragment-ordered
+// operands of the resample pass: the same draw as k_finish with the loads laid
+// out as in the selection kernel.  The first rejection, the schedule and this
+// thread's 16-byte piece of the residual's Markov operand (which k_accept
+// stored in B-fragment order: E[x_{k*-1}], the RNN state, or zeros for a bonus
+// row) are requested with the partials; the winning chunk's 128 Wt rows are
+// one contiguous block read with consecutive threads on consecutive pieces,
+// and the partial dot products are summed through LDS (entry r by thread r).
+template <int R>
+__global__ __launch_bounds__(256) void k_finish_b16(VerifyArgs a) {
+  constexpr int PR = R / 8, NP = PR / 2, RG = 256 / PR;
+  constexpr int STR = PR % 4 == 0 ? PR + 4 : PR;
+  static_assert(NP * RG == kChunk, "one chunk of rows over the workgroup");
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, V = a.V;
+  __shared__ float s_f[4], s_best[4];
+  __shared__ int s_idx[4];
+  __shared__ __attribute__((aligned(16))) float s_part[kChunk * STR];
+  const int c = tid % PR, grp = tid / PR;
+
+  const int kstar = a.job[b];
+  int nb = a.n_sched[b];
+  nb = nb < 0 ? 0 : (nb > K ? K : nb);
+  float4 p = a.part[(size_t)b * a.G + (tid < a.G ? tid : 0)];
+  if (tid >= a.G) p = make_float4(0.f, 0.f, -INFINITY, 0.f);
+  const uint4 ep = a.efrag[((size_t)(b >> 5) * (R >> 4) + (c >> 1)) * 64 + (b & 31) + 32 * (c & 1)];
+
+  // merge the partials of the resample pass: residual mass, winning chunk
+  float mass = wave_sum(p.x), best = p.z;
+  int bc = __float_as_int(p.w);
+  if (tid >= a.G) bc = 0x7fffffff;
+  wave_argmax(best, bc);
+  if (lane == 0) {
+    s_f[wave] = mass;
+    s_best[wave] = best;
+    s_idx[wave] = bc;
+  }
+  __syncthreads();
+  float Bm = s_best[0];
+  int C0 = s_idx[0];
+  for (int w = 1; w < 4; ++w)
+    if (better(s_best[w], s_idx[w], Bm, C0)) {
+      Bm = s_best[w];
+      C0 = s_idx[w];
+    }
+  const float tot_mass = (s_f[0] + s_f[1]) + (s_f[2] + s_f[3]);
+  const int cstar = (Bm == -INFINITY || C0 < 0 || C0 * kChunk >= V) ? -1 : C0;
+  __syncthreads();  // s_best / s_idx are reused below (and by full_row_draw)
+  const uint16_t* Zt = static_cast<const uint16_t*>(a.Zt);
+  const int r = tid & (kChunk - 1);
+  const int v0 = cstar >= 0 ? cstar * kChunk : 0;
+  const int v = v0 + r;
+  const bool inside = cstar >= 0 && tid < kChunk && v < V;
+
+  int y = -1;
+  __shared__ int s_y;
+  if (kstar > 0) {
+    const int k0 = kstar - 1;
+    const uint16_t* trow = Zt + ((size_t)b * (K + 1) + k0) * V;
+    if (tot_mass > 0.f && cstar >= 0) {
+      const int nrow = V - v0 < kChunk ? V - v0 : kChunk;
+      const uint16_t* blk = static_cast<const uint16_t*>(a.Wt) + (size_t)v0 * R;
+      uint4 w[NP];
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int row = i * RG + grp;
+        w[i] = *reinterpret_cast<const uint4*>(blk + (size_t)(row < nrow ? row : 0) * R + 8 * c);
+      }
+      const uint16_t* zrow = static_cast<const uint16_t*>(a.Z) + ((size_t)b * K + k0) * V;
+      const float z = bf16_to_f32(zrow[r < nrow ? v : v0]);
+      const float zt = bf16_to_f32(trow[r < nrow ? v : v0]);
+      const float lq = a.lse_q[(size_t)b * K + k0], lp = a.lse_p[(size_t)b * K + k0];
+      const float gum = gumbel_from_word(draw_word(a.key, (uint32_t)v, (uint32_t)b, (uint32_t)kstar, kResidElem));
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        float acc = 0.f;
+        const uint4 e = ep, x = w[i];
+        acc = fmaf(bf16_lo(e.x), bf16_lo(x.x), acc);
+        acc = fmaf(bf16_hi(e.x), bf16_hi(x.x), acc);
+        acc = fmaf(bf16_lo(e.y), bf16_lo(x.y), acc);
+        acc = fmaf(bf16_hi(e.y), bf16_hi(x.y), acc);
+        acc = fmaf(bf16_lo(e.z), bf16_lo(x.z), acc);
+        acc = fmaf(bf16_hi(e.z), bf16_hi(x.z), acc);
+        acc = fmaf(bf16_lo(e.w), bf16_lo(x.w), acc);
+        acc = fmaf(bf16_hi(e.w), bf16_hi(x.w), acc);
+        s_part[(i * RG + grp) * STR + c] = acc;
+      }
+      __syncthreads();
+      float sc = -INFINITY;
+      int idx = 0x7fffffff;
+      if (inside) {
+        float dot = 0.f;
+        if constexpr (STR != PR) {
+          const float4* q = reinterpret_cast<const float4*>(s_part + r * STR);
+#pragma unroll
+          for (int j = 0; j < PR / 4; ++j) {
+            const float4 xx = q[j];
+            dot += xx.x;
+            dot += xx.y;
+            dot += xx.z;
+            dot += xx.w;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < PR; ++j) dot += s_part[r * STR + j];
+        }
+        const float q = expf((z + dot) * a.inv_T - lq);
+        const float pp = expf(zt * a.inv_T - lp);
+        const float rr = fmaxf(pp - q, 0.f);
+        if (rr > 0.f) {
+          sc = logf(rr) + gum;
+          idx = v;
+        }
+      }
+      wave_argmax(sc, idx);
+      if (lane == 0) {
+        s_best[wave] = sc;
+        s_idx[wave] = idx;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        float B1 = s_best[0];
+        int X = s_idx[0];
+        for (int ww = 1; ww < 4; ++ww)
+          if (better(s_best[ww], s_idx[ww], B1, X)) {
+            B1 = s_best[ww];
+            X = s_idx[ww];
+          }
+        s_y = (B1 == -INFINITY) ? -1 : X;
+      }
+      __syncthreads();
+      y = s_y;
+    }
+    if (y < 0) y = full_row_draw<uint16_t>(trow, V, a.inv_T, a.key, b, kstar, kResidChunk, kResidElem, s_best, s_idx);
+  } else {
+    const uint16_t* trow = Zt + ((size_t)b * (K + 1) + nb) * V;
+    float sc = -INFINITY;
+    int idx = 0x7fffffff;
+    if (inside) {
+      sc = bf16_to_f32(trow[v]) * a.inv_T +
+           gumbel_from_word(draw_word(a.key, (uint32_t)v, (uint32_t)b, (uint32_t)(nb + 1), kBonusElem));
+      idx = v;
+    }
+    wave_argmax(sc, idx);
+    if (lane == 0) {
+      s_best[wave] = sc;
+      s_idx[wave] = idx;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float B1 = s_best[0];
+      int X = s_idx[0];
+      for (int ww = 1; ww < 4; ++ww)
+        if (better(s_best[ww], s_idx[ww], B1, X)) {
+          B1 = s_best[ww];
+          X = s_idx[ww];
+        }
+      s_y = (B1 == -INFINITY) ? -1 : X;
+    }
+    __syncthreads();
+    y = s_y;
+    if (y < 0) y = full_row_draw<uint16_t>(trow, V, a.inv_T, a.key, b, nb + 1, kBonusChunk, kBonusElem, s_best, s_idx);
+  }
+
+  const int acc = kstar > 0 ? kstar - 1 : nb;
+  for (int j = tid; j <= K; j += 256) {
+    int t = -1;
+    if (j < acc) t = a.tok[(size_t)b * K + j];
+    else if (j == acc) t = y;
+    a.out_tok[(size_t)b * (K + 1) + j] = t;
+  }
+  if (tid == 0) {
+    a.n_acc[b] = acc;
+    a.next_anchor[b] = y;
+    a.resid_mass[b] = kstar > 0 ? tot_mass : __int_as_float(0x7fc00000);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_verify_pre(const dspark_problem& P, const VerifyArgs& a, hipStream_t s) {
@@ -488,7 +666,17 @@ hipError_t launch_verify_pre(const dspark_problem& P, const VerifyArgs& a, hipSt
 
 hipError_t launch_verify_finish(const dspark_problem& P, const VerifyArgs& a, hipStream_t s) {
   const bool zb = P.logits_dtype == DSPARK_BF16, wb = P.weight_dtype == DSPARK_BF16;
-  if (zb && wb) hipLaunchKernelGGL((k_finish<uint16_t, uint16_t>), P.B, 256, 0, s, a);
+  if (zb && wb && a.efrag) {
+    switch (P.r) {
+      case 16: hipLaunchKernelGGL(k_finish_b16<16>, P.B, 256, 0, s, a); break;
+      case 32: hipLaunchKernelGGL(k_finish_b16<32>, P.B, 256, 0, s, a); break;
+      case 64: hipLaunchKernelGGL(k_finish_b16<64>, P.B, 256, 0, s, a); break;
+      case 128: hipLaunchKernelGGL(k_finish_b16<128>, P.B, 256, 0, s, a); break;
+      case 256: hipLaunchKernelGGL(k_finish_b16<256>, P.B, 256, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  else if (zb && wb) hipLaunchKernelGGL((k_finish<uint16_t, uint16_t>), P.B, 256, 0, s, a);
   else if (zb) hipLaunchKernelGGL((k_finish<uint16_t, float>), P.B, 256, 0, s, a);
   else if (wb) hipLaunchKernelGGL((k_finish<float, uint16_t>), P.B, 256, 0, s, a);
   else hipLaunchKernelGGL((k_finish<float, float>), P.B, 256, 0, s, a);
