@@ -225,16 +225,28 @@ __global__ __launch_bounds__(64) void k_accept(VerifyArgs a) {
   const int b = blockIdx.x, k0 = threadIdx.x;
   const int K = a.K;
   int nb = a.n_sched[b];
+  const int anc = a.anchor[b];
   nb = nb < 0 ? 0 : (nb > K ? K : nb);
   const bool tested = k0 < nb;
   float logp = __int_as_float(0x7fc00000);  // NaN where not verified
   bool rej = false;
+  int x = 0;  // draft token of position k0 + 1 (tested positions)
   if (tested) {
     float m = -INFINITY, s = 0.f;
     const float2* part = a.vlse + ((size_t)b * K + k0) * a.nseg;
-    for (int i = 0; i < a.nseg; ++i) lse2_merge(m, s, part[i].x, part[i].y);
+    // the segment partials in batches of loads issued together (one round trip
+    // per batch: 152K entries are 19 segments), merged in segment order
+    constexpr int kBatch = 20;
+    for (int i0 = 0; i0 < a.nseg; i0 += kBatch) {
+      float2 pv[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) pv[u] = part[i0 + u < a.nseg ? i0 + u : 0];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (i0 + u < a.nseg) lse2_merge(m, s, pv[u].x, pv[u].y);
+    }
     const float lse_p = (m + log2f(s)) * kLn2;
-    const int x = clamp_id(a.tok[(size_t)b * K + k0], a.V);
+    x = clamp_id(a.tok[(size_t)b * K + k0], a.V);
     const ZT* row = static_cast<const ZT*>(a.Zt) + ((size_t)b * (K + 1) + k0) * a.V;
     logp = logit_at<ZT>(row, x) * a.inv_T - lse_p;
     a.lse_p[(size_t)b * K + k0] = lse_p;
@@ -246,12 +258,13 @@ __global__ __launch_bounds__(64) void k_accept(VerifyArgs a) {
   const unsigned long long mask = __ballot(rej);
   const int ks = mask ? __ffsll((long long)mask) : 0;
   if (k0 == 0) a.job[b] = ks;
+  // x_{k*-1}: the anchor, or the token lane k* - 2 holds (k* <= n_b, so it was tested)
+  const int prev = ks > 0 ? (ks == 1 ? clamp_id(anc, a.V) : __builtin_amdgcn_readlane(x, ks - 2)) : -1;
   if (a.efrag && k0 < (a.r >> 3)) {
     // B fragments of the resample pass: E[x_{k*-1}] for a rejection at k*, zeros for a bonus row
     if (a.state) {  // RNN head: the state of position k*
       efrag_store_piece_f32(a.efrag, ks > 0 ? a.state + ((size_t)b * K + ks - 1) * a.r : nullptr, b, a.r, k0);
     } else {
-      const int prev = ks > 0 ? clamp_id(ks == 1 ? a.anchor[b] : a.tok[(size_t)b * K + ks - 2], a.V) : -1;
       efrag_store_piece(a.efrag, static_cast<const uint16_t*>(a.E), prev, b, a.r, k0);
     }
   }
