@@ -1209,8 +1209,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify_stream(StreamArgs a) {
       const int ks = a.job[bb];
       int nb = a.n_sched[bb];
       nb = nb < 0 ? 0 : (nb > K ? K : nb);
-      // a bonus row has no draft term (B fragments 0, q = 0): any valid draft-logit row will do
-      s_zrow[row] = (uint32_t)(((size_t)rr * K + (ks > 0 ? ks - 1 : 0)) * V * 2);
+      // a bonus row has no draft term (B fragments 0, q = 0, its epilogue reads only the
+      // target tile): its draft-logit slots read past the buffer, zeros without memory traffic
+      s_zrow[row] = ks > 0 ? (uint32_t)(((size_t)rr * K + (ks - 1)) * V * 2) : VerifyDma<R>::kOutOfRange;
       s_trow[row] = (uint32_t)(((size_t)rr * (K + 1) + (ks > 0 ? ks - 1 : nb)) * V * 2);
     }
     barrier_lds_only();
