@@ -83,6 +83,9 @@ EDGE = [
     # K = 32: the resample pass exceeds the buffer-offset range of its DMA kernel at the full vocabulary,
     # here a small vocabulary keeps it on that kernel while the draft spans 32 positions
     synth.get_config("tbias_bf16").replace(name="edge_k32", B=20, K=32, V=1032, r=64, d=32, seed=13),
+    # bf16 everything at rank 16 (two 16-byte pieces per factor row): the selection and finishing kernels'
+    # smallest piece layout, ragged batch and last chunk
+    synth.get_config("tbias_bf16").replace(name="edge_r16_bf16", B=9, K=3, V=1000, r=16, d=32, seed=14),
     # identical draft and target: every scheduled position is accepted
     synth.get_config("tbias").replace(name="edge_p_eq_q", B=3, K=4, V=640, r=16, d=16, target_noise=0.0,
                                       ew_std=0.0, ttable=("linear", 1.0, 0.0), seed=11),
