@@ -902,21 +902,24 @@ __device__ __forceinline__ void draft_step(const StreamArgs& a, unsigned char* b
     // when all but the second unit have landed; the first chunk Gumbels are
     // drawn in the meantime.  (FIRST: the anchor is loaded ahead of the first
     // stage, so waiting for it leaves that stage in flight.)
-    int anc = 0;
-    if (FIRST) anc = a.anchor[rv ? b : B - 1];
-    __builtin_amdgcn_sched_barrier(0);
-    dma.stage(buf0, zr, wr, vb, wave);
-    __builtin_amdgcn_sched_barrier(0);
     bf16x8_t bfrag[T::kSteps];
     if (FIRST) {
+      const int anc = a.anchor[rv ? b : B - 1];
+      __builtin_amdgcn_sched_barrier(0);
+      dma.stage(buf0, zr, wr, vb, wave);
+      __builtin_amdgcn_sched_barrier(0);
       const bf16x8_t* src =
           reinterpret_cast<const bf16x8_t*>(static_cast<const uint16_t*>(a.E) + (size_t)clamp_id(anc, V) * R + 8 * h);
 #pragma unroll
       for (int t = 0; t < T::kSteps; ++t) bfrag[t] = src[2 * t];
     } else {
+      // the fragments (L2-resident, written by the selection) ahead of the first
+      // stage's DMA, so that they do not queue behind 64 KB of HBM requests
       const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(a.efrag) + (size_t)((base >> 5) + wave) * T::kSteps * 64 + lane;
 #pragma unroll
       for (int t = 0; t < T::kSteps; ++t) bfrag[t] = src[t * 64];  // rows past B: unwritten slots, own column only
+      __builtin_amdgcn_sched_barrier(0);
+      dma.stage(buf0, zr, wr, vb, wave);
     }
     __builtin_amdgcn_sched_barrier(0);
     dma.stage(buf1, zr, wr, vb + T::kUnit, wave);  // every workgroup has at least one chunk (two units)
