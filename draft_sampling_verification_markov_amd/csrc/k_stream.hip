@@ -1474,7 +1474,7 @@ __global__ __launch_bounds__(256) void k_select_b16(SelectArgs a) {
   const int K = a.K, V = a.V;
   __shared__ float s_m[4], s_s[4], s_best[4], s_ell[kChunk];
   __shared__ __attribute__((aligned(16))) float s_part[kChunk * STR];
-  __shared__ int s_c[4];
+  __shared__ int s_c[4], s_x;
   const int c = tid % PR, grp = tid / PR;
 
   // the previous token and the partials (G <= 256: at most one per thread);
@@ -1579,6 +1579,12 @@ __global__ __launch_bounds__(256) void k_select_b16(SelectArgs a) {
     idx = v;
   }
   wave_argmax(score, idx);
+  // the E row of this wave's best entry, requested before the waves' results
+  // meet: the winner's row (the next draft step's B operand) is then already in
+  // the winning wave's registers when the token is known
+  const uint16_t* E16 = static_cast<const uint16_t*>(a.E);
+  const int cand = (idx >= v0 && idx < V) ? idx : v0;
+  const uint4 erow_pre = *reinterpret_cast<const uint4*>(E16 + (size_t)cand * R + 8 * (lane < (R >> 3) ? lane : 0));
   if (lane == 0) {
     s_best[wave] = score;
     s_c[wave] = idx;
@@ -1601,12 +1607,20 @@ __global__ __launch_bounds__(256) void k_select_b16(SelectArgs a) {
     a.tok[o] = X;
     a.logq[o] = s_ell[X - v0] - lse;
     a.lse[o] = lse;
-    s_c[0] = X;
+    s_x = X;
   }
   if (a.efrag) {  // the next draft step's B fragments
     __syncthreads();
-    const int X = s_c[0];
-    if (tid < (R >> 3)) efrag_store_piece(a.efrag, static_cast<const uint16_t*>(a.E), X, b, R, tid);
+    const int X = s_x;
+    // the wave whose candidate won stores the row it holds; if none did (no
+    // finite score), wave 0 loads the row of the fallback token
+    int owner = -1;
+    for (int ww = 0; ww < 4; ++ww)
+      if (owner < 0 && s_c[ww] == X) owner = ww;
+    if (wave == (owner < 0 ? 0 : owner) && lane < (R >> 3)) {
+      const uint4 v = owner < 0 ? *reinterpret_cast<const uint4*>(E16 + (size_t)X * R + 8 * lane) : erow_pre;
+      a.efrag[((size_t)(b >> 5) * (R >> 4) + (lane >> 1)) * 64 + (b & 31) + 32 * (lane & 1)] = v;
+    }
   }
 }
 
