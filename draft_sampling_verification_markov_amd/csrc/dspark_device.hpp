@@ -220,6 +220,27 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return h.x + h.y;
 }
 
+// Inclusive prefix sum over the wave in fp64 on the same VALU paths: DPP
+// row_shr 1, 2, 4, 8 (bound_ctrl: a lane with no source in its row of 16 adds
+// zero) scan each row, row_bcast:15 adds row 0's (row 2's) total to row 1
+// (row 3), row_bcast:31 adds the first half's total to the second.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_d(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROWMASK, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROWMASK, 0xF, true);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+__device__ __forceinline__ double wave_scan_incl(double v) {
+  v += dpp_d<0x111, 0xF>(v);
+  v += dpp_d<0x112, 0xF>(v);
+  v += dpp_d<0x114, 0xF>(v);
+  v += dpp_d<0x118, 0xF>(v);
+  v += dpp_d<0x142, 0xA>(v);
+  v += dpp_d<0x143, 0xC>(v);
+  return v;
+}
+
 __device__ __forceinline__ void argmax_step(float& s, int& i, float so, int io) {
   if (better(so, io, s, i)) {
     s = so;

@@ -137,17 +137,34 @@ __global__ __launch_bounds__(256) void k_sched_rank(const float* surv, int n, in
 // Greedy pass over candidates in schedule order (sorted_s / sorted_i, any
 // address space): fp64 prefix sums over per-thread segments, the first
 // refusal of (A + s) * T[N] >= A * T[N + 1], the total and per-request counts.
-template <int THREADS, typename SS, typename SI>
-__device__ __forceinline__ void sched_greedy(const SS* sorted_s, const SI* sorted_i, const float* T, int B, int K,
-                                             int32_t* n_sched, int32_t* n_total, double* s_wsum, int* s_wmin,
-                                             int* s_stop) {
+// The step-time entries of the first batch of a thread's segment, loaded at the
+// start of the kernel (their round trip overlaps the ordering).
+constexpr int kGreedyBatch = 8;
+struct GreedyT {
+  float tv[kGreedyBatch + 1];
+  template <int THREADS>
+  __device__ __forceinline__ void load(const float* T, int B, int K) {
+    const int n = B * K;
+    const int lo = (int)(((long long)threadIdx.x * n) / THREADS);
+#pragma unroll
+    for (int j = 0; j <= kGreedyBatch; ++j) tv[j] = T[B + min(lo + j, n)];  // T has B + n + 1 entries
+  }
+};
+
+// LDS_COUNT: per-request counts in LDS (s_cnt, B entries, zeroed by the caller
+// before an earlier barrier) stored to n_sched at the end, instead of global
+// atomics on n_sched.
+template <int THREADS, bool LDS_COUNT, typename SS, typename SI>
+__device__ __forceinline__ void sched_greedy(const SS* sorted_s, const SI* sorted_i, const float* T, const GreedyT& t0,
+                                             int B, int K, int32_t* n_sched, int32_t* n_total, double* s_wsum,
+                                             int* s_wmin, int* s_stop, int* s_cnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = B * K;
   const int lo = (int)(((long long)tid * n) / THREADS);
   const int hi = (int)(((long long)(tid + 1) * n) / THREADS);
   // segments are read in register batches of kBatch (clamped, unconditional
   // loads), so a batch costs one memory round trip instead of one per element
-  constexpr int kBatch = 8;
+  constexpr int kBatch = kGreedyBatch;
   double local = 0.0;
   for (int m0 = lo; m0 < hi; m0 += kBatch) {
     float sv[kBatch];
@@ -157,12 +174,7 @@ __device__ __forceinline__ void sched_greedy(const SS* sorted_s, const SI* sorte
     for (int j = 0; j < kBatch; ++j)
       if (m0 + j < hi) local += (double)sv[j];
   }
-  double incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const double incl = wave_scan_incl(local);
   if (lane == 63) s_wsum[wave] = incl;
   __syncthreads();
   double wbase = 0.0;
@@ -174,8 +186,13 @@ __device__ __forceinline__ void sched_greedy(const SS* sorted_s, const SI* sorte
     float sv[kBatch], tv[kBatch + 1];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) sv[j] = (float)sorted_s[min(m0 + j, n - 1)];
+    if (m0 == lo) {
 #pragma unroll
-    for (int j = 0; j <= kBatch; ++j) tv[j] = T[B + min(m0 + j, n)];  // T has B + n + 1 entries
+      for (int j = 0; j <= kBatch; ++j) tv[j] = t0.tv[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j <= kBatch; ++j) tv[j] = T[B + min(m0 + j, n)];  // T has B + n + 1 entries
+    }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (open && m0 + j < hi) {
@@ -206,7 +223,12 @@ __device__ __forceinline__ void sched_greedy(const SS* sorted_s, const SI* sorte
   for (int m = tid; m < stop; m += THREADS) {
     int idx = (int)sorted_i[m];
     idx = idx < 0 ? 0 : (idx >= n ? n - 1 : idx);
-    atomicAdd(&n_sched[idx / K], 1);
+    if (LDS_COUNT) atomicAdd(&s_cnt[idx / K], 1);
+    else atomicAdd(&n_sched[idx / K], 1);
+  }
+  if (LDS_COUNT) {
+    __syncthreads();
+    for (int b = tid; b < B; b += THREADS) n_sched[b] = s_cnt[b];
   }
 }
 
@@ -239,9 +261,12 @@ __global__ __launch_bounds__(kGreedyThreads) void k_sched_greedy_global(const fl
   __shared__ double s_wsum[kGreedyThreads / 64];
   __shared__ int s_wmin[kGreedyThreads / 64];
   __shared__ int s_stop;
+  GreedyT t0;
+  t0.load<kGreedyThreads>(T, B, K);
   for (int b = threadIdx.x; b < B; b += kGreedyThreads) n_sched[b] = 0;
   __syncthreads();
-  sched_greedy<kGreedyThreads>(sorted_s, sorted_i, T, B, K, n_sched, n_total, s_wsum, s_wmin, &s_stop);
+  sched_greedy<kGreedyThreads, false>(sorted_s, sorted_i, T, t0, B, K, n_sched, n_total, s_wsum, s_wmin, &s_stop,
+                                      nullptr);
 }
 
 // Candidate sets up to kSchedLdsMax: each candidate's rank is summed from the
@@ -253,11 +278,14 @@ __global__ __launch_bounds__(kGreedyThreads) void k_sched_greedy_lds(const float
                                                                    int32_t* n_total) {
   __shared__ float s_sorted_s[kSchedLdsMax];
   __shared__ int32_t s_sorted_i[kSchedLdsMax];
+  __shared__ int s_cnt[kSchedLdsMax];
   __shared__ double s_wsum[kGreedyThreads / 64];
   __shared__ int s_wmin[kGreedyThreads / 64];
   __shared__ int s_stop;
   const int n = B * K;
-  for (int b = threadIdx.x; b < B; b += kGreedyThreads) n_sched[b] = 0;
+  GreedyT t0;
+  t0.load<kGreedyThreads>(T, B, K);
+  for (int b = threadIdx.x; b < B; b += kGreedyThreads) s_cnt[b] = 0;
   // kBatchC candidates per thread at a time, all their loads in flight before the
   // first sum: kSchedSegMax segments each, unconditional (clamped) and masked after
   constexpr int kBatchC = 4;
@@ -285,7 +313,8 @@ __global__ __launch_bounds__(kGreedyThreads) void k_sched_greedy_lds(const float
     }
   }
   __syncthreads();
-  sched_greedy<kGreedyThreads>(s_sorted_s, s_sorted_i, T, B, K, n_sched, n_total, s_wsum, s_wmin, &s_stop);
+  sched_greedy<kGreedyThreads, true>(s_sorted_s, s_sorted_i, T, t0, B, K, n_sched, n_total, s_wsum, s_wmin, &s_stop,
+                                     s_cnt);
 }
 
 // Asynchronous budget: the first M = lag_total - B candidates of the current
