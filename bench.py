@@ -139,7 +139,7 @@ def step_kernels(cfg) -> dict:
         {"k_sched_rank": 1, "k_sched_scatter": 1, "k_sched_greedy_global": 1}
     rowlist = {} if (cfg.B <= 1024 and n <= 8192) else {"k_rowlist": 1}  # else built inside k_vlse
     return {"k_draft_first": 1, DOMINANT: cfg.K - 1, "k_select_b16": cfg.K, "k_conf": 1, **sched, **rowlist,
-            "k_vlse": 1, "k_accept": 1, "k_verify_stream": 1, "k_finish_b16": 1}
+            "k_vlse": 1, "k_accept": 1, "k_verify64": 1, "k_finish_b16": 1}
 
 
 def step_traffic_from_profile(cfg):

@@ -1029,166 +1029,74 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft_first(StreamArgs a) {
 // log-partition) and its chunk Gumbel score; per (row, workgroup) the mass and
 // the best chunk, which the finishing kernel merges.
 //
-// Same machinery as the draft kernel, 32-entry units: per stage a draft-logit
-// tile, a target tile (256 requests x 64 bytes, 16-byte slots swizzled by
-// (row >> 2) & 3 so that 16 consecutive rows hit 16 distinct bank groups) and
-// a Wt tile of 32 rows in MFMA row order; a three-stage ring of distinct LDS
-// objects, two units in flight.  The B fragments come from the fragment-ordered
-// region that the acceptance kernel fills (zeros for bonus rows, whose q is 0).
-template <int R>
-struct VerifyTiles {
-  static constexpr int kUnit = 32;
-  static constexpr int kZRow = 64, kZSlots = 4;
-  static constexpr int kZBytes = kRowsPerPass * kZRow;  // 16 KB
-  static constexpr int kTOff = kZBytes;                 // target tile
-  static constexpr int kWOff = 2 * kZBytes;             // Wt tile
-  static constexpr int kWRow = R * 2;
-  static constexpr int kWStride = kWRow + 16;
-  static constexpr int kWSlots = R / 8;
-  static constexpr int kWBlocks = (kUnit * kWStride + 1023) / 1024;
-  static constexpr int kSink = kWOff + kWBlocks * 1024;
-  static constexpr int kStage = kSink + 1024;
-  static constexpr int kSteps = R / 16;
-  static constexpr int kUnitsPerChunk = kChunk / kUnit;
-  static constexpr int kZRowsPerBlk = 1024 / kZRow;  // 16
-  static constexpr int kZPer = kZBytes / 1024 / kWaves;
-  static constexpr int kWPer = (kWBlocks + kWaves - 1) / kWaves;
-  static constexpr int kOps = 2 * kZPer + kWPer;  // DMA instructions per wave and stage
-  __device__ __forceinline__ static int z_off(int row, int s) { return row * kZRow + ((s ^ ((row >> 2) & 3)) << 4); }
+// The draft step's tile machinery with 64-entry units: per stage a target tile
+// (256 requests x 128 bytes, the draft kernel's logits-tile layout) and a Wt
+// tile, 65 KB, two stages.  The residual rows' draft logits only seed the MFMA
+// accumulator, so they go straight to registers (two 16-byte buffer loads per
+// lane and M-tile, one unit ahead; a bonus row's, or a row past the batch, read
+// past the buffer: zeros, no traffic) instead of a third tile.  The B fragments
+// come from the fragment-ordered region that the acceptance kernel fills
+// (zeros for bonus rows, whose q is 0).
+struct VerifyRowState {
+  float mass, best, cm, cs;
+  int best_c;
 };
 
 template <int R>
 struct VerifyDma {
-  using T = VerifyTiles<R>;
-  // beyond every buffer of a pass (each below 2^31 bytes); a filler Wt slot of a
-  // dummy stage wraps round to the start of Wt, which only lands in the sink
+  using T = DraftTiles<R>;
+  static constexpr int kZPer = T::kZBytes / 1024 / kWaves;
+  static constexpr int kWPer = (T::kWBlocks + kWaves - 1) / kWaves;
   static constexpr uint32_t kOutOfRange = 0x80000000u;
-  uint32_t zoff[T::kZPer], toff[T::kZPer], woff[T::kWPer];
-
-  // zrow/trow: byte offset of the draft-logit and target rows of pass row `row`
-  __device__ __forceinline__ void init(int wave, int lane, const uint32_t* zrow_lds, const uint32_t* trow_lds) {
+  uint32_t toff[kZPer], woff[kWPer];
+  __device__ __forceinline__ void init(int wave, int lane, const uint32_t* trow_lds) {
 #pragma unroll
-    for (int j = 0; j < T::kZPer; ++j) {
-      const int row = (wave + j * kWaves) * T::kZRowsPerBlk + lane / T::kZSlots;
-      const int s = (lane % T::kZSlots) ^ ((row >> 2) & 3);
-      zoff[j] = zrow_lds[row] + (uint32_t)s * 16;
-      toff[j] = trow_lds[row] + (uint32_t)s * 16;
+    for (int j = 0; j < kZPer; ++j) {
+      const int blk = wave + j * kWaves;
+      const int row = blk * T::kZRowsPerBlk + lane / T::kZSlots;
+      const int sl = (lane % T::kZSlots) ^ (row & (T::kZSlots - 1));
+      toff[j] = trow_lds[row] + (uint32_t)sl * 16;
     }
 #pragma unroll
-    for (int j = 0; j < T::kWPer; ++j) {
+    for (int j = 0; j < kWPer; ++j) {
       const int blk = wave + j * kWaves;
       const int byte = blk * 1024 + lane * 16;
       const int lrow = byte / T::kWStride, slot = (byte % T::kWStride) / 16;
       const bool real = slot < T::kWSlots && lrow < T::kUnit;
-      woff[j] = blk >= T::kWBlocks ? kOutOfRange
-                                   : real ? (uint32_t)mfma_row_entry(lrow) * T::kWRow + (uint32_t)slot * 16 : 0u;
+      const int entry = (lrow / 32) * 32 + mfma_row_entry(lrow % 32);
+      woff[j] = blk >= T::kWBlocks ? kOutOfRange : real ? (uint32_t)entry * T::kWRow + (uint32_t)slot * 16 : 0u;
     }
   }
-  // unit starting at entry v0, or (v0 < 0) a dummy stage whose reads all fall
-  // past the end of the buffers: zeros, no memory traffic
-  __device__ __forceinline__ void stage(unsigned char* buf, __amdgpu_buffer_rsrc_t zr, __amdgpu_buffer_rsrc_t tr,
-                                        __amdgpu_buffer_rsrc_t wr, int v0, int wave) const {
-    const int zs = v0 >= 0 ? v0 * 2 : (int)kOutOfRange;
+  static constexpr int kOps = kZPer + kWPer;
+  // unit starting at entry v0, or (v0 < 0) a dummy stage whose reads fall past
+  // the buffers (a Wt filler slot may wrap to the start of Wt: it lands in the sink)
+  __device__ __forceinline__ void stage(unsigned char* buf, __amdgpu_buffer_rsrc_t tr, __amdgpu_buffer_rsrc_t wr,
+                                        int v0, int wave) const {
+    const int ts = v0 >= 0 ? v0 * 2 : (int)kOutOfRange;
     const int ws = v0 >= 0 ? v0 * T::kWRow : (int)kOutOfRange;
 #pragma unroll
-    for (int j = 0; j < T::kZPer; ++j)
+    for (int j = 0; j < kZPer; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          zr, (__attribute__((address_space(3))) void*)(buf + (wave + j * kWaves) * 1024), 16, (int)zoff[j], zs, 0,
-          0);
+          tr, (__attribute__((address_space(3))) void*)(buf + (wave + j * kWaves) * 1024), 16, (int)toff[j], ts, 0, 0);
 #pragma unroll
-    for (int j = 0; j < T::kZPer; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          tr, (__attribute__((address_space(3))) void*)(buf + T::kTOff + (wave + j * kWaves) * 1024), 16,
-          (int)toff[j], zs, 0, 0);
-#pragma unroll
-    for (int j = 0; j < T::kWPer; ++j) {
+    for (int j = 0; j < kWPer; ++j) {
       const int blk = wave + j * kWaves;
-      const int dst = blk < T::kWBlocks ? T::kWOff + blk * 1024 : T::kSink;
+      const int dst = blk < T::kWBlocks ? T::kZBytes + blk * 1024 : T::kSink;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(buf + dst), 16,
                                                (int)woff[j], ws, 0, 0);
     }
   }
 };
 
-struct VerifyRowState {
-  float mass, best, cm, cs;
-  int best_c;
-};
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4_t;
 
-// One 32-entry unit: seed from the draft-logit tile, MFMA over the rank,
-// then the residual (or bonus log-partition) epilogue.
 template <int R>
-__device__ __forceinline__ void verify_unit(const unsigned char* buf, const bf16x8_t* bfrag, int prow, int h, int lane,
-                                            int v0, int V, bool resid, float scale2, float lsp2, float lsq2,
-                                            VerifyRowState& st) {
-  using T = VerifyTiles<R>;
-  f32x16_t acc;
-  float tz[16];
-  {
-    const uint4 x = *reinterpret_cast<const uint4*>(buf + T::z_off(prow, 2 * h));
-    const uint4 y = *reinterpret_cast<const uint4*>(buf + T::z_off(prow, 2 * h + 1));
-    const uint4 tx = *reinterpret_cast<const uint4*>(buf + T::kTOff + T::z_off(prow, 2 * h));
-    const uint4 ty = *reinterpret_cast<const uint4*>(buf + T::kTOff + T::z_off(prow, 2 * h + 1));
-    const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-    const uint32_t tw[8] = {tx.x, tx.y, tx.z, tx.w, ty.x, ty.y, ty.z, ty.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      acc[2 * i] = bf16_lo(w[i]);
-      acc[2 * i + 1] = bf16_hi(w[i]);
-      tz[2 * i] = bf16_lo(tw[i]);
-      tz[2 * i + 1] = bf16_hi(tw[i]);
-    }
-  }
-  {
-    const unsigned char* wt = buf + T::kWOff + (lane & 31) * T::kWStride + 16 * h;
-    bf16x8_t af[3];
-    af[0] = *reinterpret_cast<const bf16x8_t*>(wt);
-    if (T::kSteps > 1) af[1] = *reinterpret_cast<const bf16x8_t*>(wt + 32);
-#pragma unroll
-    for (int t = 0; t < T::kSteps; ++t) {
-      if (t + 2 < T::kSteps) af[(t + 2) % 3] = *reinterpret_cast<const bf16x8_t*>(wt + 32 * (t + 2));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t % 3], bfrag[t], acc, 0, 0, 0);
-    }
-  }
-  const int e0 = v0 + 16 * h;  // first entry of this lane
-  const bool ragged = v0 + T::kUnit > V;
-  if (resid) {
-    float rs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(tz[i], scale2, -lsp2));
-      const float q = __builtin_amdgcn_exp2f(fmaf(acc[i], scale2, -lsq2));
-      const float d = fmaxf(p - q, 0.f);
-      rs += (!ragged || e0 + i < V) ? d : 0.f;
-    }
-    st.cs += rs;
-  } else {
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (ragged && e0 + i >= V) tz[i] = -INFINITY;
-      m = fmaxf(m, tz[i]);
-    }
-    m = halves32_max(m);
-    float s = 0.f;
-    if (m != -INFINITY) {
-      const float off = -m * scale2;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s += __builtin_amdgcn_exp2f(fmaf(tz[i], scale2, off));
-    }
-    s = halves32_sum(s);
-    lse2_merge(st.cm, st.cs, m * scale2, s);
-  }
-}
-
-template <int R, int STAGES>
-__global__ __launch_bounds__(kThreads, 1) void k_verify_stream(StreamArgs a) {
-  using T = VerifyTiles<R>;
-  static_assert(STAGES == 2 || STAGES == 3, "ring of two or three stages");
+__global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
+  using T = DraftTiles<R>;
+  using D = DraftUnit<R>;
   __shared__ __attribute__((aligned(1024))) unsigned char buf0[T::kStage];
   __shared__ __attribute__((aligned(1024))) unsigned char buf1[T::kStage];
-  __shared__ __attribute__((aligned(1024))) unsigned char buf2[STAGES == 3 ? T::kStage : 16];
-  __shared__ uint32_t s_zrow[kRowsPerPass], s_trow[kRowsPerPass];
+  __shared__ uint32_t s_trow[kRowsPerPass];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x, g = blockIdx.x;
@@ -1201,38 +1109,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify_stream(StreamArgs a) {
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.Wt, (uint32_t)((size_t)V * T::kWRow));
   const uint16_t* Z = static_cast<const uint16_t*>(a.Z);
   const uint16_t* Zt = static_cast<const uint16_t*>(a.Zt);
+  const int abase = T::kZBytes + (lane & 31) * T::kWStride + 16 * h;
 
   for (int base = 0; base < B; base += kRowsPerPass) {
     const int rows_valid = B - base < kRowsPerPass ? B - base : kRowsPerPass;
-    // byte offsets of each pass row's draft-logit and target rows (rows past B
-    // repeat the last valid row; their results are never stored)
+    // byte offsets of each pass row's target row (rows past B read past the buffer)
     for (int row = tid; row < kRowsPerPass; row += kThreads) {
-      const int bb = base + (row < rows_valid ? row : rows_valid - 1);
-      const int rr = row < rows_valid ? row : rows_valid - 1;
-      const int ks = a.job[bb];
-      int nb = a.n_sched[bb];
-      nb = nb < 0 ? 0 : (nb > K ? K : nb);
-      // a bonus row has no draft term (B fragments 0, q = 0, its epilogue reads only the
-      // target tile): its draft-logit slots read past the buffer, zeros without memory traffic
-      s_zrow[row] = ks > 0 ? (uint32_t)(((size_t)rr * K + (ks - 1)) * V * 2) : VerifyDma<R>::kOutOfRange;
-      s_trow[row] = (uint32_t)(((size_t)rr * (K + 1) + (ks > 0 ? ks - 1 : nb)) * V * 2);
+      uint32_t off = VerifyDma<R>::kOutOfRange;
+      if (row < rows_valid) {
+        const int bb = base + row;
+        const int ks = a.job[bb];
+        int nb = a.n_sched[bb];
+        nb = nb < 0 ? 0 : (nb > K ? K : nb);
+        off = (uint32_t)(((size_t)row * (K + 1) + (ks > 0 ? ks - 1 : nb)) * V * 2);
+      }
+      s_trow[row] = off;
     }
     barrier_lds_only();
-    const __amdgpu_buffer_rsrc_t zr =
-        make_rsrc(Z + (size_t)base * K * V, (uint32_t)((size_t)rows_valid * K * V * 2));
     const __amdgpu_buffer_rsrc_t tr =
         make_rsrc(Zt + (size_t)base * (K + 1) * V, (uint32_t)((size_t)rows_valid * (K + 1) * V * 2));
+    const __amdgpu_buffer_rsrc_t zr = make_rsrc(Z + (size_t)base * K * V, (uint32_t)((size_t)rows_valid * K * V * 2));
     VerifyDma<R> dma;
-    dma.init(wave, lane, s_zrow, s_trow);
+    dma.init(wave, lane, s_trow);
 
     const int prow = wave * 32 + (lane & 31);
     const int b = base + prow;
     const bool rv = b < B;
-    const bool wave_on = base + wave * 32 < B;
     bool resid = false;
     int kpos = 1;
     uint32_t purpose = kBonusChunk;
     float lsq2 = INFINITY, lsp2 = 0.f;  // a bonus row: q = exp2(-inf) = 0
+    uint32_t zoff = VerifyDma<R>::kOutOfRange;  // this lane's draft-logit row (residual rows only)
     if (rv) {
       const int ks = a.job[b];
       if (ks > 0) {
@@ -1241,6 +1148,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify_stream(StreamArgs a) {
         purpose = kResidChunk;
         lsq2 = a.lse_q[(size_t)b * K + ks - 1] * kLog2e;
         lsp2 = a.lse_p[(size_t)b * K + ks - 1] * kLog2e;
+        zoff = (uint32_t)(((size_t)prow * K + (ks - 1)) * V * 2);
       } else {
         int nb = a.n_sched[b];
         nb = nb < 0 ? 0 : (nb > K ? K : nb);
@@ -1249,9 +1157,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify_stream(StreamArgs a) {
     }
     const int v_first = c_begin * kChunk;
     auto unit_v0 = [&](int u) { return u < nunits ? v_first + u * T::kUnit : -1; };
-    dma.stage(buf0, zr, tr, wr, unit_v0(0), wave);
-    __builtin_amdgcn_sched_barrier(0);
-    // rows past B read fragment slots nobody wrote: only their own (discarded) MFMA column sees them
+    // this lane's 2 x 16 draft logits of unit u (entries mt * 32 + 16h + [0, 16))
+    auto zload = [&](int u, u32x4_t (&zr4)[4]) {
+      const int v0 = unit_v0(u);
+      const uint32_t zo = v0 >= 0 ? zoff : VerifyDma<R>::kOutOfRange;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          zr4[2 * mt + q] = __builtin_amdgcn_raw_buffer_load_b128(
+              zr, (int)(zo + (uint32_t)((v0 < 0 ? 0 : v0) + mt * 32 + 16 * h) * 2u + 16u * q), 0, 0);
+    };
     bf16x8_t bfrag[T::kSteps];
     {
       const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(a.efrag) + (size_t)((base >> 5) + wave) * T::kSteps * 64 + lane;
@@ -1259,7 +1175,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify_stream(StreamArgs a) {
       for (int t = 0; t < T::kSteps; ++t) bfrag[t] = src[t * 64];
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (STAGES == 3) dma.stage(buf1, zr, tr, wr, unit_v0(1), wave);
+    u32x4_t zA[4], zB[4];
+    dma.stage(buf0, tr, wr, unit_v0(0), wave);
+    zload(0, zA);
     __builtin_amdgcn_sched_barrier(0);
 
     VerifyRowState st;
@@ -1269,19 +1187,75 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify_stream(StreamArgs a) {
     st.cs = 0.f;
     st.best_c = 0x7fffffff;
     ChunkGumbels cg;
+    const bool any_bonus = __builtin_amdgcn_ballot_w64(!resid) != 0;  // this wave holds a bonus row
 
-    // unit u from stage u % 3; at its start the DMA of unit u + 2 goes into the
-    // stage that unit u - 1 used (every wave is past it at the barrier).  Every
-    // step issues exactly one stage (a dummy one past the last unit), so that
-    // one wait count means "unit u has landed" on every path.
-    auto step = [&](int u, unsigned char* cur, unsigned char* nxt2) {
-      if (STAGES == 3) wait_vmem_n<T::kOps>();
-      else wait_vmem();
-      barrier_lds_only();
-      dma.stage(nxt2, zr, tr, wr, unit_v0(u + STAGES - 1), wave);
-      if (!wave_on || u >= nunits) return;
+    auto step = [&](int u, unsigned char* cur, unsigned char* nxt, const u32x4_t (&zc)[4], u32x4_t (&zn)[4]) {
+      wait_vmem();          // unit u's tiles and draft logits have landed
+      barrier_lds_only();   // everyone's have; unit u - 1's stage is free
+      dma.stage(nxt, tr, wr, unit_v0(u + 1), wave);
+      zload(u + 1, zn);
+      if (u >= nunits) return;
       const int v0 = v_first + u * T::kUnit;
-      verify_unit<R>(cur, bfrag, prow, h, lane, v0, V, resid, scale2, lsp2, lsq2, st);
+      if (v0 + T::kUnit > V) {  // ragged tail (final unit only): targets past V become -inf
+        mask_tail<T>(cur, v0, V, tid);
+        barrier_lds_only();
+      }
+      f32x16_t acc[T::kMt];
+#pragma unroll
+      for (int mt = 0; mt < T::kMt; ++mt) {
+        const uint32_t w[8] = {zc[2 * mt][0], zc[2 * mt][1], zc[2 * mt][2], zc[2 * mt][3],
+                               zc[2 * mt + 1][0], zc[2 * mt + 1][1], zc[2 * mt + 1][2], zc[2 * mt + 1][3]};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          acc[mt][2 * i] = bf16_lo(w[i]);
+          acc[mt][2 * i + 1] = bf16_hi(w[i]);
+        }
+      }
+      D::mma(cur + abase, bfrag, acc);
+      float tz[T::kMt][16];
+#pragma unroll
+      for (int mt = 0; mt < T::kMt; ++mt) {
+        const int s0 = (mt * 32 + 16 * h) * 2 / 16;
+        const uint4 x = *reinterpret_cast<const uint4*>(cur + T::z_off(prow, s0));
+        const uint4 y = *reinterpret_cast<const uint4*>(cur + T::z_off(prow, s0 + 1));
+        const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          tz[mt][2 * i] = bf16_lo(w[i]);
+          tz[mt][2 * i + 1] = bf16_hi(w[i]);
+        }
+      }
+      // One formula for both kinds of row: d = max(2^(t s - o) - 2^(q s - lq), 0)
+      // with t the target and q the draft logit.  A residual row: o and lq are
+      // the log2 partitions, so d is the residual mass of the entry.  A bonus
+      // row: lq = +inf (no draft term) and o = the unit's maximum, so d is the
+      // target weight relative to that maximum, merged into the chunk's
+      // log-partition once per unit.  Entries past V hold -inf targets: d = 0.
+      float off = lsp2, mb = -INFINITY;
+      if (any_bonus) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < T::kMt; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) m = fmaxf(m, tz[mt][i]);
+        m = halves32_max(m);
+        mb = m * scale2;
+        if (!resid) off = m == -INFINITY ? 0.f : mb;
+      }
+      float rs = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < T::kMt; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pp = __builtin_amdgcn_exp2f(fmaf(tz[mt][i], scale2, -off));
+          const float qq = __builtin_amdgcn_exp2f(fmaf(acc[mt][i], scale2, -lsq2));
+          rs += fmaxf(pp - qq, 0.f);
+        }
+      if (any_bonus) {
+        const float sb = halves32_sum(rs);
+        if (!resid) lse2_merge(st.cm, st.cs, mb, sb);
+      }
+      if (resid) st.cs += rs;
       if ((u & (T::kUnitsPerChunk - 1)) == T::kUnitsPerChunk - 1) {  // chunk closes
         const int c = c_begin + u / T::kUnitsPerChunk;
         const float gum = cg.get(a.key, b, kpos, c, h, purpose);
@@ -1301,22 +1275,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify_stream(StreamArgs a) {
         st.cs = 0.f;
       }
     };
-    // the first step is peeled: the B fragments are first used outside the loop,
-    // so the compiler does not drain every load (the DMA in flight included)
-    // before entering it
-    if (STAGES == 3) {
-      step(0, buf0, buf2);
-      for (int u = 1; u < nunits; u += 3) {
-        step(u, buf1, buf0);
-        step(u + 1, buf2, buf1);
-        step(u + 2, buf0, buf2);
-      }
-    } else {  // two stages: unit u + 1 streams in while unit u is computed
-      step(0, buf0, buf1);
-      for (int u = 1; u < nunits; u += 2) {
-        step(u, buf1, buf0);
-        step(u + 1, buf0, buf1);
-      }
+    // the first step is peeled (the fragments are first used outside the loop)
+    step(0, buf0, buf1, zA, zB);
+    for (int u = 1; u < nunits; u += 2) {
+      step(u, buf1, buf0, zB, zA);
+      step(u + 1, buf0, buf1, zA, zB);
     }
     wait_vmem();         // the dummy stages have landed
     barrier_lds_only();  // the next pass restages the ring and the row offsets
@@ -1636,17 +1599,13 @@ __global__ __launch_bounds__(256) void k_select_b16(SelectArgs a) {
     case 256: hipLaunchKernelGGL((k_stream<ZT, 256, MODE>), G, kThreads, 0, s, a); break; \
     default: return hipErrorInvalidValue;                                               \
   }
-#ifndef DSPARK_VERIFY_STAGES
-#define DSPARK_VERIFY_STAGES 2
-#endif
-constexpr int kVerifyStages = DSPARK_VERIFY_STAGES;
 #define DSPARK_R_CASES_VERIFY16                                                        \
   switch (P.r) {                                                                       \
-    case 16: hipLaunchKernelGGL((k_verify_stream<16, kVerifyStages>), G, kThreads, 0, s, a); break;     \
-    case 32: hipLaunchKernelGGL((k_verify_stream<32, kVerifyStages>), G, kThreads, 0, s, a); break;     \
-    case 64: hipLaunchKernelGGL((k_verify_stream<64, kVerifyStages>), G, kThreads, 0, s, a); break;     \
-    case 128: hipLaunchKernelGGL((k_verify_stream<128, kVerifyStages>), G, kThreads, 0, s, a); break;   \
-    case 256: hipLaunchKernelGGL((k_verify_stream<256, kVerifyStages>), G, kThreads, 0, s, a); break;   \
+    case 16: hipLaunchKernelGGL((k_verify64<16>), G, kThreads, 0, s, a); break;         \
+    case 32: hipLaunchKernelGGL((k_verify64<32>), G, kThreads, 0, s, a); break;         \
+    case 64: hipLaunchKernelGGL((k_verify64<64>), G, kThreads, 0, s, a); break;         \
+    case 128: hipLaunchKernelGGL((k_verify64<128>), G, kThreads, 0, s, a); break;       \
+    case 256: hipLaunchKernelGGL((k_verify64<256>), G, kThreads, 0, s, a); break;       \
     default: return hipErrorInvalidValue;                                              \
   }
 #define DSPARK_DRAFT_K(R)                                                              \
