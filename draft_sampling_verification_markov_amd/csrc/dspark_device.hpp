@@ -106,6 +106,8 @@ __device__ __forceinline__ void wait_vmem_n() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 // 128-bit buffer descriptor over [base, base + bytes) (raw; reads past the end return 0)
+// four dwords, the result type of a 16-byte buffer load
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4_t;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }

@@ -1088,7 +1088,6 @@ struct VerifyDma {
   }
 };
 
-typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4_t;
 
 template <int R>
 __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
