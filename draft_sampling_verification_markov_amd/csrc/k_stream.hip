@@ -489,11 +489,19 @@ struct DraftDma {
   // DMA of the unit starting at entry v0 into `buf`
   __device__ __forceinline__ void stage(unsigned char* buf, __amdgpu_buffer_rsrc_t zr, __amdgpu_buffer_rsrc_t wr, int v0,
                                         int wave) const {
+    stage_z(buf, zr, v0, wave);
+    stage_w(buf, wr, v0, wave);
+  }
+  // the logits tile of the unit
+  __device__ __forceinline__ void stage_z(unsigned char* buf, __amdgpu_buffer_rsrc_t zr, int v0, int wave) const {
 #pragma unroll
     for (int j = 0; j < kZPer; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           zr, (__attribute__((address_space(3))) void*)(buf + (wave + j * kWaves) * 1024), 16, (int)zoff[j],
           v0 * 2, 0, 0);
+  }
+  // the Wt tile of the unit
+  __device__ __forceinline__ void stage_w(unsigned char* buf, __amdgpu_buffer_rsrc_t wr, int v0, int wave) const {
 #pragma unroll
     for (int j = 0; j < kWPer; ++j) {
       const int blk = wave + j * kWaves;
@@ -961,7 +969,9 @@ __device__ __forceinline__ void draft_step(const StreamArgs& a, unsigned char* b
       // unit 2j (first half of chunk c) from buf0, with the epilogue closing chunk c-1
       wait_vmem();
       __syncthreads();
-      dma.stage(buf1, zr, wr, v0 + T::kUnit, wave);
+      // the next unit's logits tile now, its Wt tile between this unit's two
+      // phases: the waves do not all block in issue before computing
+      dma.stage_z(buf1, zr, v0 + T::kUnit, wave);
       const float g_cur = cg.get(a.key, b, k, c, h);  // closes chunk c in the next iteration
       if (v0 + T::kUnit > V) {
         mask_tail<T>(buf0, v0, V, tid);
@@ -970,11 +980,15 @@ __device__ __forceinline__ void draft_step(const StreamArgs& a, unsigned char* b
       if (wave & 4) {  // the partner wave on this SIMD runs the other order: MFMA and VALU overlap
         draft_half<T, true>(acc1, st, c - 1, scale2, g_prev);
         __builtin_amdgcn_sched_barrier(0);
+        dma.stage_w(buf1, wr, v0 + T::kUnit, wave);
+        __builtin_amdgcn_sched_barrier(0);
         D::seed(buf0, acc0, prow, h);
         D::mma(buf0 + abase, bfrag, acc0);
       } else {
         D::seed(buf0, acc0, prow, h);
         D::mma(buf0 + abase, bfrag, acc0);
+        __builtin_amdgcn_sched_barrier(0);
+        dma.stage_w(buf1, wr, v0 + T::kUnit, wave);
         __builtin_amdgcn_sched_barrier(0);
         draft_half<T, true>(acc1, st, c - 1, scale2, g_prev);
       }
@@ -982,7 +996,8 @@ __device__ __forceinline__ void draft_step(const StreamArgs& a, unsigned char* b
       // unit 2j+1 (second half of chunk c) from buf1, with the epilogue of unit 2j
       wait_vmem();
       __syncthreads();
-      if (j + 1 < nc) dma.stage(buf0, zr, wr, v0 + kChunk, wave);
+      const bool more = j + 1 < nc;
+      if (more) dma.stage_z(buf0, zr, v0 + kChunk, wave);
       if (v0 + 2 * T::kUnit > V) {
         mask_tail<T>(buf1, v0 + T::kUnit, V, tid);
         __syncthreads();
@@ -990,11 +1005,15 @@ __device__ __forceinline__ void draft_step(const StreamArgs& a, unsigned char* b
       if (wave & 4) {
         draft_half<T, false>(acc0, st, c, scale2, 0.f);
         __builtin_amdgcn_sched_barrier(0);
+        if (more) dma.stage_w(buf0, wr, v0 + kChunk, wave);
+        __builtin_amdgcn_sched_barrier(0);
         D::seed(buf1, acc1, prow, h);
         D::mma(buf1 + abase, bfrag, acc1);
       } else {
         D::seed(buf1, acc1, prow, h);
         D::mma(buf1 + abase, bfrag, acc1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) dma.stage_w(buf0, wr, v0 + kChunk, wave);
         __builtin_amdgcn_sched_barrier(0);
         draft_half<T, false>(acc0, st, c, scale2, 0.f);
       }
@@ -1072,12 +1091,20 @@ struct VerifyDma {
   // the buffers (a Wt filler slot may wrap to the start of Wt: it lands in the sink)
   __device__ __forceinline__ void stage(unsigned char* buf, __amdgpu_buffer_rsrc_t tr, __amdgpu_buffer_rsrc_t wr,
                                         int v0, int wave) const {
+    stage_t(buf, tr, v0, wave);
+    stage_w(buf, wr, v0, wave);
+  }
+  // the target tile of the unit
+  __device__ __forceinline__ void stage_t(unsigned char* buf, __amdgpu_buffer_rsrc_t tr, int v0, int wave) const {
     const int ts = v0 >= 0 ? v0 * 2 : (int)kOutOfRange;
-    const int ws = v0 >= 0 ? v0 * T::kWRow : (int)kOutOfRange;
 #pragma unroll
     for (int j = 0; j < kZPer; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           tr, (__attribute__((address_space(3))) void*)(buf + (wave + j * kWaves) * 1024), 16, (int)toff[j], ts, 0, 0);
+  }
+  // the Wt tile of the unit
+  __device__ __forceinline__ void stage_w(unsigned char* buf, __amdgpu_buffer_rsrc_t wr, int v0, int wave) const {
+    const int ws = v0 >= 0 ? v0 * T::kWRow : (int)kOutOfRange;
 #pragma unroll
     for (int j = 0; j < kWPer; ++j) {
       const int blk = wave + j * kWaves;
@@ -1191,9 +1218,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
     auto step = [&](int u, unsigned char* cur, unsigned char* nxt, const u32x4_t (&zc)[4], u32x4_t (&zn)[4]) {
       wait_vmem();          // unit u's tiles and draft logits have landed
       barrier_lds_only();   // everyone's have; unit u - 1's stage is free
-      dma.stage(nxt, tr, wr, unit_v0(u + 1), wave);
+      // the next unit's requests in two bursts, the Wt tile after this unit's
+      // MFMA, so the waves do not all block in issue before computing
+      dma.stage_t(nxt, tr, unit_v0(u + 1), wave);
       zload(u + 1, zn);
-      if (u >= nunits) return;
+      if (u >= nunits) {
+        dma.stage_w(nxt, wr, unit_v0(u + 1), wave);
+        return;
+      }
       const int v0 = v_first + u * T::kUnit;
       if (v0 + T::kUnit > V) {  // ragged tail (final unit only): targets past V become -inf
         mask_tail<T>(cur, v0, V, tid);
@@ -1211,6 +1243,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
         }
       }
       D::mma(cur + abase, bfrag, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      dma.stage_w(nxt, wr, unit_v0(u + 1), wave);
+      __builtin_amdgcn_sched_barrier(0);
       float tz[T::kMt][16];
 #pragma unroll
       for (int mt = 0; mt < T::kMt; ++mt) {
