@@ -954,13 +954,15 @@ __device__ __forceinline__ void draft_step(const StreamArgs& a, unsigned char* b
     D::mma(buf0 + abase, bfrag, acc0);
     wait_vmem();
     __syncthreads();
-    if (nc > 1) dma.stage(buf0, zr, wr, vb + kChunk, wave);
+    if (nc > 1) dma.stage_z(buf0, zr, vb + kChunk, wave);
     if (vb + 2 * T::kUnit > V) {
       mask_tail<T>(buf1, vb + T::kUnit, V, tid);
       __syncthreads();
     }
     D::seed(buf1, acc1, prow, h);
     D::mma(buf1 + abase, bfrag, acc1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nc > 1) dma.stage_w(buf0, wr, vb + kChunk, wave);
     __builtin_amdgcn_sched_barrier(0);
     draft_half<T, false>(acc0, st, c_begin, scale2, 0.f);
     for (int j = 1; j < nc; ++j) {
