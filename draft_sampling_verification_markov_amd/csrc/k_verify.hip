@@ -86,17 +86,20 @@ struct Vec16<float> {
   }
 };
 
-// Raw 16-byte pieces of one (row, segment) item, prefetched one item ahead.
+// Raw 16-byte pieces of one (row, segment) item, through a buffer descriptor
+// over the row: entries past V, and every piece when the item does not exist
+// (a zero-sized descriptor), read as zeros without a memory access, so the
+// next item's loads need no branch.  (Behind a branch the compiler made the
+// reduction wait for them too, and nothing overlapped.)
 template <typename ZT>
 struct VlseItem {
   static constexpr int kLoads = kVlseSeg / 256 / Vec16<ZT>::N;  // 16-byte loads per thread
-  uint4 raw[kLoads];
-  __device__ __forceinline__ void load(const ZT* row, int lo, int V, int tid) {
+  u32x4_t raw[kLoads];
+  __device__ __forceinline__ void load(const ZT* row, bool valid, int lo, int V, int tid) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, valid ? (uint32_t)V * (uint32_t)sizeof(ZT) : 0u);
 #pragma unroll
-    for (int l = 0; l < kLoads; ++l) {
-      const int v = lo + (l * 256 + tid) * Vec16<ZT>::N;
-      raw[l] = *reinterpret_cast<const uint4*>(row + (v < V ? v : 0));  // past V: a valid address, masked below
-    }
+    for (int l = 0; l < kLoads; ++l)
+      raw[l] = __builtin_amdgcn_raw_buffer_load_b128(rs, (lo + (l * 256 + tid) * Vec16<ZT>::N) * (int)sizeof(ZT), 0, 0);
   }
 };
 
@@ -106,7 +109,7 @@ __device__ __forceinline__ const ZT* vlse_row(const VerifyArgs& a, const int* s_
                                               int& seg) {
   const int j = w / a.nseg;
   seg = w - j * a.nseg;
-  const int code = LOCAL ? s_rows[j] : a.rows[j];
+  const int code = __builtin_amdgcn_readfirstlane(LOCAL ? s_rows[j] : a.rows[j]);  // uniform: scalar row base
   b = code >> 6;
   k0 = code & 63;
   return static_cast<const ZT*>(a.Zt) + ((size_t)b * (a.K + 1) + k0) * a.V;
@@ -168,21 +171,24 @@ __global__ __launch_bounds__(256) void k_vlse(VerifyArgs a) {
   } else {
     M = *a.nrows;
   }
-  const int items = M * a.nseg;
+  const int items = __builtin_amdgcn_readfirstlane(M) * a.nseg;  // the same in every lane
   int w = blockIdx.x;
   if (w >= items) return;
   int b, k0, seg;
   const ZT* row = vlse_row<ZT, LOCAL>(a, s_rows, w, b, k0, seg);
   It cur;
-  cur.load(row, seg * kVlseSeg, a.V, tid);
+  __builtin_amdgcn_sched_barrier(0);
+  cur.load(row, true, seg * kVlseSeg, a.V, tid);
+  __builtin_amdgcn_sched_barrier(0);
   for (; w < items; w += gridDim.x) {
     const int wn = w + gridDim.x;
-    int bn = 0, kn = 0, segn = 0;
+    const bool vn = wn < items;
+    int bn, kn, segn;
     It nxt;
-    if (wn < items) {
-      const ZT* rown = vlse_row<ZT, LOCAL>(a, s_rows, wn, bn, kn, segn);
-      nxt.load(rown, segn * kVlseSeg, a.V, tid);
-    }
+    const ZT* rown = vlse_row<ZT, LOCAL>(a, s_rows, vn ? wn : w, bn, kn, segn);
+    __builtin_amdgcn_sched_barrier(0);
+    nxt.load(rown, vn, segn * kVlseSeg, a.V, tid);
+    __builtin_amdgcn_sched_barrier(0);
     // VALU-bound (one transcendental per entry): the max is taken on the raw
     // logits, the temperature folds into one fma per entry, and only the last
     // segment of a row masks entries past V (V is a multiple of 8: a 16-byte
