@@ -1220,11 +1220,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
     auto step = [&](int u, unsigned char* cur, unsigned char* nxt, const u32x4_t (&zc)[4], u32x4_t (&zn)[4]) {
       wait_vmem();          // unit u's tiles and draft logits have landed
       barrier_lds_only();   // everyone's have; unit u - 1's stage is free
-      // the next unit's requests in two bursts, the Wt tile after this unit's
-      // MFMA, so the waves do not all block in issue before computing
+      // the next unit's requests in two bursts: its target tile now, its Wt
+      // tile and draft logits after this unit's MFMA, so the waves do not all
+      // block in issue before computing
       dma.stage_t(nxt, tr, unit_v0(u + 1), wave);
-      zload(u + 1, zn);
       if (u >= nunits) {
+        zload(u + 1, zn);
         dma.stage_w(nxt, wr, unit_v0(u + 1), wave);
         return;
       }
@@ -1247,6 +1248,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
       D::mma(cur + abase, bfrag, acc);
       __builtin_amdgcn_sched_barrier(0);
       dma.stage_w(nxt, wr, unit_v0(u + 1), wave);
+      zload(u + 1, zn);
       __builtin_amdgcn_sched_barrier(0);
       float tz[T::kMt][16];
 #pragma unroll
