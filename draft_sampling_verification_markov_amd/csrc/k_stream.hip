@@ -1522,9 +1522,12 @@ __global__ __launch_bounds__(256) void k_select_b16(SelectArgs a) {
   const int v0 = cstar * kChunk;
   const int nrow = V - v0 < kChunk ? V - v0 : kChunk;
   const uint16_t* blk = static_cast<const uint16_t*>(a.Wt) + (size_t)v0 * R;
+  // (the block in two bursts around the entry Gumbel: all 64 KB at once kept
+  // the waves blocked in issue, and the Gumbel's arithmetic waited behind it)
   uint4 w[NP];
+  constexpr int NH = NP > 1 ? NP / 2 : NP;
 #pragma unroll
-  for (int i = 0; i < NP; ++i) {
+  for (int i = 0; i < NH; ++i) {
     const int row = i * RG + grp;
     w[i] = *reinterpret_cast<const uint4*>(blk + (size_t)(row < nrow ? row : 0) * R + 8 * c);
   }
@@ -1539,7 +1542,14 @@ __global__ __launch_bounds__(256) void k_select_b16(SelectArgs a) {
   const bool inside = tid < kChunk && r < nrow;
   const ZT* zrow = static_cast<const ZT*>(a.Z) + ((size_t)b * K + (a.k - 1)) * V;
   const float z = logit_at<ZT>(zrow, r < nrow ? v : v0);
+  __builtin_amdgcn_sched_barrier(0);
   const float gum = gumbel_from_word(draw_word(a.key, (uint32_t)v, (uint32_t)b, (uint32_t)a.k, kDraftElem));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = NH; i < NP; ++i) {
+    const int row = i * RG + grp;
+    w[i] = *reinterpret_cast<const uint4*>(blk + (size_t)(row < nrow ? row : 0) * R + 8 * c);
+  }
   {
     float m = -INFINITY, sm = 0.f;
     if (tid < a.G) lse2_merge(m, sm, p.x, p.y);
