@@ -92,9 +92,3 @@ def test_zero_weights_never_drawn():
     logw[support] = [0.0, 1.0, -1.0, 0.5]
     seen = {sampling.two_level_sample(logw, s, 0, 1, 4, 5)[0] for s in range(400)}
     assert seen == set(support)
-
-
-def test_margin_is_the_smaller_top2_gap():
-    logw = np.array([0.0, 0.0] + [-np.inf] * 126 + [5.0])
-    v, margin, c = sampling.two_level_sample(logw, 0, 0, 1, 1, 2)
-    assert margin >= 0 and np.isfinite(margin)
