@@ -66,10 +66,18 @@ def cycle_bytes(cfg, N: int, R: int) -> float:
     return (B * K * V * sz + r * V * sw + 2 * B * K * r * sw + B * K * d * sh + N * V * sz + R * V * sz)
 
 
-def stream_launch_bytes(cfg, G: int) -> float:
-    """Algorithmic bytes of one draft-step stream launch: the step's Z slab, Wt
-    (the launch forms the whole [B x r] . [r x V] product), the gathered E rows,
-    and the per-(row, workgroup) partials written."""
+def stream_launch_bytes(cfg) -> float:
+    """Algorithmic bytes of one draft step: the step's Z slab, the gathered E rows
+    of the previous tokens, and 1/K of Wt.  The cycle reads Wt once
+    (B*K*V*s_z + r*V*s_w + B*K*r*s_w ... per cycle): a re-read of Wt at each of the K
+    steps is traffic, not algorithmic bytes, so a step is charged Wt / K."""
+    sz, sw = element_size(cfg.logits_dtype), element_size(cfg.weight_dtype)
+    return cfg.B * cfg.V * sz + cfg.V * cfg.r * sw / cfg.K + cfg.B * cfg.r * sw
+
+
+def stream_launch_bytes_full_wt(cfg, G: int) -> float:
+    """The same launch charged a whole Wt read (what the launch streams when Wt
+    does not stay on chip across the steps) plus the partials it writes."""
     sz, sw = element_size(cfg.logits_dtype), element_size(cfg.weight_dtype)
     return cfg.B * cfg.V * sz + cfg.V * cfg.r * sw + cfg.B * cfg.r * sw + cfg.B * G * 16
 
@@ -157,26 +165,32 @@ def step_traffic_from_profile(cfg):
     return float(sum(per[k] * c for k, c in kern.items()))
 
 
-def cpu_baseline(cfg, inp, gpu, n_req: int, min_seconds: float = 10.0):
+def cpu_baseline(cfg, inp, n_req: int, min_seconds: float = 10.0):
     """The oracle, as it stands, on a bounded sample: all K draft steps, the
     confidence head and verification for n_req requests, and the scheduler over
-    the whole batch (on the GPU's survivals)."""
+    a whole batch of candidates (the sample's own survivals, the other requests'
+    from the seeded survival generator).  Nothing the GPU computed enters it."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
+    import synth
     from oracle import conf as oconf
     from oracle import draft as odraft
     from oracle import sched as osched
     from oracle import verify as overify
 
     reqs = np.arange(n_req)
+    S_rest = synth.make_survivals(cfg.B, cfg.K, seed=cfg.seed).astype(np.float64)
     reps = 0
     t0 = time.perf_counter()
     while True:  # the sample, repeated until at least min_seconds of CPU work
         d = odraft.draft(inp["Z"], inp["E"], inp["Wt"], inp["anchor"], cfg.T_s, cfg.seed, requests=reqs)
-        oconf.confidence(inp["h"][reqs], inp["E"], inp["w_c"], inp["b_c"], inp["tau"], inp["anchor"][reqs], d["x"])
-        sc = osched.schedule(gpu["surv"].astype(np.float64), inp["T"])
-        x = gpu["tok"].astype(np.int64).copy()
+        _, S = oconf.confidence(inp["h"][reqs], inp["E"], inp["w_c"], inp["b_c"], inp["tau"], inp["anchor"][reqs],
+                                d["x"])
+        S_all = S_rest.copy()
+        S_all[reqs] = S
+        sc = osched.schedule(S_all, inp["T"])
+        x = np.zeros((cfg.B, cfg.K), np.int64)
         x[reqs] = d["x"]
         overify.verify(inp["Zt"], inp["Z"], inp["E"], inp["Wt"], inp["anchor"], x, sc["n"], cfg.T_s, cfg.seed,
                        requests=reqs)
@@ -312,8 +326,8 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="high_concurrency")
     ap.add_argument("--cpu-requests", type=int, default=0,
                     help="requests in the oracle's timed sample (default: the whole batch)")
@@ -381,16 +395,23 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"{args.warmup} warm-up steps done")
 
-    # timed region: exactly `steps` whole steps
+    # timed region: exactly `steps` whole steps, back to back; an event between
+    # consecutive steps also gives each step's own duration (for the median)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     start.record()
+    marks[0].record()
     for i in range(args.steps):
         runner.run_cycle(P, sets[i % 3], o)
+        marks[i + 1].record()
     stop.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / args.steps
-    log(f"{args.steps} timed steps: {ms_step:.3f} ms/step")
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    ms_median = float(np.median(per_step))
+    log(f"{args.steps} timed steps: {ms_step:.3f} ms/step (median {ms_median:.3f}, "
+        f"min {per_step.min():.3f}, max {per_step.max():.3f})")
 
     # per-call split (a separate pass over the same steps)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -579,7 +600,8 @@ def main() -> int:
     alg_bytes = cycle_bytes(cfg, N, R)
     nc = (cfg.V + 127) // 128                     # the library's stream grid: fewest workgroups
     G = -(-nc // -(-nc // 256))                    # with the busiest one's chunk count unchanged
-    launch_bytes = stream_launch_bytes(cfg, G)
+    launch_bytes = stream_launch_bytes(cfg)
+    launch_bytes_full = stream_launch_bytes_full_wt(cfg, G)
     achieved = launch_bytes / (k_ms / 1e3) / 1e9
     traffic = traffic_from_profile(cfg.name)
     step_traffic = step_traffic_from_profile(cfg)
@@ -593,6 +615,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_median": ms_median,
+        "positions_per_s_median_step": positions / (ms_median / 1e3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -606,6 +630,7 @@ def main() -> int:
         "hbm_frac_counters": None if step_traffic is None else step_traffic / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
         "counter_bytes_per_step": step_traffic,
         "algorithmic_bytes_per_step": alg_bytes,
+        "traffic_over_algorithmic_step": None if step_traffic is None else step_traffic / alg_bytes,
         "logits_per_s": (positions + N) * cfg.V / (ms_step / 1e3),
         "ms_split": {"draft": split[0], "schedule": split[1], "verify": split[2]},
         "ms_per_step_graph_replay": ms_graph,
@@ -631,14 +656,18 @@ def main() -> int:
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
+            "traffic_over_algorithmic": None if traffic is None else traffic / launch_bytes,
             "avg_launch_ms": k_ms,
             "bytes_per_launch": launch_bytes,
+            "bytes_per_launch_note": "Z slab + E rows of the previous tokens + Wt/K (Wt counted once per cycle)",
+            "bytes_per_launch_full_wt": launch_bytes_full,
+            "frac_full_wt": launch_bytes_full / (k_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         },
     }
     if not args.no_cpu_baseline:
         n_cpu = args.cpu_requests if args.cpu_requests > 0 else cfg.B
         log(f"timing the CPU oracle on {n_cpu} requests")
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, g, n_cpu)
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, n_cpu)
     print(json.dumps(line), flush=True)
     return 0
 

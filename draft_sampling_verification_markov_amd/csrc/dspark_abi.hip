@@ -15,6 +15,7 @@ Layout make_layout(const dspark_problem& P) {
   L.nseg = vlse_segments(P.V);
   size_t off = 0;
   L.part = off;   off = align_up(off + B * L.G * sizeof(float4));
+  L.zpart = off;  off = align_up(off + B * L.G * sizeof(float2));
   L.vlse = off;   off = align_up(off + B * K * L.nseg * sizeof(float2));
   L.lsep = off;   off = align_up(off + B * K * sizeof(float));
   L.job = off;    off = align_up(off + B * sizeof(int32_t));
@@ -378,6 +379,7 @@ static dspark_status verify_impl(const dspark_problem* P, const void* target, co
   va.rows = at<int32_t>(workspace, L.rows);
   va.nrows = at<int32_t>(workspace, L.nrows);
   va.part = at<float4>(workspace, L.part);
+  va.zpart = at<float2>(workspace, L.zpart);
   va.B = p.B;
   va.K = p.K;
   va.V = p.V;
@@ -403,6 +405,7 @@ static dspark_status verify_impl(const dspark_problem* P, const void* target, co
   sa.job = va.job;
   sa.n_sched = n_sched;
   sa.part = at<float4>(workspace, L.part);
+  sa.zpart = at<float2>(workspace, L.zpart);
   sa.efrag = va.efrag;
   sa.B = p.B;
   sa.K = p.K;

@@ -86,6 +86,78 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
   return -logf(e);
 }
 
+// 2^x - 1 for 0 <= x <= 1/2 without the cancellation of exp2(x) - 1: the power
+// series of e^y - 1 at y = x ln 2 through y^8 (coefficients (ln 2)^k / k!; the
+// remainder is below 2e-9 of the result on this range), in Horner form.
+__device__ __forceinline__ float exp2m1_small(float x) {
+  float p = 1.3215486790144307e-06f;
+  p = fmaf(x, p, 1.525273380405984e-05f);
+  p = fmaf(x, p, 1.5403530393381608e-04f);
+  p = fmaf(x, p, 1.3333558146428443e-03f);
+  p = fmaf(x, p, 9.618129107628477e-03f);
+  p = fmaf(x, p, 5.550410866482158e-02f);
+  p = fmaf(x, p, 2.402265069591007e-01f);
+  p = fmaf(x, p, 6.931471805599453e-01f);
+  return x * p;
+}
+
+// One vocabulary entry of a rejected position's residual max(0, p - q), in the
+// row's reference units: p^ = 2^(t s2 - lp2) with t the target logit, q^ =
+// 2^((z + bias) s2 - lq2) with z the base draft logit and bias the Markov term,
+// s2 = log2(e) / T_s and lp2, lq2 the log2-partitions the row is referred to.
+// The draft logit z + bias is never rounded as one number: q^'s exponent is
+// fma(bias, s2, fma(z, s2, -lq2)), and d = log2(p^ / q^) is
+// ((t - z) - bias) s2 - (lp2 - lq2) with t - z exact, so neither carries a
+// rounding at the logits' magnitude (a bias accumulated onto the logit would
+// round at every step of the contraction).  The weight is q^ (2^d - 1) for
+// 0 < d <= 1/2 (no cancellation where p and q are close), p^ - q^ for d > 1/2
+// and 0 otherwise.  dlp = lp2 - lq2; a row without a draft term (a bonus row)
+// passes lq2 = +inf and dlp = -inf, and gets r = p^; an entry past the end of
+// the row passes t = z = -inf and gets zeros.  Every kernel that forms residual
+// weights uses this function, so the chunk masses of the resample pass and the
+// entry weights of the final draw come from one formula.
+// qa is q^ where d > 0 (the entries the residual keeps), else 0: the residual
+// mass normalised by the row's own sums of p^ and q^ is then
+// (sum r + sum qa) / sum p^ - sum qa / sum q^.
+struct ResidEntry {
+  float p, q, r, qa;
+};
+__device__ __forceinline__ ResidEntry resid_entry(float t, float z, float bias, float s2, float lp2, float lq2,
+                                                  float dlp) {
+  ResidEntry e;
+  e.p = __builtin_amdgcn_exp2f(fmaf(t, s2, -lp2));
+  e.q = __builtin_amdgcn_exp2f(fmaf(bias, s2, fmaf(z, s2, -lq2)));
+  const float d = fmaf((t - z) - bias, s2, -dlp);
+  const float small = e.q * exp2m1_small(d);
+  e.r = d > 0.5f ? e.p - e.q : (d > 0.f ? small : 0.f);
+  e.qa = d > 0.f ? e.q : 0.f;
+  return e;
+}
+// Running sums of the residual terms of one row in two interleaved partials
+// per quantity (entry i goes to partial i & 1), so that a sum of n terms has
+// n / 2 + 1 roundings in its longest chain instead of n.
+struct ResidSums {
+  float r[2], p[2], q[2], qa[2];
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) r[j] = p[j] = q[j] = qa[j] = 0.f;
+  }
+  __device__ __forceinline__ void add(int i, const ResidEntry& e) {
+    r[i & 1] += e.r;
+    p[i & 1] += e.p;
+    q[i & 1] += e.q;
+    qa[i & 1] += e.qa;
+  }
+  __device__ __forceinline__ static float fold(const float (&x)[2]) { return x[0] + x[1]; }
+};
+// The residual mass of a row from the fp64 sums of r, qa, p^ and q^ over the
+// whole vocabulary (the resample pass's partials merged): p = p^ / Zp and
+// q = q^ / Zq exactly, whatever the error of the log-partitions the entries
+// were referred to.
+__device__ __forceinline__ double resid_mass_normalised(double R, double QA, double Zp, double Zq) {
+  return R / Zp + QA * ((Zq - Zp) / (Zp * Zq));
+}
+
 // bf16 halves of a packed 32-bit word -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -144,6 +216,15 @@ __device__ __forceinline__ float2 halves32(float x) {
   return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float halves32_max(float x) { const float2 h = halves32(x); return fmaxf(h.x, h.y); }
+// The same sum of the two half-wave values in float64 (both 32-bit halves swapped alike).
+__device__ __forceinline__ double halves32_sum_d(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)u, (unsigned)u, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((unsigned)(u >> 32), (unsigned)(u >> 32), false, false);
+  const double a = __longlong_as_double((long long)(((unsigned long long)hi[0] << 32) | lo[0]));
+  const double b = __longlong_as_double((long long)(((unsigned long long)hi[1] << 32) | lo[1]));
+  return a + b;
+}
 __device__ __forceinline__ float halves32_sum(float x) { const float2 h = halves32(x); return h.x + h.y; }
 
 // Whole-wave reductions on the VALU cross-lane paths instead of the LDS
@@ -198,6 +279,13 @@ __device__ __forceinline__ float wave_sum(float v) {
   v = h.x + h.y;
   h = halves32(v);
   return h.x + h.y;
+}
+
+// float64 sum over the wave (ds_bpermute exchanges; for once-per-row merges)
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
 __device__ __forceinline__ int wave_min_i(int v) {

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "../../include/dspark.h"
+#include "../../include/dspark_instr.h"
 #include "dspark_device.hpp"
 
 namespace dspark {
@@ -41,6 +42,7 @@ struct Layout {
   int G;        // stream-kernel workgroups
   int nseg;     // verify segments per target row
   size_t part;  // float4 [B][G]: per-(row, workgroup) partials of the stream kernel
+  size_t zpart; // float2 [B][G]: resample pass, per-(row, workgroup) sums of p^ and q^ (residual normalisers)
   size_t vlse;  // float2 [B*K][nseg]: per-segment (max, sum) of target rows, base 2
   size_t lsep;  // float [B][K]: log-partition of p_k in nats
   size_t job;   // int32 [B]: position of the first rejection (0 = all accepted)
@@ -69,6 +71,7 @@ struct StreamArgs {
   const int32_t* job;    // [B] (verify)
   const int32_t* n_sched;// [B] (verify)
   float4* part;          // [B][G]
+  float2* zpart;         // [B][G] (verify): sums of p^ and q^ over the workgroup's entries of a residual row
   const uint4* efrag;    // B fragments of the previous tokens (draft kernel with bf16 logits and factors)
   int first_from_anchor; // draft kernel with bf16 logits and factors: B fragments gathered from E[anchor]
   int B, K, V, k;        // k: 1-based draft position (draft mode)
@@ -128,6 +131,7 @@ struct VerifyArgs {
   int32_t* rows;
   int32_t* nrows;
   const float4* part;
+  const float2* zpart;   // [B][G]: the resample pass's sums of p^ and q^ (residual rows)
   uint4* efrag;          // if set, k_accept stores the resample pass's B fragments there
   const float* state;    // RNN head: [B][K][r] states, the projection operands (bf16-rounded) of the positions
   int B, K, V, r, G, nseg;

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream_generic(StreamArgs a) {
     const ZT* zrow = Z;
     const ZT* trow = Zt;
     bool resid = false;
-    float lsq2 = 0.f, lsp2 = 0.f;
+    float lsq2 = 0.f, lsp2 = 0.f, dlp = 0.f;
     if (rv) {
       if (MODE == MODE_DRAFT) {
         prev = clamp_id(a.k == 1 ? a.anchor[b] : a.tok[(size_t)b * K + a.k - 2], V);
@@ -212,6 +212,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream_generic(StreamArgs a) {
           trow = Zt + ((size_t)b * (K + 1) + (ks - 1)) * V;
           lsq2 = a.lse_q[(size_t)b * K + ks - 1] * kLog2e;
           lsp2 = a.lse_p[(size_t)b * K + ks - 1] * kLog2e;
+          dlp = lsp2 - lsq2;
         } else {
           int nb = a.n_sched[b];
           nb = nb < 0 ? 0 : (nb > K ? K : nb);
@@ -225,7 +226,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream_generic(StreamArgs a) {
     F frag;
     frag.load(static_cast<const WT*>(a.E), prev, need_bias, lane);
 
-    float run_m = -INFINITY, run_s = 0.f, best = -INFINITY, mass = 0.f;
+    float run_m = -INFINITY, run_s = 0.f, best = -INFINITY;
+    double Rs = 0.0, QAs = 0.0, Zps = 0.0, Zqs = 0.0;  // residual rows: this lane's sums of r, qa, p^, q^
     int best_c = 0x7fffffff;
     int quad_id = -1;
     Words4 quad = {};
@@ -260,22 +262,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream_generic(StreamArgs a) {
 
       if (MODE == MODE_VERIFY && resid) {
         // residual max(0, p - q) of the rejected position
-        float rs = 0.f;
+        ResidSums sums;
+        sums.clear();
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int q = mt * 4 + (i >> 2);
             const int v = v0 + mt * 32 + (i >> 2) * 8 + 4 * (lane >> 5) + (i & 3);
-            if (v < V) {
-              const float p = exp2f(L::get(tr, q, i & 3) * a.scale2 - lsp2);
-              const float qq = exp2f((L::get(zr, q, i & 3) + acc[mt][i]) * a.scale2 - lsq2);
-              rs += fmaxf(p - qq, 0.f);
-            }
+            // entries past V: the target and draft logit -inf, so every weight is 0
+            const bool in = v < V;
+            sums.add(i, resid_entry(in ? L::get(tr, q, i & 3) : -INFINITY, in ? L::get(zr, q, i & 3) : -INFINITY,
+                                    acc[mt][i], a.scale2, lsp2, lsq2, dlp));
           }
         }
-        rs += __shfl_xor(rs, 32);
-        mass += rs;
+        float rs = ResidSums::fold(sums.r);
+        Rs += (double)rs;
+        QAs += (double)ResidSums::fold(sums.qa);
+        Zps += (double)ResidSums::fold(sums.p);
+        Zqs += (double)ResidSums::fold(sums.q);
+        rs = halves32_sum(rs);
         const float score = rs > 0.f ? logf(rs) + gum : -INFINITY;
         if (score > best) {
           best = score;
@@ -320,14 +326,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream_generic(StreamArgs a) {
       }
     }
 
-    if (rv && lane < 32) {
-      float4 out;
-      if (MODE == MODE_DRAFT) {
-        out = make_float4(run_m, run_s, best, __int_as_float(best_c));
-      } else {
-        out = make_float4(mass, 0.f, best, __int_as_float(best_c));
+    if (MODE == MODE_DRAFT) {
+      if (rv && lane < 32) a.part[(size_t)b * G + g] = make_float4(run_m, run_s, best, __int_as_float(best_c));
+    } else {
+      const double R_g = halves32_sum_d(Rs), QA_g = halves32_sum_d(QAs);
+      const double Zp_g = halves32_sum_d(Zps), Zq_g = halves32_sum_d(Zqs);
+      if (rv && lane < 32) {
+        a.part[(size_t)b * G + g] = make_float4((float)R_g, (float)QA_g, best, __int_as_float(best_c));
+        a.zpart[(size_t)b * G + g] = make_float2((float)Zp_g, (float)Zq_g);
       }
-      a.part[(size_t)b * G + g] = out;
     }
   }
 }
@@ -595,7 +602,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(StreamArgs a) {
     int prev = 0, kpos = a.k;
     uint32_t purpose = kDraftChunk;
     bool resid = false;
-    float lsq2 = 0.f, lsp2 = 0.f;
+    float lsq2 = 0.f, lsp2 = 0.f, dlp = 0.f;
     if (rv) {
       if (MODE == MODE_DRAFT) {
         prev = clamp_id(a.k == 1 ? a.anchor[b] : a.tok[(size_t)b * K + a.k - 2], V);
@@ -608,6 +615,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(StreamArgs a) {
           prev = clamp_id(ks == 1 ? a.anchor[b] : a.tok[(size_t)b * K + ks - 2], V);
           lsq2 = a.lse_q[(size_t)b * K + ks - 1] * kLog2e;
           lsp2 = a.lse_p[(size_t)b * K + ks - 1] * kLog2e;
+          dlp = lsp2 - lsq2;
         } else {
           int nb = a.n_sched[b];
           nb = nb < 0 ? 0 : (nb > K ? K : nb);
@@ -625,7 +633,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(StreamArgs a) {
         bfrag[t] = need ? *reinterpret_cast<const bf16x8_t*>(src + 16 * t) : bf16x8_t{};
     }
 
-    float run_m = -INFINITY, run_s = 0.f, best = -INFINITY, mass = 0.f;
+    float run_m = -INFINITY, run_s = 0.f, best = -INFINITY;
+    double Rs = 0.0, QAs = 0.0, Zps = 0.0, Zqs = 0.0;  // residual rows: this lane's sums of r, qa, p^, q^
     int best_c = 0x7fffffff;
     float cm = -INFINITY, cs = 0.f;  // current chunk: (max, sum) base 2, or residual sum
     int quad_id = -1;
@@ -646,13 +655,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(StreamArgs a) {
       }
       if (!wave_on) continue;
 
+      // draft mode: the accumulator starts from the logits (D = logits + bias);
+      // verify mode: from zero, so that the Markov term of a residual row is
+      // accumulated at its own small magnitude and the logits are added once,
+      // in the epilogue (the residual is sensitive to that rounding)
       f32x16_t acc[T::kMt];
 #pragma unroll
       for (int mt = 0; mt < T::kMt; ++mt) {
         float z[16];
-        read16<ZT, T>(cur, prow, (mt * 32 + 16 * h) * (int)sizeof(ZT) / 16, z);
+        if (MODE == MODE_DRAFT) read16<ZT, T>(cur, prow, (mt * 32 + 16 * h) * (int)sizeof(ZT) / 16, z);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mt][i] = z[i];
+        for (int i = 0; i < 16; ++i) acc[mt][i] = MODE == MODE_DRAFT ? z[i] : 0.f;
       }
 #pragma unroll
       for (int t = 0; t < T::kSteps; ++t) {
@@ -667,21 +680,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(StreamArgs a) {
 
       if (MODE == MODE_VERIFY && resid) {
         // residual max(0, p - q) of the rejected position; q from the same tiles as the draft
-        float rs = 0.f;
+        ResidSums sums;
+        sums.clear();
 #pragma unroll
         for (int mt = 0; mt < T::kMt; ++mt) {
-          float tz[16];
+          float tz[16], zz[16];
           read16<ZT, T>(cur + T::kZBytes, prow, (mt * 32 + 16 * h) * (int)sizeof(ZT) / 16, tz);
+          read16<ZT, T>(cur, prow, (mt * 32 + 16 * h) * (int)sizeof(ZT) / 16, zz);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(tz[i], scale2, -lsp2));
-            const float q = __builtin_amdgcn_exp2f(fmaf(acc[mt][i], scale2, -lsq2));
-            const float d = fmaxf(p - q, 0.f);
-            rs += (!ragged || v0 + mt * 32 + 16 * h + i < V) ? d : 0.f;
+            // entries past V: the target and draft logit -inf, so every weight is 0
+            const bool in = !ragged || v0 + mt * 32 + 16 * h + i < V;
+            sums.add(i, resid_entry(in ? tz[i] : -INFINITY, in ? zz[i] : -INFINITY, acc[mt][i], scale2, lsp2, lsq2,
+                                    dlp));
           }
         }
+        const float rs = ResidSums::fold(sums.r);
         cs += rs;
+        Rs += (double)rs;
+        QAs += (double)ResidSums::fold(sums.qa);
+        Zps += (double)ResidSums::fold(sums.p);
+        Zqs += (double)ResidSums::fold(sums.q);
       } else {
+        if (MODE == MODE_VERIFY) {  // a bonus row: its target row (the logits tile); no draft term
+#pragma unroll
+          for (int mt = 0; mt < T::kMt; ++mt) {
+            float zz[16];
+            read16<ZT, T>(cur, prow, (mt * 32 + 16 * h) * (int)sizeof(ZT) / 16, zz);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mt][i] += zz[i];
+          }
+        }
         if (ragged) {
 #pragma unroll
           for (int mt = 0; mt < T::kMt; ++mt)
@@ -714,8 +743,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(StreamArgs a) {
         const float gum = gumbel_from_word(quad_word(quad, c & 3));
         float score;
         if (MODE == MODE_VERIFY && resid) {
-          const float rc = cs + __shfl_xor(cs, 32);
-          mass += rc;
+          const float rc = halves32_sum(cs);
           score = rc > 0.f ? logf(rc) + gum : -INFINITY;
         } else {
           score = cs > 0.f ? (cm + log2f(cs)) * kLn2 + gum : -INFINITY;
@@ -730,10 +758,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream(StreamArgs a) {
       }
     }
     __syncthreads();  // the next pass restages buffer 0
-    if (rv && lane < 32) {
-      const float4 out = MODE == MODE_DRAFT ? make_float4(run_m, run_s, best, __int_as_float(best_c))
-                                            : make_float4(mass, 0.f, best, __int_as_float(best_c));
-      a.part[(size_t)b * G + g] = out;
+    if (MODE == MODE_DRAFT) {
+      if (rv && lane < 32) a.part[(size_t)b * G + g] = make_float4(run_m, run_s, best, __int_as_float(best_c));
+    } else {
+      const double R_g = halves32_sum_d(Rs), QA_g = halves32_sum_d(QAs);
+      const double Zp_g = halves32_sum_d(Zps), Zq_g = halves32_sum_d(Zqs);
+      if (rv && lane < 32) {
+        a.part[(size_t)b * G + g] = make_float4((float)R_g, (float)QA_g, best, __int_as_float(best_c));
+        a.zpart[(size_t)b * G + g] = make_float2((float)Zp_g, (float)Zq_g);
+      }
     }
   }
 }
@@ -753,8 +786,9 @@ template <int R>
 struct DraftUnit {
   using T = DraftTiles<R>;
   static constexpr int kPrefetch = DSPARK_DRAFT_PREFETCH;  // K-steps of A fragments read ahead
+  template <int D = kPrefetch>
   __device__ __forceinline__ static void mma(const unsigned char* wtile, const bf16x8_t* bfrag, f32x16_t* acc) {
-    constexpr int S = T::kSteps, M = T::kMt, D = kPrefetch;
+    constexpr int S = T::kSteps, M = T::kMt;
     bf16x8_t af[D + 1][M];
 #pragma unroll
     for (int t = 0; t < D && t < S; ++t)
@@ -1059,8 +1093,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_draft_first(StreamArgs a) {
 // come from the fragment-ordered region that the acceptance kernel fills
 // (zeros for bonus rows, whose q is 0).
 struct VerifyRowState {
-  float mass, best, cm, cs;
+  float best, cm, cs;
   int best_c;
+  double R, QA, Zp, Zq;  // residual rows: sums of r, qa, p^ and q^ over this lane's entries
 };
 
 template <int R>
@@ -1167,6 +1202,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
     int kpos = 1;
     uint32_t purpose = kBonusChunk;
     float lsq2 = INFINITY, lsp2 = 0.f;  // a bonus row: q = exp2(-inf) = 0
+    float dlp = -INFINITY;              // lsp2 - lsq2 (a bonus row: every weight is p^)
     uint32_t zoff = VerifyDma<R>::kOutOfRange;  // this lane's draft-logit row (residual rows only)
     if (rv) {
       const int ks = a.job[b];
@@ -1176,6 +1212,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
         purpose = kResidChunk;
         lsq2 = a.lse_q[(size_t)b * K + ks - 1] * kLog2e;
         lsp2 = a.lse_p[(size_t)b * K + ks - 1] * kLog2e;
+        dlp = lsp2 - lsq2;
         zoff = (uint32_t)(((size_t)prow * K + (ks - 1)) * V * 2);
       } else {
         int nb = a.n_sched[b];
@@ -1203,13 +1240,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
       for (int t = 0; t < T::kSteps; ++t) bfrag[t] = src[t * 64];
     }
     __builtin_amdgcn_sched_barrier(0);
-    u32x4_t zA[4], zB[4];
+    u32x4_t zA[4];  // this lane's draft logits of the current unit (loaded after the previous unit's epilogue)
     dma.stage(buf0, tr, wr, unit_v0(0), wave);
     zload(0, zA);
     __builtin_amdgcn_sched_barrier(0);
 
     VerifyRowState st;
-    st.mass = 0.f;
+    st.R = st.QA = st.Zp = st.Zq = 0.0;
     st.best = -INFINITY;
     st.cm = -INFINITY;
     st.cs = 0.f;
@@ -1234,73 +1271,86 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
         mask_tail<T>(cur, v0, V, tid);
         barrier_lds_only();
       }
+      // the Markov term from zero: accumulated at its own small magnitude, the
+      // draft logits added once, in the epilogue (the residual is sensitive to
+      // a rounding at the logits' magnitude at every step of the contraction)
       f32x16_t acc[T::kMt];
 #pragma unroll
-      for (int mt = 0; mt < T::kMt; ++mt) {
-        const uint32_t w[8] = {zc[2 * mt][0], zc[2 * mt][1], zc[2 * mt][2], zc[2 * mt][3],
-                               zc[2 * mt + 1][0], zc[2 * mt + 1][1], zc[2 * mt + 1][2], zc[2 * mt + 1][3]};
+      for (int mt = 0; mt < T::kMt; ++mt)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          acc[mt][2 * i] = bf16_lo(w[i]);
-          acc[mt][2 * i + 1] = bf16_hi(w[i]);
-        }
-      }
-      D::mma(cur + abase, bfrag, acc);
+        for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+      D::template mma<1>(cur + abase, bfrag, acc);  // A fragments one K-step ahead (registers are short here)
       __builtin_amdgcn_sched_barrier(0);
       dma.stage_w(nxt, wr, unit_v0(u + 1), wave);
-      zload(u + 1, zn);
       __builtin_amdgcn_sched_barrier(0);
-      float tz[T::kMt][16];
-#pragma unroll
-      for (int mt = 0; mt < T::kMt; ++mt) {
+      // this lane's 16 target logits of M-tile mt, read from the tile when needed
+      // (the 32 of a unit are never all held in registers)
+      auto tload = [&](int mt, float (&t)[16]) {
         const int s0 = (mt * 32 + 16 * h) * 2 / 16;
         const uint4 x = *reinterpret_cast<const uint4*>(cur + T::z_off(prow, s0));
         const uint4 y = *reinterpret_cast<const uint4*>(cur + T::z_off(prow, s0 + 1));
         const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          tz[mt][2 * i] = bf16_lo(w[i]);
-          tz[mt][2 * i + 1] = bf16_hi(w[i]);
+          t[2 * i] = bf16_lo(w[i]);
+          t[2 * i + 1] = bf16_hi(w[i]);
         }
-      }
-      // One formula for both kinds of row: d = max(2^(t s - o) - 2^(q s - lq), 0)
-      // with t the target and q the draft logit.  A residual row: o and lq are
-      // the log2 partitions, so d is the residual mass of the entry.  A bonus
-      // row: lq = +inf (no draft term) and o = the unit's maximum, so d is the
-      // target weight relative to that maximum, merged into the chunk's
-      // log-partition once per unit.  Entries past V hold -inf targets: d = 0.
+      };
+      // One formula for both kinds of row, resid_entry with t the target, z the
+      // draft logit and bias the Markov term.  A residual row: o and lq are the
+      // log2 partitions, so r is the residual weight of the entry.  A bonus row:
+      // lq = +inf (no draft term), dlp = -inf and o = the unit's maximum, so r
+      // is the target weight relative to that maximum, merged into the chunk's
+      // log-partition once per unit.  Entries past V hold -inf targets and draft
+      // logits: every weight 0.
+      // draft logit of entry i of M-tile mt (residual rows; zeros for a bonus row), -inf past V
+      const bool ragged = v0 + T::kUnit > V;
+      auto zl = [&](int mt, int i) {
+        const uint32_t w = zc[2 * mt + (i >> 3)][(i >> 1) & 3];
+        const float z = (i & 1) ? bf16_hi(w) : bf16_lo(w);
+        return ragged && v0 + mt * 32 + 16 * h + i >= V ? -INFINITY : z;
+      };
       float off = lsp2, mb = -INFINITY;
       if (any_bonus) {
         float m = -INFINITY;
 #pragma unroll
-        for (int mt = 0; mt < T::kMt; ++mt)
+        for (int mt = 0; mt < T::kMt; ++mt) {
+          float t[16];
+          tload(mt, t);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) m = fmaxf(m, tz[mt][i]);
+          for (int i = 0; i < 16; ++i) m = fmaxf(m, t[i]);
+        }
         m = halves32_max(m);
         mb = m * scale2;
         if (!resid) off = m == -INFINITY ? 0.f : mb;
       }
-      float rs = 0.f;
+      ResidSums sums;
+      sums.clear();
 #pragma unroll
-      for (int mt = 0; mt < T::kMt; ++mt)
+      for (int mt = 0; mt < T::kMt; ++mt) {
+        float t[16];
+        tload(mt, t);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pp = __builtin_amdgcn_exp2f(fmaf(tz[mt][i], scale2, -off));
-          const float qq = __builtin_amdgcn_exp2f(fmaf(acc[mt][i], scale2, -lsq2));
-          rs += fmaxf(pp - qq, 0.f);
-        }
+        for (int i = 0; i < 16; ++i) sums.add(i, resid_entry(t[i], zl(mt, i), acc[mt][i], scale2, off, lsq2, dlp));
+      }
+      const float rs = ResidSums::fold(sums.r);
       if (any_bonus) {
         const float sb = halves32_sum(rs);
         if (!resid) lse2_merge(st.cm, st.cs, mb, sb);
       }
-      if (resid) st.cs += rs;
+      if (resid) {
+        st.cs += rs;
+        st.R += (double)rs;
+        st.QA += (double)ResidSums::fold(sums.qa);
+        st.Zp += (double)ResidSums::fold(sums.p);
+        st.Zq += (double)ResidSums::fold(sums.q);
+      }
       if ((u & (T::kUnitsPerChunk - 1)) == T::kUnitsPerChunk - 1) {  // chunk closes
         const int c = c_begin + u / T::kUnitsPerChunk;
         const float gum = cg.get(a.key, b, kpos, c, h, purpose);
         float score;
         if (resid) {
           const float rc = halves32_sum(st.cs);
-          st.mass += rc;
           score = rc > 0.f ? logf(rc) + gum : -INFINITY;
         } else {
           score = st.cs > 0.f ? (st.cm + log2f(st.cs)) * kLn2 + gum : -INFINITY;
@@ -1312,16 +1362,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
         st.cm = -INFINITY;
         st.cs = 0.f;
       }
+      // the next unit's draft logits once this unit's are consumed (one
+      // register set for both)
+      zload(u + 1, zn);
     };
     // the first step is peeled (the fragments are first used outside the loop)
-    step(0, buf0, buf1, zA, zB);
+    step(0, buf0, buf1, zA, zA);
     for (int u = 1; u < nunits; u += 2) {
-      step(u, buf1, buf0, zB, zA);
-      step(u + 1, buf0, buf1, zA, zB);
+      step(u, buf1, buf0, zA, zA);
+      step(u + 1, buf0, buf1, zA, zA);
     }
     wait_vmem();         // the dummy stages have landed
     barrier_lds_only();  // the next pass restages the ring and the row offsets
-    if (rv && lane < 32) a.part[(size_t)b * G + g] = make_float4(st.mass, 0.f, st.best, __int_as_float(st.best_c));
+    const double R_g = halves32_sum_d(st.R), QA_g = halves32_sum_d(st.QA);
+    const double Zp_g = halves32_sum_d(st.Zp), Zq_g = halves32_sum_d(st.Zq);
+    if (rv && lane < 32) {
+      a.part[(size_t)b * G + g] = make_float4((float)R_g, (float)QA_g, st.best, __int_as_float(st.best_c));
+      a.zpart[(size_t)b * G + g] = make_float2((float)Zp_g, (float)Zq_g);
+    }
   }
 }
 

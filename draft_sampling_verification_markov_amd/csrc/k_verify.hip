@@ -344,28 +344,40 @@ template <typename ZT, typename WT>
 __global__ __launch_bounds__(256) void k_finish(VerifyArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K, V = a.V;
-  __shared__ float s_f[4], s_best[4];
+  __shared__ float s_best[4];
   __shared__ int s_idx[4];
+  __shared__ double s_d[4][4];
   __shared__ int s_y;
-  __shared__ float s_mass;
+  __shared__ double s_R, s_mass;
   __shared__ int s_cstar;
 
-  // merge the partials of the resample pass
-  float mass = 0.f, best = -INFINITY;
+  // merge the partials of the resample pass: residual sums (float64), winning chunk
+  double R = 0.0, QA = 0.0, Zp = 0.0, Zq = 0.0;
+  float best = -INFINITY;
   int bc = 0x7fffffff;
   for (int i = tid; i < a.G; i += 256) {
     const float4 p = a.part[(size_t)b * a.G + i];
-    mass += p.x;
+    const float2 z = a.zpart[(size_t)b * a.G + i];
+    R += (double)p.x;
+    QA += (double)p.y;
+    Zp += (double)z.x;
+    Zq += (double)z.y;
     const int pc = __float_as_int(p.w);
     if (better(p.z, pc, best, bc)) {
       best = p.z;
       bc = pc;
     }
   }
-  mass = wave_sum(mass);
+  R = wave_sum_d(R);
+  QA = wave_sum_d(QA);
+  Zp = wave_sum_d(Zp);
+  Zq = wave_sum_d(Zq);
   wave_argmax(best, bc);
   if (lane == 0) {
-    s_f[wave] = mass;
+    s_d[wave][0] = R;
+    s_d[wave][1] = QA;
+    s_d[wave][2] = Zp;
+    s_d[wave][3] = Zq;
     s_best[wave] = best;
     s_idx[wave] = bc;
   }
@@ -378,7 +390,10 @@ __global__ __launch_bounds__(256) void k_finish(VerifyArgs a) {
         Bm = s_best[w];
         C0 = s_idx[w];
       }
-    s_mass = s_f[0] + s_f[1] + s_f[2] + s_f[3];
+    double t[4];
+    for (int j = 0; j < 4; ++j) t[j] = (s_d[0][j] + s_d[1][j]) + (s_d[2][j] + s_d[3][j]);
+    s_R = t[0];
+    s_mass = resid_mass_normalised(t[0], t[1], t[2], t[3]);
     s_cstar = (Bm == -INFINITY) ? -1 : C0;
   }
   __syncthreads();
@@ -392,7 +407,7 @@ __global__ __launch_bounds__(256) void k_finish(VerifyArgs a) {
   if (kstar > 0) {
     const int k0 = kstar - 1;
     const ZT* trow = Zt + ((size_t)b * (K + 1) + k0) * V;
-    if (s_mass > 0.f && cstar >= 0) {
+    if (s_R > 0.0 && cstar >= 0) {
       const ZT* zrow = static_cast<const ZT*>(a.Z) + ((size_t)b * K + k0) * V;
       const int prev = clamp_id(k0 == 0 ? a.anchor[b] : a.tok[(size_t)b * K + k0 - 1], V);
       const int j = tid >> 1, h = tid & 1;
@@ -412,9 +427,8 @@ __global__ __launch_bounds__(256) void k_finish(VerifyArgs a) {
       float sc = -INFINITY;
       int idx = 0x7fffffff;
       if (h == 0 && inside) {
-        const float q = expf((logit_at<ZT>(zrow, v) + dot) * a.inv_T - a.lse_q[(size_t)b * K + k0]);
-        const float p = expf(logit_at<ZT>(trow, v) * a.inv_T - a.lse_p[(size_t)b * K + k0]);
-        const float r = fmaxf(p - q, 0.f);
+        const float lq2 = a.lse_q[(size_t)b * K + k0] * kLog2e, lp2 = a.lse_p[(size_t)b * K + k0] * kLog2e;
+        const float r = resid_entry(logit_at<ZT>(trow, v), logit_at<ZT>(zrow, v), dot, a.scale2, lp2, lq2, lp2 - lq2).r;
         if (r > 0.f) {
           sc = logf(r) + gumbel_from_word(draw_word(a.key, (uint32_t)v, (uint32_t)b, (uint32_t)kstar, kResidElem));
           idx = v;
@@ -483,7 +497,7 @@ __global__ __launch_bounds__(256) void k_finish(VerifyArgs a) {
   if (tid == 0) {
     a.n_acc[b] = acc;
     a.next_anchor[b] = y;
-    a.resid_mass[b] = kstar > 0 ? s_mass : __int_as_float(0x7fc00000);
+    a.resid_mass[b] = kstar > 0 ? (float)s_mass : __int_as_float(0x7fc00000);
   }
 }
 
@@ -502,8 +516,9 @@ __global__ __launch_bounds__(256) void k_finish_b16(VerifyArgs a) {
   static_assert(NP * RG == kChunk, "one chunk of rows over the workgroup");
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K, V = a.V;
-  __shared__ float s_f[4], s_best[4];
+  __shared__ float s_best[4];
   __shared__ int s_idx[4];
+  __shared__ double s_d[4][4];
   __shared__ __attribute__((aligned(16))) float s_part[kChunk * STR];
   const int c = tid % PR, grp = tid / PR;
 
@@ -511,16 +526,25 @@ __global__ __launch_bounds__(256) void k_finish_b16(VerifyArgs a) {
   int nb = a.n_sched[b];
   nb = nb < 0 ? 0 : (nb > K ? K : nb);
   float4 p = a.part[(size_t)b * a.G + (tid < a.G ? tid : 0)];
-  if (tid >= a.G) p = make_float4(0.f, 0.f, -INFINITY, 0.f);
+  float2 zs = a.zpart[(size_t)b * a.G + (tid < a.G ? tid : 0)];
+  if (tid >= a.G) {
+    p = make_float4(0.f, 0.f, -INFINITY, 0.f);
+    zs = make_float2(0.f, 0.f);
+  }
   const uint4 ep = a.efrag[((size_t)(b >> 5) * (R >> 4) + (c >> 1)) * 64 + (b & 31) + 32 * (c & 1)];
 
-  // merge the partials of the resample pass: residual mass, winning chunk
-  float mass = wave_sum(p.x), best = p.z;
+  // merge the partials of the resample pass: residual sums (float64), winning chunk
+  const double Rw = wave_sum_d((double)p.x), QAw = wave_sum_d((double)p.y);
+  const double Zpw = wave_sum_d((double)zs.x), Zqw = wave_sum_d((double)zs.y);
+  float best = p.z;
   int bc = __float_as_int(p.w);
   if (tid >= a.G) bc = 0x7fffffff;
   wave_argmax(best, bc);
   if (lane == 0) {
-    s_f[wave] = mass;
+    s_d[wave][0] = Rw;
+    s_d[wave][1] = QAw;
+    s_d[wave][2] = Zpw;
+    s_d[wave][3] = Zqw;
     s_best[wave] = best;
     s_idx[wave] = bc;
   }
@@ -532,7 +556,9 @@ __global__ __launch_bounds__(256) void k_finish_b16(VerifyArgs a) {
       Bm = s_best[w];
       C0 = s_idx[w];
     }
-  const float tot_mass = (s_f[0] + s_f[1]) + (s_f[2] + s_f[3]);
+  double tot[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) tot[j] = (s_d[0][j] + s_d[1][j]) + (s_d[2][j] + s_d[3][j]);
   const int cstar = (Bm == -INFINITY || C0 < 0 || C0 * kChunk >= V) ? -1 : C0;
   __syncthreads();  // s_best / s_idx are reused below (and by full_row_draw)
   const uint16_t* Zt = static_cast<const uint16_t*>(a.Zt);
@@ -546,7 +572,7 @@ __global__ __launch_bounds__(256) void k_finish_b16(VerifyArgs a) {
   if (kstar > 0) {
     const int k0 = kstar - 1;
     const uint16_t* trow = Zt + ((size_t)b * (K + 1) + k0) * V;
-    if (tot_mass > 0.f && cstar >= 0) {
+    if (tot[0] > 0.0 && cstar >= 0) {
       const int nrow = V - v0 < kChunk ? V - v0 : kChunk;
       const uint16_t* blk = static_cast<const uint16_t*>(a.Wt) + (size_t)v0 * R;
       uint4 w[NP];
@@ -558,7 +584,7 @@ __global__ __launch_bounds__(256) void k_finish_b16(VerifyArgs a) {
       const uint16_t* zrow = static_cast<const uint16_t*>(a.Z) + ((size_t)b * K + k0) * V;
       const float z = bf16_to_f32(zrow[r < nrow ? v : v0]);
       const float zt = bf16_to_f32(trow[r < nrow ? v : v0]);
-      const float lq = a.lse_q[(size_t)b * K + k0], lp = a.lse_p[(size_t)b * K + k0];
+      const float lq2 = a.lse_q[(size_t)b * K + k0] * kLog2e, lp2 = a.lse_p[(size_t)b * K + k0] * kLog2e;
       const float gum = gumbel_from_word(draw_word(a.key, (uint32_t)v, (uint32_t)b, (uint32_t)kstar, kResidElem));
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
@@ -593,9 +619,7 @@ __global__ __launch_bounds__(256) void k_finish_b16(VerifyArgs a) {
 #pragma unroll
           for (int j = 0; j < PR; ++j) dot += s_part[r * STR + j];
         }
-        const float q = expf((z + dot) * a.inv_T - lq);
-        const float pp = expf(zt * a.inv_T - lp);
-        const float rr = fmaxf(pp - q, 0.f);
+        const float rr = resid_entry(zt, z, dot, a.scale2, lp2, lq2, lp2 - lq2).r;
         if (rr > 0.f) {
           sc = logf(rr) + gum;
           idx = v;
@@ -661,7 +685,7 @@ __global__ __launch_bounds__(256) void k_finish_b16(VerifyArgs a) {
   if (tid == 0) {
     a.n_acc[b] = acc;
     a.next_anchor[b] = y;
-    a.resid_mass[b] = kstar > 0 ? tot_mass : __int_as_float(0x7fc00000);
+    a.resid_mass[b] = kstar > 0 ? (float)resid_mass_normalised(tot[0], tot[1], tot[2], tot[3]) : __int_as_float(0x7fc00000);
   }
 }
 

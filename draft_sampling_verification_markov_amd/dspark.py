@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdspark.so")
 
-OK, E_INVALID, E_DTYPE, E_UNSUPPORTED, E_WORKSPACE, E_POINTER, E_LAUNCH = 0, -1, -2, -3, -4, -5, -6
+OK, E_INVALID, E_DTYPE, E_UNSUPPORTED, E_WORKSPACE, E_LAUNCH, E_POINTER = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
 _DT = {"f32": F32, "bf16": BF16}
 _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}

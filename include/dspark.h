@@ -84,8 +84,8 @@ typedef enum {
   DSPARK_E_DTYPE = -2,        /* a dtype code is not a dspark_dtype */
   DSPARK_E_UNSUPPORTED = -3,  /* valid, but no kernel is built for it (e.g. r = 48) */
   DSPARK_E_WORKSPACE = -4,    /* workspace null, misaligned or smaller than required */
-  DSPARK_E_POINTER = -5,      /* a required pointer is null or misaligned */
-  DSPARK_E_LAUNCH = -6        /* the runtime rejected a kernel launch */
+  DSPARK_E_LAUNCH = -5,       /* the runtime rejected a kernel launch */
+  DSPARK_E_POINTER = -6       /* a required pointer is null or misaligned (appended after the five codes above) */
 } dspark_status;
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
@@ -103,7 +103,9 @@ typedef struct {
  * Host-only: makes no HIP call. */
 size_t dspark_workspace_bytes(const dspark_problem* P);
 
-/* Static, NUL-terminated description of a status code. */
+/* Static, NUL-terminated description of a status code.  Takes an int so that a
+ * code read back as an integer (from another language, or out of range) is
+ * accepted; values that are not a dspark_status give "unknown status". */
 const char* dspark_status_string(int status);
 
 /*
@@ -132,23 +134,6 @@ dspark_status dspark_draft(const dspark_problem* P,
                            int32_t* draft_tok, float* draft_logq, float* draft_lse,
                            float* conf, float* surv,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
-
-/*
- * dspark_draft_timed -- dspark_draft, plus instrumentation: events[2i] and
- * events[2i+1] (caller-created HIP events, 2*K of them) are recorded on
- * `stream` immediately before and after the vocabulary-stream kernel of draft
- * step i+1, so that the caller can read that kernel's duration with
- * hipEventElapsedTime.  Same inputs, outputs and errors as dspark_draft;
- * DSPARK_E_POINTER if events is NULL.
- */
-dspark_status dspark_draft_timed(const dspark_problem* P,
-                                 const void* Z, const void* E, const void* Wt, const void* h,
-                                 const float* w_conf, float b_conf, const float* tau,
-                                 const int32_t* anchor,
-                                 int32_t* draft_tok, float* draft_logq, float* draft_lse,
-                                 float* conf, float* surv,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                 hipEvent_t* events);
 
 /*
  * dspark_schedule -- choose n_b, the number of draft positions of request b to

@@ -3,13 +3,9 @@
 Decision rule: a GPU decision (token, acceptance, scheduled length) may differ
 from the oracle's only where the oracle's decision margin is below 1e-4, and
 such mismatches must stay below 0.01% of the decisions of their kind.
-Floating-point outputs: probabilities (q(x), p(x)) within 1e-5 relative,
-confidences and survivals within 1e-6 absolute.  The residual mass
-sum_v max(0, p_v - q_v) is within 1e-5 relative plus RESID_ATOL absolute: each
-term is a difference of two fp32 probabilities, each off by about 1e-6 of
-itself (rounding and the fp32 log-partitions), so the sum can be off by 1e-6
-times sum_v (p_v + q_v) = 2e-6 however small the mass (the cancellation where
-p_v is close to q_v); RESID_ATOL doubles that.
+Floating-point outputs: probabilities (q(x), p(x)) and the residual mass
+sum_v max(0, p_v - q_v) within 1e-5 relative, confidences and survivals within
+1e-6 absolute.
 """
 from __future__ import annotations
 
@@ -19,7 +15,6 @@ MARGIN = 1e-4
 MISMATCH_RATE = 1e-4
 PROB_RTOL = 1e-5
 CONF_ATOL = 1e-6
-RESID_ATOL = 4e-6
 
 
 def check_decisions(kind: str, gpu, ref, margin) -> int:
@@ -67,12 +62,18 @@ def cycle_check(cfg, g, ref, slack=None) -> dict:
 
     Nothing the GPU produced is fed to the oracle: the two cycles run
     independently and are compared stage by stage.  The first token of a request
-    that differs must be a decision of oracle margin below MARGIN; the request's
-    later positions are then not compared (its prefixes differ), and neither is
-    anything downstream of the whole-batch schedule.  ``slack`` (B x K, the RNN
-    head's bound on logit shifts from bf16 code flips) widens the margins and the
-    probability tolerances of the draft distribution.
-    Returns counts of low-margin differences per decision kind."""
+    that differs must be a decision of oracle margin below MARGIN; that
+    request's later positions, its schedule and its verification are then not
+    compared (its prefixes differ), while every other request still is.  The
+    whole-batch schedule must equal the oracle's unless the oracle's scheduler
+    margin or survival cut gap is below MARGIN, or a draft token differed
+    (then the survivals the schedule ranks differ too); where it differs, the
+    requests whose scheduled lengths differ leave the verification comparison.
+    ``slack`` (B x K, the RNN head's bound on logit shifts from bf16 code
+    flips) widens the margins and the probability tolerances of the draft
+    distribution.  Returns counts of low-margin differences per decision kind
+    and of the requests each stage compared (asserted to cover every request
+    that no excused difference touched)."""
     B, K = cfg.B, cfg.K
     d = ref["draft"]
     sl = np.zeros((B, K)) if slack is None else np.asarray(slack, np.float64)
@@ -94,21 +95,33 @@ def cycle_check(cfg, g, ref, slack=None) -> dict:
         err = np.abs(g[key].astype(np.float64) - ref[key])[prev_ok]
         assert (err <= CONF_ATOL).all(), f"{key}: worst {err.max():.3e}"
     assert (np.diff(g["surv"], axis=1) <= 0).all(), "GPU survivals must be non-increasing"
-    if counts["draft"]:
-        return counts
+    clean = prefix.all(axis=1)                                            # requests with every token equal
+    counts["draft_compared_requests"] = int(clean.sum())
+    assert counts["draft_compared_requests"] == B - int(first.any(axis=1).sum())
+
     sc = ref["sched"]
     n_ref = np.array(sc["n"])
-    if not (g["n_sched"] == n_ref).all():
-        assert sc["margin"] < MARGIN, f"schedule differs at margin {sc['margin']:.3e}"
+    n_gpu = np.asarray(g["n_sched"])
+    sched_same = n_gpu == n_ref
+    if sched_same.all():
+        counts["sched"] = 0
+        assert int(g["n_total"][0]) == sc["N"]
+    else:
+        low = sc["margin"] < MARGIN or sc["cut_gap"] < MARGIN
+        assert low or counts["draft"] > 0, (f"schedule differs at margin {sc['margin']:.3e}, cut gap "
+                                             f"{sc['cut_gap']:.3e} with no draft token differing")
         counts["sched"] = 1
-        return counts
-    counts["sched"] = 0
-    assert int(g["n_total"][0]) == sc["N"]
+    counts["sched_requests_differing"] = int((~sched_same).sum())
+
+    comp = clean & sched_same                                             # requests verified on equal inputs
     acc_diff = emit_diff = 0
-    for b in range(B):
+    compared = 0
+    resid_worst = 0.0
+    for b in np.flatnonzero(comp):
         v = ref["verify"][b]
-        nb = int(g["n_sched"][b])
+        nb = int(n_gpu[b])
         s_b = float(sl[b].max()) if K else 0.0
+        compared += 1
         if nb:
             r = np.abs(np.expm1(g["logp"][b, :nb].astype(np.float64) - v["logp"][:nb]))
             assert (r <= PROB_RTOL).all(), f"target p(x) of request {b}: worst {r.max():.3e}"
@@ -120,8 +133,10 @@ def cycle_check(cfg, g, ref, slack=None) -> dict:
         if v["kind"] == "bonus":
             assert np.isnan(g["resid_mass"][b])
         else:
-            tol = PROB_RTOL * abs(v["mass"]) + RESID_ATOL + 2 * sl[b, v["k_star"] - 1]
+            tol = PROB_RTOL * abs(v["mass"]) + 2 * sl[b, v["k_star"] - 1]
             assert abs(float(g["resid_mass"][b]) - v["mass"]) <= tol, (b, g["resid_mass"][b], v["mass"])
+            if v["mass"] > 0:
+                resid_worst = max(resid_worst, abs(float(g["resid_mass"][b]) / v["mass"] - 1))
         if int(g["next_anchor"][b]) != v["y"]:
             assert v["token_margin"] < MARGIN + 2 * s_b, (b, g["next_anchor"][b], v["y"], v["token_margin"])
             emit_diff += 1
@@ -130,5 +145,8 @@ def cycle_check(cfg, g, ref, slack=None) -> dict:
         row[:len(v["tokens"])] = v["tokens"]
         assert (g["out_tok"][b] == row).all(), (b, g["out_tok"][b], row)
     counts["accept"], counts["emit"] = acc_diff, emit_diff
+    counts["verify_compared_requests"] = compared
+    counts["resid_mass_rel_worst"] = resid_worst
+    assert compared == int(comp.sum()) and compared >= 1, counts
     assert acc_diff <= MISMATCH_RATE * B and emit_diff <= MISMATCH_RATE * B, counts
     return counts

@@ -10,6 +10,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dspark.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "dspark_instr.h")]
 
 
 @pytest.fixture(scope="module")
@@ -22,17 +23,32 @@ def ds():
     return dspark
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(headers=HEADERS):
+    text = "".join(open(h).read() for h in headers)
     return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == sorted(["dspark_draft", "dspark_draft_timed", "dspark_schedule", "dspark_schedule_async",
-                                  "dspark_schedule_fixed", "dspark_schedule_threshold", "dspark_sts_fit",
-                                  "dspark_sts_workspace_bytes", "dspark_verify", "dspark_workspace_bytes",
-                                  "dspark_status_string", "dspark_rnn_workspace_bytes", "dspark_draft_rnn",
-                                  "dspark_verify_rnn"])
+    assert _declared([HEADER]) == sorted(["dspark_draft", "dspark_schedule", "dspark_schedule_async",
+                                          "dspark_schedule_fixed", "dspark_schedule_threshold", "dspark_sts_fit",
+                                          "dspark_sts_workspace_bytes", "dspark_verify", "dspark_workspace_bytes",
+                                          "dspark_status_string", "dspark_rnn_workspace_bytes", "dspark_draft_rnn",
+                                          "dspark_verify_rnn"])
+    # instrumentation, outside the step's contract
+    assert _declared([HEADERS[1]]) == ["dspark_draft_timed"]
+
+
+def test_status_codes_are_the_contract(ds):
+    # the five codes of the boundary's contract keep their values; the pointer
+    # error is appended after them
+    text = open(HEADER).read()
+    codes = {m.group(1): int(m.group(2)) for m in re.finditer(r"DSPARK_(OK|E_[A-Z]+)\s*=\s*(-?\d+)", text)}
+    assert codes == {"OK": 0, "E_INVALID": -1, "E_DTYPE": -2, "E_UNSUPPORTED": -3, "E_WORKSPACE": -4,
+                     "E_LAUNCH": -5, "E_POINTER": -6}
+    assert (ds.OK, ds.E_INVALID, ds.E_DTYPE, ds.E_UNSUPPORTED, ds.E_WORKSPACE, ds.E_LAUNCH, ds.E_POINTER) == \
+        (0, -1, -2, -3, -4, -5, -6)
+    assert ds.status_string(-5) == "kernel launch failed"
+    assert ds.status_string(-6) == "null or misaligned pointer argument"
 
 
 def test_library_exports_every_declared_symbol(ds):
@@ -45,7 +61,8 @@ def test_library_exports_every_declared_symbol(ds):
 
 
 def test_header_compiles_as_c():
-    src = '#include "dspark.h"\nint main(void){ dspark_problem p; (void)p; return (int)sizeof(dspark_problem); }\n'
+    src = ('#include "dspark.h"\n#include "dspark_instr.h"\n'
+           'int main(void){ dspark_problem p; (void)p; return (int)sizeof(dspark_problem); }\n')
     r = subprocess.run(["gcc", "-x", "c", "-std=c99", "-fsyntax-only", "-I", os.path.join(ROOT, "include"),
                         "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", "-"], input=src, text=True,
                        capture_output=True)

@@ -12,7 +12,7 @@ whose codes do differ is bounded by
 (step_j the bf16 spacing at the entry, doubled to cover a binade edge),
 and every comparison downstream of the projection widens by it: a decision may
 differ only where its oracle margin is below 1e-4 + 2 amb; log q within 1e-5
-relative plus 2 amb; the residual mass within 1e-5 relative plus 4e-6 plus 2 amb.  Where
+relative plus 2 amb; the residual mass within 1e-5 relative plus 2 amb.  Where
 no code differs (amb = 0) these are the Markov head's bounds.  States are
 compared to STATE_ATOL absolute (about three times the largest error seen:
 3.3e-6); confidences and survivals to 1e-6."""

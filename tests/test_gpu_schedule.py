@@ -127,3 +127,76 @@ def test_schedule_baselines(lib, B, K, ties):
         assert int(n_total.item()) == ref["N"], theta
     with pytest.raises(RuntimeError):
         dspark.schedule_fixed(P, K + 1, n_sched, n_total)
+
+
+def _linear_table(B, K, slope):
+    return (5.0 + slope * np.arange(B * (K + 1) + 1)).astype(np.float32)
+
+
+def _stair_table(B, K, delta, width=64):
+    N = np.arange(B * (K + 1) + 1)
+    return (1.0 + delta * np.maximum(N - B, 0) // width).astype(np.float32)
+
+
+def _mid_order_table(B, K, S, kind):
+    """A table whose first drop lands near the middle of the candidate order, away
+    from a tie: the parameter (slope, or step height) is the geometric middle of
+    the interval over which the oracle takes the same number of candidates as at
+    the parameter that splits the order in half (bisection on the oracle, log scale)."""
+    make = _linear_table if kind == "linear" else _stair_table
+    n = B * K
+    S64 = S.astype(np.float64)
+
+    def taken(x):
+        return osched.schedule(S64, make(B, K, x).astype(np.float64))["taken"]
+
+    def edge(lo, hi, keep_lo):
+        # bisect [lo, hi] for the point where keep_lo(taken) stops holding
+        for _ in range(50):
+            mid = (lo * hi) ** 0.5
+            lo, hi = (mid, hi) if keep_lo(taken(mid)) else (lo, mid)
+        return lo, hi
+
+    _, x0 = edge(1e-9, 10.0, lambda t: t > n // 2)
+    t0 = taken(x0)
+    a, _ = edge(1e-9, x0, lambda t: t > t0)           # below a more are taken
+    _, b = edge(x0, 10.0, lambda t: t >= t0)          # above b fewer are taken
+    return make(B, K, (a * b) ** 0.5)
+
+
+GREEDY_CASES = [(256, 16, "linear"), (256, 16, "stair"), (512, 32, "linear"), (512, 32, "stair"),
+                (1024, 32, "linear"), (1024, 32, "stair")]
+
+
+@pytest.mark.parametrize("B,K,kind", GREEDY_CASES, ids=[f"B{b}_K{k}_{t}" for b, k, t in GREEDY_CASES])
+def test_schedule_greedy_mid_order(lib, B, K, kind):
+    """Linear and staircase step-time tables whose first drop lands mid-order: the
+    greedy comparison (A + s) T[N] >= A T[N + 1] decides every candidate up to the
+    stop (the GPU sums A in float64 in a parallel prefix, the oracle in order), so
+    the whole schedule is compared exactly (margins and cut gap reported)."""
+    dspark = lib
+    n = B * K
+    S = synth.make_survivals(B, K, seed=21, ties=False)
+    T = _mid_order_table(B, K, S, kind)
+    ref = osched.schedule(S.astype(np.float64), T.astype(np.float64))
+    print(f"[gpu] schedule greedy B={B} K={K} {kind}: oracle takes {ref['taken']} of {n}, margin "
+          f"{ref['margin']:.3e}, cut gap {ref['cut_gap']:.3e}", flush=True)
+    assert n // 4 < ref["taken"] < 3 * n // 4
+    P = dspark.Problem.make(B, K, 1024, 16, 8)
+    ws = torch.empty(dspark.workspace_bytes(P), dtype=torch.uint8, device="cuda")
+    n_sched = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    n_total = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dspark.schedule(P, torch.from_numpy(S).cuda(), torch.from_numpy(T).cuda(), n_sched, n_total, ws)
+    torch.cuda.synchronize()
+    g = n_sched.cpu().numpy()
+    differ = int((g != np.array(ref["n"])).sum())
+    print(f"[gpu]   N = {int(n_total.item())} (oracle {ref['N']}); requests differing: {differ}", flush=True)
+    # Both sides evaluate every comparison in float64 on the same float32 survivals and
+    # table entries; they differ only in the order of the additions that form A (a
+    # relative difference of order n * 1e-16).  The comparisons' relative margins here
+    # are about (survival spacing) / A, 1e-9 to 1e-8, far above that: the schedule must
+    # be identical unless the oracle's margin is below 1e-12.
+    if differ or int(n_total.item()) != ref["N"]:
+        assert ref["margin"] < 1e-12, "schedule differs at a comparison margin above 1e-12"
+    else:
+        assert int(n_total.item()) == ref["N"]
