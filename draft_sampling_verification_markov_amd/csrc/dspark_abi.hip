@@ -2,6 +2,8 @@
 // kernel sequence of each call.  See include/dspark.h for the contract.
 #include <math.h>
 
+#include <mutex>
+
 #include "dspark_internal.hpp"
 
 namespace dspark {
@@ -248,6 +250,64 @@ extern "C" dspark_status dspark_schedule(const dspark_problem* P, const float* s
   const Layout L = make_layout(*P);
   if (launch_schedule(*P, surv, T_table, n_sched, n_total, at<int32_t>(workspace, L.rpart),
                       at<float>(workspace, L.sorts), at<int32_t>(workspace, L.sorti), stream) != hipSuccess)
+    return DSPARK_E_LAUNCH;
+  return DSPARK_OK;
+}
+
+// ---------------------------------------------------------------- schedule without allocation
+// The scheduler's scratch for callers that cannot allocate: a file-scope device
+// array, one copy per GPU for the life of the process, holding the partial
+// ranks (int32 [S][n], S <= 16 segments), the survivals in schedule order
+// (float [n]) and their candidate indices (int32 [n]) for up to
+// kNoAllocCandidates = 32,768 candidates (2.25 MiB).  Its device address is
+// taken once per device with hipGetSymbolAddress (host code never passes the
+// symbol itself to a kernel) and kept per device.  Nothing in it needs
+// clearing: the rank kernel writes every partial and the ordering writes
+// every slot before any read.
+namespace dspark {
+constexpr int kNoAllocCandidates = 32768;
+constexpr size_t kNoAllocRankBytes = (size_t)kSchedSegMax * kNoAllocCandidates * sizeof(int32_t);
+constexpr size_t kNoAllocScratchBytes = kNoAllocRankBytes + (size_t)kNoAllocCandidates * (sizeof(float) + sizeof(int32_t));
+constexpr int kNoAllocMaxDevices = 64;
+}  // namespace dspark
+
+static __device__ __align__(256) unsigned char scratch[dspark::kNoAllocScratchBytes];
+
+static std::mutex g_scratch_mutex;
+static unsigned char* g_scratch_ptr[dspark::kNoAllocMaxDevices];
+
+// Device address of this device's scratch (the current device), looked up once.
+static hipError_t scratch_for_current_device(unsigned char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= dspark::kNoAllocMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<unsigned char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+extern "C" dspark_status dspark_schedule_noalloc(const dspark_problem* P, const float* surv, const float* T_table,
+                                                 int32_t* n_sched, int32_t* n_total, hipStream_t stream) {
+  dspark_status st = check_problem(P);
+  if (st != DSPARK_OK) return st;
+  if ((long long)P->B * P->K > kNoAllocCandidates) return DSPARK_E_WORKSPACE;
+  if (!surv || !T_table || !n_sched || !n_total) return DSPARK_E_POINTER;
+  for (const void* q : {(const void*)surv, (const void*)T_table, (const void*)n_sched, (const void*)n_total})
+    if (!aligned(q, 4)) return DSPARK_E_POINTER;
+  (void)hipGetLastError();
+  unsigned char* ws = nullptr;
+  if (scratch_for_current_device(&ws) != hipSuccess) return DSPARK_E_LAUNCH;
+  int32_t* rpart = reinterpret_cast<int32_t*>(ws);
+  float* sorted_s = reinterpret_cast<float*>(ws + kNoAllocRankBytes);
+  int32_t* sorted_i = reinterpret_cast<int32_t*>(ws + kNoAllocRankBytes + (size_t)kNoAllocCandidates * sizeof(float));
+  if (launch_schedule(*P, surv, T_table, n_sched, n_total, rpart, sorted_s, sorted_i, stream) != hipSuccess)
     return DSPARK_E_LAUNCH;
   return DSPARK_OK;
 }

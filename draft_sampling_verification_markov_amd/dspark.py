@@ -23,7 +23,7 @@ _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 SYMBOLS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft", "dspark_draft_timed",
            "dspark_schedule", "dspark_schedule_async", "dspark_schedule_fixed", "dspark_schedule_threshold",
            "dspark_sts_workspace_bytes", "dspark_sts_fit", "dspark_verify", "dspark_rnn_workspace_bytes",
-           "dspark_draft_rnn", "dspark_verify_rnn")
+           "dspark_draft_rnn", "dspark_verify_rnn", "dspark_schedule_noalloc")
 
 
 class Problem(ctypes.Structure):
@@ -74,6 +74,8 @@ def load() -> ctypes.CDLL:
     lib.dspark_draft_timed.restype = i32
     lib.dspark_schedule.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_schedule.restype = i32
+    lib.dspark_schedule_noalloc.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.dspark_schedule_noalloc.restype = i32
     lib.dspark_schedule_async.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_schedule_async.restype = i32
     lib.dspark_sts_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -167,6 +169,14 @@ def schedule(P: Problem, surv, T_table, n_sched, n_total, workspace, stream=None
         _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
         _stream(stream))
     _check("dspark_schedule", st)
+
+
+def schedule_noalloc(P: Problem, surv, T_table, n_sched, n_total, stream=None) -> None:
+    """dspark_schedule with the library's static scratch instead of a workspace (B * K <= 32768)."""
+    st = load().dspark_schedule_noalloc(
+        ctypes.byref(P), _ptr(surv, torch.float32, "surv"), _ptr(T_table, torch.float32, "T_table"),
+        _ptr(n_sched, torch.int32, "n_sched"), _ptr(n_total, torch.int32, "n_total"), _stream(stream))
+    _check("dspark_schedule_noalloc", st)
 
 
 def schedule_async(P: Problem, surv_lag, surv, T_table, n_sched, n_total, workspace, stream=None) -> None:

@@ -155,6 +155,26 @@ dspark_status dspark_schedule(const dspark_problem* P,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dspark_schedule_noalloc -- dspark_schedule for callers that cannot allocate
+ * (code under HIP graph capture that may not call hipMalloc, tight serving
+ * loops, harnesses that forbid allocation): the same schedule, bit for bit,
+ * with no workspace argument.  Its scratch (partial ranks and the candidates in
+ * schedule order) is a static device array inside the library, 2.25 MiB per
+ * GPU, held until the process ends; the call itself allocates nothing.
+ *
+ * Limit: B * K <= 32768 candidates; larger problems return DSPARK_E_WORKSPACE
+ * (use dspark_schedule with a workspace).  Every call on one GPU shares that
+ * GPU's scratch, so calls that overlap on one GPU (concurrent streams, or
+ * threads issuing to different streams) race and give unspecified results;
+ * calls ordered on one stream, or separated by synchronisation, do not.
+ * Other arguments, outputs and errors as for dspark_schedule; DSPARK_E_LAUNCH
+ * also when the scratch's device address cannot be obtained.
+ */
+dspark_status dspark_schedule_noalloc(const dspark_problem* P,
+                                      const float* surv, const float* T_table,
+                                      int32_t* n_sched, int32_t* n_total, hipStream_t stream);
+
+/*
  * dspark_schedule_async -- the asynchronous "dynamic top-k" form of the
  * scheduler (DSpark page, Production deployment results): the verification
  * budget is sized from the confidence-head outputs of two steps earlier and

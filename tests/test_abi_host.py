@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
                                           "dspark_schedule_fixed", "dspark_schedule_threshold", "dspark_sts_fit",
                                           "dspark_sts_workspace_bytes", "dspark_verify", "dspark_workspace_bytes",
                                           "dspark_status_string", "dspark_rnn_workspace_bytes", "dspark_draft_rnn",
-                                          "dspark_verify_rnn"])
+                                          "dspark_verify_rnn", "dspark_schedule_noalloc"])
     # instrumentation, outside the step's contract
     assert _declared([HEADERS[1]]) == ["dspark_draft_timed"]
 
