@@ -260,8 +260,13 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
     src = kernel_source_hash()
     # kernel trace
     rows = _csv_rows(os.path.join(prof_dir, "trace"), "kernel_stats.csv")
-    lines = [f"# Kernel trace: {workload} workload, bench.py --main-only --steps 5 --warmup 2", "",
-             "Command (one of the sequence below; trace run first):", "", "```", PROFILE_COMMANDS, "```", "",
+    cmd = PROFILE_COMMANDS if workload == "high_concurrency" else "\n".join(
+        l.replace("bench.py --main-only", f"bench.py --config {workload} --main-only")
+        for l in PROFILE_COMMANDS.splitlines() if "--kernel-trace" in l or "summarize" in l or l.startswith("cd "))
+    if workload != "high_concurrency":
+        cmd = cmd.replace("--summarize-profiles $OUT", f"--config {workload} --summarize-profiles $OUT")
+    lines = [f"# Kernel trace: {workload} workload, bench.py --config {workload} --main-only --steps 5 --warmup 2", "",
+             "Command (one of the sequence below; trace run first):", "", "```", cmd, "```", "",
              "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---:|---:|---:|---:|---:|"]
     for r in rows:
         lines.append(f"| {_short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -272,6 +277,8 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
               "verify kernel average is at the step's own schedule."]
     with open(os.path.join(PROFILE_DIR, f"cycle_{workload}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
+    if not os.path.isdir(os.path.join(prof_dir, "fetch")):
+        return  # a kernel-trace run only (no counter passes)
     # HBM counters, scaled by what the same counters read for a plain 1 GiB copy
     fetch, write = _pmc_means(os.path.join(prof_dir, "fetch"), "FETCH_SIZE"), _pmc_means(os.path.join(prof_dir, "write"), "WRITE_SIZE")
     cf, cw = _pmc_means(os.path.join(prof_dir, "cfetch"), "FETCH_SIZE"), _pmc_means(os.path.join(prof_dir, "cwrite"), "WRITE_SIZE")

@@ -23,7 +23,8 @@ _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 SYMBOLS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft", "dspark_draft_timed",
            "dspark_schedule", "dspark_schedule_async", "dspark_schedule_fixed", "dspark_schedule_threshold",
            "dspark_sts_workspace_bytes", "dspark_sts_fit", "dspark_verify", "dspark_rnn_workspace_bytes",
-           "dspark_draft_rnn", "dspark_verify_rnn", "dspark_schedule_noalloc")
+           "dspark_draft_rnn", "dspark_verify_rnn", "dspark_schedule_noalloc",
+           "dspark_probe_draws")
 
 
 class Problem(ctypes.Structure):
@@ -74,6 +75,8 @@ def load() -> ctypes.CDLL:
     lib.dspark_draft_timed.restype = i32
     lib.dspark_schedule.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_schedule.restype = i32
+    lib.dspark_probe_draws.argtypes = [ctypes.c_uint64, vp, i32, vp, vp, i32, vp, vp, vp]
+    lib.dspark_probe_draws.restype = i32
     lib.dspark_schedule_noalloc.argtypes = [P, vp, vp, vp, vp, vp]
     lib.dspark_schedule_noalloc.restype = i32
     lib.dspark_schedule_async.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -169,6 +172,18 @@ def schedule(P: Problem, surv, T_table, n_sched, n_total, workspace, stream=None
         _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
         _stream(stream))
     _check("dspark_schedule", st)
+
+
+def probe_draws(seed: int, ctr=None, out_words=None, w=None, uniform=None, gumbel=None, stream=None) -> None:
+    """The device's Philox words of counters ctr [n][4] (uint32 as int32 tensors) and the uniform
+    and Gumbel transforms of words w [m] (instrumentation)."""
+    n = 0 if ctr is None else int(ctr.shape[0])
+    m = 0 if w is None else int(w.numel())
+    st = load().dspark_probe_draws(ctypes.c_uint64(seed), _ptr(ctr, torch.int32, "ctr"), n,
+                                   _ptr(out_words, torch.int32, "out_words"), _ptr(w, torch.int32, "w"), m,
+                                   _ptr(uniform, torch.float32, "uniform"), _ptr(gumbel, torch.float32, "gumbel"),
+                                   _stream(stream))
+    _check("dspark_probe_draws", st)
 
 
 def schedule_noalloc(P: Problem, surv, T_table, n_sched, n_total, stream=None) -> None:

@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
                                           "dspark_status_string", "dspark_rnn_workspace_bytes", "dspark_draft_rnn",
                                           "dspark_verify_rnn", "dspark_schedule_noalloc"])
     # instrumentation, outside the step's contract
-    assert _declared([HEADERS[1]]) == ["dspark_draft_timed"]
+    assert _declared([HEADERS[1]]) == ["dspark_draft_timed", "dspark_probe_draws"]
 
 
 def test_status_codes_are_the_contract(ds):
