@@ -109,20 +109,46 @@ class Hip:
             self.lib.hipEventDestroy(h)
 
 
-DOMINANT = "k_draft"   # the draft-step vocabulary stream kernel
+PERSIST_MAX_B = 48  # dspark_draft's batch limit for the persistent schedule
+
+
+def draft_persistent(cfg) -> bool:
+    """Whether dspark_draft takes the persistent draft schedule for this workload
+    (the library's rule, which dspark_draft_path reports on the GPU: bf16 logits
+    and factors, rank 256, at most 5 vocabulary chunks per workgroup, and at most
+    PERSIST_MAX_B requests)."""
+    nc = (cfg.V + 127) // 128
+    G = min(nc, 256)
+    return (cfg.logits_dtype == "bf16" and cfg.weight_dtype == "bf16" and cfg.r == 256
+            and cfg.B <= PERSIST_MAX_B and -(-nc // G) <= 5)
+
+
+DOMINANT = "k_draft_persist"  # the kernel of the draft phase (all K positions in one launch)
+DOMINANT_STEPWISE = "k_draft"  # the per-position stream kernel where the persistent one does not apply
+
+
+def dominant(cfg) -> str:
+    return DOMINANT if draft_persistent(cfg) else DOMINANT_STEPWISE
 
 
 def _profile_record(workload: str):
-    path = os.path.join(PROFILE_DIR, f"{DOMINANT}_{workload}_pmc.json")
-    if not os.path.exists(path):
+    """The counter record of the workload's dominant draft kernel (whichever
+    schedule the profile run took: the file is named for that kernel)."""
+    path = None
+    for k in (DOMINANT, DOMINANT_STEPWISE):
+        q = os.path.join(PROFILE_DIR, f"{k}_{workload}_pmc.json")
+        if os.path.exists(q):
+            path = q
+            break
+    if path is None:
         return None
     with open(path) as f:
         return json.load(f)
 
 
 def traffic_from_profile(workload: str):
-    """HBM bytes per draft-stream launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+    """HBM bytes per launch of the draft phase's dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source; else None."""
     rec = _profile_record(workload)
     if rec is None or rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
@@ -136,7 +162,7 @@ def mfma_from_profile(workload: str):
     rec = _profile_record(workload)
     if rec is None or rec.get("kernel_source_sha256") != kernel_source_hash() or not rec.get("mfma"):
         return None
-    return rec["mfma"].get(DOMINANT)
+    return rec["mfma"].get(rec.get("kernel", DOMINANT))
 
 
 def step_kernels(cfg) -> dict:
@@ -146,7 +172,9 @@ def step_kernels(cfg) -> dict:
     sched = {"k_sched_rank": 1, "k_sched_greedy_lds": 1} if n <= 8192 else \
         {"k_sched_rank": 1, "k_sched_scatter": 1, "k_sched_greedy_global": 1}
     rowlist = {} if (cfg.B <= 1024 and n <= 8192) else {"k_rowlist": 1}  # else built inside k_vlse
-    return {"k_draft_first": 1, DOMINANT: cfg.K - 1, "k_select_b16": cfg.K, "k_conf": 1, **sched, **rowlist,
+    draft = {"k_persist_init": 1, DOMINANT: 1} if draft_persistent(cfg) else \
+        {"k_draft_first": 1, DOMINANT_STEPWISE: cfg.K - 1, "k_select_b16": cfg.K}
+    return {**draft, "k_conf": 1, **sched, **rowlist,
             "k_vlse": 1, "k_accept": 1, "k_verify64": 1, "k_finish_b16": 1}
 
 
@@ -318,14 +346,15 @@ def summarize_profiles(prof_dir: str, workload: str) -> None:
         f.write("\n".join(lines) + "\n")
     per_kernel = {k: (fetch[k] * fscale + write.get(k, 0.0) * wscale) * 1024 for k in fetch
                   if k.startswith("k_")}
-    rec = {"kernel": DOMINANT, "workload": workload, "main_only": True, "commit": commit, "kernel_source_sha256": src,
+    dom = DOMINANT if DOMINANT in fetch else DOMINANT_STEPWISE
+    rec = {"kernel": dom, "workload": workload, "main_only": True, "commit": commit, "kernel_source_sha256": src,
            "all_sources_sha256": kernel_source_hash(all_sources=True), "per_kernel_bytes": per_kernel,
-           "fetch_kib_per_launch": fetch[DOMINANT], "write_kib_per_launch": write.get(DOMINANT, 0.0),
+           "fetch_kib_per_launch": fetch[dom], "write_kib_per_launch": write.get(dom, 0.0),
            "fetch_scale": fscale, "write_scale": wscale,
-           "hbm_bytes_per_launch": (fetch[DOMINANT] * fscale + write.get(DOMINANT, 0.0) * wscale) * 1024,
+           "hbm_bytes_per_launch": (fetch[dom] * fscale + write.get(dom, 0.0) * wscale) * 1024,
            "mfma": mfma,
            "source": f"profiles/cycle_{workload}_hbm_counters.md"}
-    with open(os.path.join(PROFILE_DIR, f"{DOMINANT}_{workload}_pmc.json"), "w") as f:
+    with open(os.path.join(PROFILE_DIR, f"{dom}_{workload}_pmc.json"), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
 
@@ -578,23 +607,34 @@ def main() -> int:
     if not args.main_only:
         ms_graph, ms_async, baselines, sts_line, rnn_line = secondary()
 
-    # dominant kernel: the draft-step stream kernel k_draft, timed by events the
-    # library records around each of its launches on the same stream.  Position 1
-    # runs k_draft_first (it gathers the anchors' E rows itself) and is the first
-    # launch after an idle GPU, so its interval also holds the host's launch
-    # latency: the average is taken over positions 2..K, the k_draft launches.
+    # the draft phase (every position: the persistent kernel, or the per-position
+    # stream and selection kernels), timed by two events the library records
+    # around it on its own stream
     hip = Hip()
-    n_ev = 2 * cfg.K
-    kernel_ms = []
-    for i in range(args.steps):
-        xs = sets[i % 3]
-        evs = hip.events(n_ev)
-        dspark.draft_timed(P, xs.Z, xs.E, xs.Wt, xs.h, xs.w_c, xs.b_c, xs.tau, xs.anchor,
-                           o.tok, o.logq, o.lse, o.conf, o.surv, o.workspace, evs)
-        torch.cuda.synchronize()
-        kernel_ms += [hip.elapsed_ms(evs[2 * k], evs[2 * k + 1]) for k in range(1, cfg.K)]
-        hip.destroy(evs)
-    k_ms = float(np.mean(kernel_ms))
+
+    def draft_phase_ms(path, n):
+        out = []
+        for i in range(n):
+            xs = sets[i % 3]
+            evs = hip.events(2)
+            dspark.draft_timed(P, xs.Z, xs.E, xs.Wt, xs.h, xs.w_c, xs.b_c, xs.tau, xs.anchor,
+                               o.tok, o.logq, o.lse, o.conf, o.surv, o.workspace, evs, path=path)
+            torch.cuda.synchronize()
+            out.append(hip.elapsed_ms(evs[0], evs[1]))
+            hip.destroy(evs)
+        return float(np.median(out))
+
+    k_ms = draft_phase_ms(dspark.DRAFT_AUTO, args.steps)
+    lib_path = dspark.draft_path(P)
+    assert (lib_path == dspark.DRAFT_PERSISTENT) == draft_persistent(cfg), "bench's rule differs from the library's"
+    # both schedules of the draft phase on the same inputs (the dispatch evidence)
+    schedules = {"per_position": draft_phase_ms(dspark.DRAFT_PER_POSITION, 20)}
+    try:
+        schedules["persistent"] = draft_phase_ms(dspark.DRAFT_PERSISTENT, 20)
+    except dspark.DsparkError:
+        schedules["persistent"] = None  # not applicable to this workload
+    log(f"draft phase: {schedules} ms (dspark_draft takes "
+        f"{'persistent' if lib_path == dspark.DRAFT_PERSISTENT else 'per_position'})")
 
     # final outputs of one step on set 0 for the realised schedule
     runner.run_cycle(P, sets[0], o)
@@ -607,9 +647,12 @@ def main() -> int:
     alg_bytes = cycle_bytes(cfg, N, R)
     nc = (cfg.V + 127) // 128                     # the library's stream grid: fewest workgroups
     G = -(-nc // -(-nc // 256))                    # with the busiest one's chunk count unchanged
-    launch_bytes = stream_launch_bytes(cfg)
-    launch_bytes_full = stream_launch_bytes_full_wt(cfg, G)
-    achieved = launch_bytes / (k_ms / 1e3) / 1e9
+    persistent = lib_path == dspark.DRAFT_PERSISTENT
+    phase_bytes = cfg.K * stream_launch_bytes(cfg)            # Z once, Wt once, the E rows
+    phase_bytes_full = cfg.K * stream_launch_bytes_full_wt(cfg, G)
+    achieved = phase_bytes / (k_ms / 1e3) / 1e9
+    # bytes of one launch of the dominant kernel (the whole phase, or one position)
+    launch_bytes = phase_bytes if persistent else stream_launch_bytes(cfg)
     traffic = traffic_from_profile(cfg.name)
     step_traffic = step_traffic_from_profile(cfg)
     mfma = mfma_from_profile(cfg.name)
@@ -648,28 +691,30 @@ def main() -> int:
         "scheduled_N": N,
         "mean_accepted": float(g["n_acc"].mean()),
         "mfma_bias": None if mfma is None else {
-            "kernel": f"{DOMINANT} (bias contraction E[x]·Wt^T on v_mfma_f32_32x32x16_bf16)",
+            "kernel": f"{dominant(cfg)} (bias contraction E[x]·Wt^T on v_mfma_f32_32x32x16_bf16)",
             "gflop_per_launch_counted": mfma["gflop"],
-            "gflop_per_launch_algorithmic": 2.0 * cfg.B * cfg.r * cfg.V / 1e9,
-            "tflops": mfma["gflop"] / k_ms,
-            "frac_of_bf16_peak": mfma["gflop"] / k_ms / 2500.0,
+            "gflop_per_launch_algorithmic": 2.0 * cfg.B * cfg.r * cfg.V * (cfg.K if persistent else 1) / 1e9,
+            "tflops": mfma["gflop"] * (1 if persistent else cfg.K) / k_ms,
+            "frac_of_bf16_peak": mfma["gflop"] * (1 if persistent else cfg.K) / k_ms / 2500.0,
             "mfma_busy_pct": mfma["busy_pct"],
             "source": f"profiles/cycle_{cfg.name}_hbm_counters.md"},
         "roofline": {
-            "kernel": f"{DOMINANT} (draft steps 2..K)",
+            "kernel": (f"{DOMINANT}: the draft phase, all {cfg.K} positions in one launch" if persistent else
+                       f"the draft phase: {cfg.K} launches of {DOMINANT_STEPWISE} and of the selection"),
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
+            "traffic": None if traffic is None else traffic * (1 if persistent else cfg.K),
             "traffic_over_algorithmic": None if traffic is None else traffic / launch_bytes,
-            "avg_launch_ms": k_ms,
-            "bytes_per_launch": launch_bytes,
-            "bytes_per_launch_note": "Z slab + E rows of the previous tokens + Wt/K (Wt counted once per cycle)",
-            "bytes_per_launch_full_wt": launch_bytes_full,
-            "frac_full_wt": launch_bytes_full / (k_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "phase_ms": k_ms,
+            "phase_bytes": phase_bytes,
+            "phase_bytes_note": "K x (Z slab + E rows of the previous tokens) + Wt once per cycle",
+            "phase_bytes_full_wt": phase_bytes_full,
+            "frac_full_wt": phase_bytes_full / (k_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         },
+        "draft_phase_ms_by_schedule": schedules,
     }
     if not args.no_cpu_baseline:
         n_cpu = args.cpu_requests if args.cpu_requests > 0 else cfg.B

@@ -16,7 +16,9 @@ Layout make_layout(const dspark_problem& P) {
   L.G = stream_grid(P.V);
   L.nseg = vlse_segments(P.V);
   size_t off = 0;
-  L.part = off;   off = align_up(off + B * L.G * sizeof(float4));
+  // per-(row, workgroup) partials of the per-position launches or of the persistent one
+  const size_t gmax = (size_t)(L.G > persist_grid(P.V) ? L.G : persist_grid(P.V));
+  L.part = off;   off = align_up(off + B * gmax * sizeof(float4));
   L.zpart = off;  off = align_up(off + B * L.G * sizeof(float2));
   L.vlse = off;   off = align_up(off + B * K * L.nseg * sizeof(float2));
   L.lsep = off;   off = align_up(off + B * K * sizeof(float));
@@ -28,6 +30,8 @@ Layout make_layout(const dspark_problem& P) {
   L.sorti = off;  off = align_up(off + B * K * sizeof(int32_t));
   L.lagn = off;   off = align_up(off + (B + 1) * sizeof(int32_t));
   L.efrag = off;  off = align_up(off + (size_t)((B + 31) / 32) * 32 * (size_t)P.r * 2);
+  L.ptok = off;   off = align_up(off + B * sizeof(int32_t));
+  L.psync = off;  off = align_up(off + 64 * sizeof(uint32_t));
   L.total = off;
   return L;
 }
@@ -100,7 +104,8 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
                                 const void* h, const float* w_conf, float b_conf, const float* tau,
                                 const int32_t* anchor, int32_t* draft_tok, float* draft_logq, float* draft_lse,
                                 float* conf, float* surv, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream, hipEvent_t* events, const RnnDraft* rnn = nullptr) {
+                                hipStream_t stream, hipEvent_t* events, const RnnDraft* rnn = nullptr,
+                                int32_t path = DSPARK_DRAFT_AUTO) {
   dspark_status st = check_problem(P);
   if (st != DSPARK_OK) return st;
   const dspark_problem& p = *P;
@@ -160,6 +165,38 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
   se.inv_T = 1.0f / p.sampling_temp;
   se.key = sa.key;
 
+  // the persistent kernel is a cooperative launch; under stream capture the
+  // per-position kernels are recorded instead
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &capture) != hipSuccess) capture = hipStreamCaptureStatusActive;
+  (void)hipGetLastError();
+  const bool persist_ok = !rnn && capture == hipStreamCaptureStatusNone && draft_persistent_supported(p);
+  if (path == DSPARK_DRAFT_PERSISTENT && !persist_ok) return DSPARK_E_UNSUPPORTED;
+  if (path == DSPARK_DRAFT_PERSISTENT || (path == DSPARK_DRAFT_AUTO && persist_ok && p.B <= kPersistMaxB)) {
+    // every position in one cooperative launch, Wt slices held on chip
+    PersistArgs pa{};
+    pa.Z = Z;
+    pa.E = E;
+    pa.Wt = Wt;
+    pa.anchor = anchor;
+    pa.tok = draft_tok;
+    pa.logq = draft_logq;
+    pa.lse = draft_lse;
+    pa.part = part;
+    pa.ptok = at<int32_t>(workspace, L.ptok);
+    pa.sync = at<unsigned>(workspace, L.psync);
+    pa.B = p.B;
+    pa.K = p.K;
+    pa.V = p.V;
+    pa.nchunks = n_chunks(p.V);
+    pa.z_bytes = (uint32_t)((size_t)p.B * p.K * p.V * 2);
+    pa.scale2 = sa.scale2;
+    pa.inv_T = se.inv_T;
+    pa.key = sa.key;
+    if (events && hipEventRecord(events[0], stream) != hipSuccess) return DSPARK_E_LAUNCH;
+    if (launch_draft_persistent(p, pa, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+    if (events && hipEventRecord(events[1], stream) != hipSuccess) return DSPARK_E_LAUNCH;
+  } else {
   float* Gh = rnn ? at<float>(workspace, L.total) : nullptr;
   if (rnn) {
     se.state = rnn->state;
@@ -176,10 +213,11 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
     if (rnn && launch_rnn_step(p, Gh, rnn->W_ih, rnn->W_hh, rnn->b_hh, E, anchor, draft_tok, rnn->state, efrag, k,
                                stream) != hipSuccess)
       return DSPARK_E_LAUNCH;
-    if (events && hipEventRecord(events[2 * (k - 1)], stream) != hipSuccess) return DSPARK_E_LAUNCH;
+    if (events && k == 1 && hipEventRecord(events[0], stream) != hipSuccess) return DSPARK_E_LAUNCH;
     if (launch_stream_draft(p, sa, L.G, stream) != hipSuccess) return DSPARK_E_LAUNCH;
-    if (events && hipEventRecord(events[2 * (k - 1) + 1], stream) != hipSuccess) return DSPARK_E_LAUNCH;
     if (launch_select(p, se, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+    if (events && k == p.K && hipEventRecord(events[1], stream) != hipSuccess) return DSPARK_E_LAUNCH;
+  }
   }
 
   ConfArgs ca{};
@@ -214,10 +252,18 @@ extern "C" dspark_status dspark_draft_timed(const dspark_problem* P, const void*
                                             const void* h, const float* w_conf, float b_conf, const float* tau,
                                             const int32_t* anchor, int32_t* draft_tok, float* draft_logq,
                                             float* draft_lse, float* conf, float* surv, void* workspace,
-                                            size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
-  if (!events) return DSPARK_E_POINTER;
+                                            size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                                            int32_t path) {
+  if (path != DSPARK_DRAFT_AUTO && path != DSPARK_DRAFT_PER_POSITION && path != DSPARK_DRAFT_PERSISTENT)
+    return DSPARK_E_INVALID;
   return draft_impl(P, Z, E, Wt, h, w_conf, b_conf, tau, anchor, draft_tok, draft_logq, draft_lse, conf, surv,
-                    workspace, workspace_bytes, stream, events);
+                    workspace, workspace_bytes, stream, events, nullptr, path);
+}
+
+extern "C" int32_t dspark_draft_path(const dspark_problem* P) {
+  const dspark_status st = check_problem(P);
+  if (st != DSPARK_OK) return st;
+  return draft_persistent_supported(*P) && P->B <= kPersistMaxB ? DSPARK_DRAFT_PERSISTENT : DSPARK_DRAFT_PER_POSITION;
 }
 
 extern "C" size_t dspark_rnn_workspace_bytes(const dspark_problem* P) {

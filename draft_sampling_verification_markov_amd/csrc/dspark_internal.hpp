@@ -53,6 +53,8 @@ struct Layout {
   size_t sorti; // int32 [B*K]: candidate indices in schedule order (same)
   size_t lagn;  // int32 [B + 1]: the lagged schedule of the asynchronous scheduler (n_b, then N)
   size_t efrag; // uint4 [ceil(B/32)][r/16][64]: E rows of the previous draft tokens, B-fragment order
+  size_t ptok;  // int32 [B]: the persistent draft's tokens of the latest position (read by every workgroup)
+  size_t psync; // uint32 [64]: the persistent draft's grid-barrier counter [0] and time-out flag [16]
   size_t total;
 };
 
@@ -77,6 +79,25 @@ struct StreamArgs {
   int B, K, V, k;        // k: 1-based draft position (draft mode)
   int nchunks;
   float scale2;          // log2(e) / T_s
+  Key key;
+};
+
+// Arguments of the persistent draft kernel (all K positions in one cooperative
+// launch, each workgroup's slice of Wt held on chip for the whole cycle).
+struct PersistArgs {
+  const void* Z;         // [B][K][V] bf16
+  const void* E;         // [V][r] bf16
+  const void* Wt;        // [V][r] bf16
+  const int32_t* anchor; // [B]
+  int32_t* tok;          // [B][K] outputs
+  float* logq;
+  float* lse;
+  float4* part;          // [B][G] per-(row, workgroup) partials of the latest position
+  int32_t* ptok;         // [B] tokens of the latest position
+  unsigned* sync;        // [0] barrier counter (zero at launch), [16] time-out flag
+  uint32_t z_bytes;      // bytes of Z (below 2^32)
+  int B, K, V, nchunks;
+  float scale2, inv_T;
   Key key;
 };
 
@@ -173,6 +194,16 @@ hipError_t launch_stream_verify(const dspark_problem& P, const StreamArgs& a, in
 // its B fragments from the efrag region (filled by k_accept)
 bool verify_uses_efrag(const dspark_problem& P);
 hipError_t launch_select(const dspark_problem& P, const SelectArgs& a, hipStream_t s);
+// The persistent draft kernel: true when it serves P (bf16 logits and factors,
+// r = 256, B <= 256 and at most 5 chunks of the vocabulary per workgroup) and
+// the device can hold its whole grid at once.
+// workgroups of the persistent draft launch: one per vocabulary chunk up to kStreamGridMax
+int persist_grid(int V);
+// dspark_draft takes the persistent draft where it applies and the batch is at
+// most this (above it the per-position kernels, with two waves per SIMD, are faster)
+constexpr int kPersistMaxB = 48;
+bool draft_persistent_supported(const dspark_problem& P);
+hipError_t launch_draft_persistent(const dspark_problem& P, const PersistArgs& a, hipStream_t s);
 hipError_t launch_conf(const dspark_problem& P, const ConfArgs& a, hipStream_t s);
 // Segments of the candidate range that the partial-rank kernel splits the comparisons into.
 #ifndef DSPARK_SCHED_SEG_MAX

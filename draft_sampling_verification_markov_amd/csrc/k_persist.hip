@@ -1,0 +1,552 @@
+// Persistent Markov draft: every position of a cycle in one cooperative launch,
+// each CU's slice of the logit projection Wt held on chip for the whole cycle.
+//
+// DSpark page, Method > Semi-autoregressive generation: the sequential stage
+// adds a rank-r transition bias E[prev] . Wt^T to the base logits and samples
+// position after position; the low rank is what keeps the per-position work
+// small.  A launch per position re-reads all of Wt (r x V) at every position;
+// here it is read once per cycle, which pays where that re-read dominates: at
+// small batches, where the base logits of a position are a small fraction of
+// Wt's bytes.
+//
+// Every workgroup (one per CU: four waves, one per SIMD) owns a contiguous
+// range of at most 5 vocabulary chunks of 128 entries, 20 M-tiles of 32,
+// five per wave.  A wave keeps the MFMA A fragments of its first four M-tiles
+// in registers for the whole cycle (4 x 16 K-steps x 16 bytes per lane: 256
+// registers) and those of its fifth in LDS (64 KB for the workgroup).
+// Per position k:
+//  1. the previous tokens of all rows into LDS;
+//  2. per N-tile of 32 rows: the E rows of its previous tokens arrive in LDS
+//     by DMA one N-tile ahead (two buffers, rows padded by 16 bytes); per
+//     M-tile the wave chains 16 MFMAs from a zero accumulator (the Markov term
+//     at its own magnitude) while its vector unit finishes the previous
+//     M-tile: logits = base logits (requested into registers one N-tile ahead)
+//     + Markov term, then (max, sum of 2^(x - max)) in base 2 per (row,
+//     M-tile), into LDS;
+//  3. per 128 rows: chunk log-masses, chunk Gumbels, the best chunk and the
+//     running log-partition, one partial record per (row, workgroup), stored
+//     past the L2;
+//  4. grid barrier;
+//  5. selection: workgroup g takes rows g, g + G, ...: merges the row's G
+//     partials, reads the winning chunk's Wt block, recomputes its 128 logits,
+//     draws the entry, and writes the token, log q and the log-partition (the
+//     token also past the L2, for every workgroup's next gather);
+//  6. grid barrier, while the next position's first base logits are requested.
+// Records read after a barrier are read past the L2 as well (an XCD's L2 is
+// not kept coherent with another's).  Every barrier wait is bounded: past the
+// limit the flag sync[16] is set and the waits that follow return at once, so
+// the kernel always ends (its results are then unspecified).
+#include "dspark_internal.hpp"
+
+namespace dspark {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+constexpr int kPThreads = 256;
+constexpr int kPWaves = kPThreads / 64;
+constexpr int kPMt = 5;                  // M-tiles of 32 entries per wave
+constexpr int kPMtWg = kPWaves * kPMt;   // per workgroup: 5 chunks
+constexpr int kPRows = 256;              // rows of the batch at most
+constexpr int kPHalf = 128;              // rows whose M-tile partials are merged at once
+constexpr unsigned kSpinLimit = 1u << 20;
+
+// MFMA row rho of an M-tile -> vocabulary entry within it: in the 32x32
+// accumulator layout lane l then holds 16 consecutive entries 16*(l/32)..+15
+// of its column (request) l % 32.
+__device__ __forceinline__ int prow_entry(int rho) { return ((rho >> 2) & 1) * 16 + (rho >> 3) * 4 + (rho & 3); }
+
+// Chunks [c_begin, c_end) of workgroup g of G: an even split, the first
+// nchunks % G workgroups one more (the draft step's split).
+__device__ __forceinline__ void persist_chunk_range(int g, int G, int nchunks, int& c_begin, int& c_end) {
+  const unsigned q = (unsigned)nchunks / (unsigned)G, rem = (unsigned)nchunks - q * (unsigned)G;
+  const unsigned ug = (unsigned)g;
+  c_begin = (int)(ug * q + (ug < rem ? ug : rem));
+  c_end = c_begin + (int)q + (ug < rem ? 1 : 0);
+}
+
+__device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// a float4 record past the L2, as two 8-byte halves
+__device__ __forceinline__ void st_agent4(float4* p, float4 v) {
+  unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+  const unsigned long long lo = ((unsigned long long)__float_as_uint(v.y) << 32) | __float_as_uint(v.x);
+  const unsigned long long hi = ((unsigned long long)__float_as_uint(v.w) << 32) | __float_as_uint(v.z);
+  __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 ld_agent4(const float4* p) {
+  const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
+  const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float4(__uint_as_float((unsigned)lo), __uint_as_float((unsigned)(lo >> 32)), __uint_as_float((unsigned)hi),
+                     __uint_as_float((unsigned)(hi >> 32)));
+}
+
+// Grid barrier on a monotonic arrival counter, in two halves so that loads
+// independent of the other workgroups can be issued between them: arrive
+// (this workgroup's stores past the L2 complete, then one atomic add) and wait
+// (until all G workgroups of the epoch have arrived).  Bounded: past kSpinLimit
+// polls the flag is set and this and every later wait return at once.
+__device__ __forceinline__ void grid_arrive(unsigned* sync, unsigned& epoch) {
+  wait_vmem();
+  __syncthreads();
+  epoch += 1;
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void grid_wait(unsigned* sync, unsigned G, unsigned epoch) {
+  if (threadIdx.x == 0) {
+    const unsigned target = epoch * G;
+    unsigned spins = ld_agent(sync + 16) ? kSpinLimit : 0u;
+    while (ld_agent(sync) < target) {
+      if (++spins > kSpinLimit) {
+        st_agent(sync + 16, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+// one 16-byte piece of a factor row with one of E[prev] (8 products in order)
+__device__ __forceinline__ float dot8(uint4 e, uint4 w) {
+  float acc = 0.f;
+  acc = fmaf(bf16_lo(e.x), bf16_lo(w.x), acc);
+  acc = fmaf(bf16_hi(e.x), bf16_hi(w.x), acc);
+  acc = fmaf(bf16_lo(e.y), bf16_lo(w.y), acc);
+  acc = fmaf(bf16_hi(e.y), bf16_hi(w.y), acc);
+  acc = fmaf(bf16_lo(e.z), bf16_lo(w.z), acc);
+  acc = fmaf(bf16_hi(e.z), bf16_hi(w.z), acc);
+  acc = fmaf(bf16_lo(e.w), bf16_lo(w.w), acc);
+  acc = fmaf(bf16_hi(e.w), bf16_hi(w.w), acc);
+  return acc;
+}
+
+// Word i (0..3) of a Philox quad without indexing (an indexed pick can become a scratch access).
+__device__ __forceinline__ uint32_t quad_pick(const Words4& q, int i) {
+  const uint32_t lo = (i & 1) ? q.w[1] : q.w[0], hi = (i & 1) ? q.w[3] : q.w[2];
+  return (i & 2) ? hi : lo;
+}
+
+template <int R>
+__global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
+  static_assert(R == 256, "one factor row per 32 lanes of a gather instruction");
+  constexpr int S = R / 16;          // MFMA K-steps (16 ranks each)
+  constexpr int ROWB = R * 2;        // bytes of a factor row
+  constexpr int PR = R / 8;          // 16-byte pieces of a factor row
+  constexpr int RG = kPThreads / PR; // selection: rows per piece step
+  constexpr int NP = kChunk / RG;    // selection: Wt pieces per thread
+  constexpr int STR = PR + 4;        // selection: LDS row stride of the dot partials (floats)
+  constexpr int RS = PR + 1;         // LDS row stride of the E rows, in 16-byte slots (one of padding)
+  constexpr int NSLOT = 32 * RS;     // slots of an N-tile's E rows
+  constexpr int JR = kPMt - 1;       // M-tiles whose fragments stay in registers
+  static_assert(kChunk * STR * 4 <= kPHalf * kPMtWg * 8, "the selection's partials fit the merge area");
+  // A fragments of each wave's last M-tile ([wave][K-step][lane], 16 bytes each)
+  __shared__ __attribute__((aligned(1024))) bf16x8_t s_a[kPWaves][S][64];
+  // E rows of two N-tiles, even and odd (row rho's piece p at slot rho * RS +
+  // p: the padding slot makes each K-step's fragment read one base address plus
+  // a constant, and spreads the 32 rows of a read over distinct banks)
+  __shared__ __attribute__((aligned(1024))) unsigned char s_b0[(NSLOT + 63) / 64 * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_b1[(NSLOT + 63) / 64 * 1024];
+  __shared__ __attribute__((aligned(16))) float2 s_tp[kPHalf * kPMtWg];
+  __shared__ int s_tok[kPRows];
+  __shared__ float s_ell[kChunk], s_bm[kPWaves], s_bs[kPWaves], s_best[kPWaves];
+  __shared__ int s_bi[kPWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
+  const int G = gridDim.x, g = blockIdx.x;
+  int c_begin, c_end;
+  persist_chunk_range(g, G, a.nchunks, c_begin, c_end);
+  const int nct = 4 * (c_end - c_begin);
+  const int V = a.V, K = a.K, B = a.B;
+  const uint16_t* Wt = static_cast<const uint16_t*>(a.Wt);
+  const uint16_t* E = static_cast<const uint16_t*>(a.E);
+  const uint16_t* Z = static_cast<const uint16_t*>(a.Z);
+  const float scale2 = a.scale2;
+  const int vbase = c_begin * kChunk;
+
+  // 0. this wave's A fragments (Wt rows of its M-tiles) for the whole cycle:
+  // the first JR in registers, the last in LDS; a missing M-tile (past the
+  // workgroup's chunks or past V) is zero
+  bf16x8_t af[JR][S];
+#pragma unroll
+  for (int j = 0; j < kPMt; ++j) {
+    const int mtg = wave * kPMt + j;
+    const int v = vbase + mtg * 32 + prow_entry(l32);
+    const bool ok = mtg < nct && v < V;
+    const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(Wt + (size_t)(ok ? v : 0) * R + 8 * h);
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      const bf16x8_t x = ok ? src[2 * t] : bf16x8_t{};
+      if (j < JR)
+        af[j < JR ? j : 0][t] = x;
+      else
+        s_a[wave][t][lane] = x;
+    }
+  }
+
+  // base logits of this lane's 16 entries of each of the wave's M-tiles of
+  // N-tile nt at position kk: ten 16-byte buffer loads, always issued (rows
+  // past B read row B - 1).  A piece past V (wholly past it, as V % 8 == 0) is
+  // read at an offset past the end of Z, where the buffer returns zeros; its
+  // bits are set to -inf where it is used.
+  const int NT = (B + 31) / 32;
+  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(Z, a.z_bytes);
+  const __amdgpu_buffer_rsrc_t ers = make_rsrc(E, (uint32_t)V * ROWB);
+  const int vlane = vbase + wave * kPMt * 32 + 16 * h;  // this lane's first entry of the wave's M-tiles
+  const int vleft = V - vlane;
+  auto zload = [&](int kk, int nt, uint4 (&z)[kPMt][2]) {
+    const int row = nt * 32 + l32;
+    const int zr = row < B ? row : B - 1;
+    const uint32_t off = (uint32_t)((((size_t)zr * K + (kk - 1)) * V + vlane) * 2);
+#pragma unroll
+    for (int j = 0; j < kPMt; ++j)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const bool in = j * 32 + 8 * p < vleft;
+        const u32x4_t x =
+            __builtin_amdgcn_raw_buffer_load_b128(zrs, (int)(in ? off + (uint32_t)(j * 64 + 16 * p) : a.z_bytes), 0, 0);
+        z[j][p] = make_uint4(x[0], x[1], x[2], x[3]);
+      }
+  };
+  // E rows of N-tile nt's previous tokens into dst, by LDS DMA: instruction q
+  // fills slots 64q .. 64q + 63, lane i slot 64q + i (a padding slot loads
+  // piece 0; lanes past the last slot are off)
+  auto gather = [&](int nt, unsigned char* dst) {
+    for (int q = wave; q * 64 < NSLOT; q += kPWaves) {
+      const int sl = q * 64 + lane;
+      const int row = sl / RS, piece = sl - row * RS;
+      if (sl < NSLOT)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ers, (__attribute__((address_space(3))) void*)(dst + q * 1024), 16,
+            (int)((uint32_t)s_tok[nt * 32 + row] * ROWB + (uint32_t)(piece < PR ? piece : 0) * 16), 0, 0, 0);
+    }
+  };
+  // per-row merge of the M-tile partials of N-tiles 4*half .. 4*half+3:
+  // chunk log-masses, chunk Gumbels, best chunk, running log-partition, as one
+  // record per (row, workgroup) stored past the L2
+  auto merge = [&](int k, int half) {
+    barrier_lds_only();
+    if (tid < kPHalf && half * kPHalf + tid < B) {
+      const int prow = half * kPHalf + tid;
+      float run_m = -INFINITY, run_s = 0.f, best = -INFINITY;
+      int best_c = 0x7fffffff, quad = -1;
+      Words4 w4 = {};
+      for (int cc = 0; cc < c_end - c_begin; ++cc) {
+        float cm = -INFINITY, cs = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const float2 pt = s_tp[tid * kPMtWg + 4 * cc + tt];
+          lse2_merge(cm, cs, pt.x, pt.y);
+        }
+        const int c = c_begin + cc;
+        if ((c >> 2) != quad) {
+          quad = c >> 2;
+          w4 = draw_quad(a.key, (uint32_t)(quad * 4), (uint32_t)prow, (uint32_t)k, kDraftChunk);
+        }
+        const float gc = gumbel_from_word(quad_pick(w4, c & 3));
+        const float score = cs > 0.f ? (cm + log2f(cs)) * kLn2 + gc : -INFINITY;
+        lse2_merge(run_m, run_s, cm, cs);
+        if (score > best) {
+          best = score;
+          best_c = c;
+        }
+      }
+      st_agent4(a.part + (size_t)prow * G + g, make_float4(run_m, run_s, best, __int_as_float(best_c)));
+    }
+    barrier_lds_only();
+  };
+  // the reduction of one (N-tile, M-tile) accumulator: logits = base + Markov
+  // term (one rounding), then (max, sum of 2^(x - max)) in base 2 into LDS
+  auto epilogue = [&](int nt, int j, const f32x16_t& acc, const uint4 (&zj)[2]) {
+    const uint32_t n0 = j * 32 < vleft ? 0u : 0xFF80FF80u, n1 = j * 32 + 8 < vleft ? 0u : 0xFF80FF80u;
+    const uint32_t zw[8] = {zj[0].x | n0, zj[0].y | n0, zj[0].z | n0, zj[0].w | n0,
+                            zj[1].x | n1, zj[1].y | n1, zj[1].z | n1, zj[1].w | n1};
+    float ell[16];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ell[2 * i] = bf16_lo(zw[i]) + acc[2 * i];
+      ell[2 * i + 1] = bf16_hi(zw[i]) + acc[2 * i + 1];
+      m = fmaxf(m, fmaxf(ell[2 * i], ell[2 * i + 1]));
+    }
+    m = halves32_max(m);
+    const float off = m == -INFINITY ? 0.f : -m * scale2;
+    float sm = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm += __builtin_amdgcn_exp2f(fmaf(ell[i], scale2, off));
+    sm = halves32_sum(sm);
+    // both halves of the column hold the same pair: a duplicate store of equal values
+    s_tp[((nt & 3) * 32 + l32) * kPMtWg + wave * kPMt + j] = make_float2(m * scale2, sm);
+  };
+  // N-tile nt of position k: its E rows are in cur and its base logits in
+  // zc; the next N-tile's rows (into nxt) and base logits (into zn) are
+  // requested first, a whole N-tile of MFMA work ahead of their use
+  auto tile = [&](int k, int nt, uint4 (&zc)[kPMt][2], uint4 (&zn)[kPMt][2], const unsigned char* cur,
+                  unsigned char* nxt) {
+    const bool more = nt + 1 < NT;
+    if (more) {
+      gather(nt + 1, nxt);
+      zload(k, nt + 1, zn);
+    }
+    const unsigned char* brow = cur + (l32 * RS + h) * 16;
+    auto bfrag = [&](int t) { return *reinterpret_cast<const bf16x8_t*>(brow + 32 * t); };
+    // Every M-tile is computed (a missing one has zero fragments and its
+    // result is never read).  Stage j chains M-tile j's 16 MFMAs, its LDS
+    // fragments read three K-steps ahead, and gives each K-step a fixed slice
+    // of M-tile j-1's epilogue: steps 0-7 form the logits and their maximum,
+    // step 8 merges the column halves, steps 9-15 the exponentials and sums.
+    // Scheduling barriers keep the slices where they are written.
+    auto stage = [&](int j, int pj, const f32x16_t& pacc, const uint4 (&pz)[2]) {
+      f32x16_t acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      constexpr int D = 3;
+      bf16x8_t bq[D + 1], aq[D + 1];
+#pragma unroll
+      for (int t = 0; t < D; ++t) {
+        bq[t] = bfrag(t);
+        if (j >= JR) aq[t] = s_a[wave][t][lane];
+      }
+      const uint32_t n0 = pj * 32 < vleft ? 0u : 0xFF80FF80u, n1 = pj * 32 + 8 < vleft ? 0u : 0xFF80FF80u;
+      float ell[16], m = -INFINITY, off = 0.f, s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        if (t + D < S) {
+          bq[(t + D) % (D + 1)] = bfrag(t + D);
+          if (j >= JR) aq[(t + D) % (D + 1)] = s_a[wave][t + D][lane];
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(j < JR ? af[j < JR ? j : 0][t] : aq[t % (D + 1)],
+                                                      bq[t % (D + 1)], acc, 0, 0, 0);
+        if (pj >= 0) {
+          if (t < 8) {
+            const uint32_t w = (t < 4 ? (t == 0 ? pz[0].x : t == 1 ? pz[0].y : t == 2 ? pz[0].z : pz[0].w)
+                                      : (t == 4 ? pz[1].x : t == 5 ? pz[1].y : t == 6 ? pz[1].z : pz[1].w)) |
+                               (t < 4 ? n0 : n1);
+            ell[2 * t] = bf16_lo(w) + pacc[2 * t];
+            ell[2 * t + 1] = bf16_hi(w) + pacc[2 * t + 1];
+            m = fmaxf(m, fmaxf(ell[2 * t], ell[2 * t + 1]));
+          } else if (t == 8) {
+            m = halves32_max(m);
+            off = m == -INFINITY ? 0.f : -m * scale2;
+          } else {
+            // steps 9..14 two entries each, step 15 the last four
+            const int e0 = 2 * (t - 9), e1 = t == 15 ? 16 : e0 + 2;
+#pragma unroll
+            for (int e = e0; e < e1; ++e) {
+              const float x = __builtin_amdgcn_exp2f(fmaf(ell[e], scale2, off));
+              if (e & 1)
+                s1 += x;
+              else
+                s0 += x;
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (pj >= 0) {
+        const float sm = halves32_sum(s0 + s1);
+        // both halves of the column hold the same pair: a duplicate store of equal values
+        s_tp[((nt & 3) * 32 + l32) * kPMtWg + wave * kPMt + pj] = make_float2(m * scale2, sm);
+      }
+      return acc;
+    };
+    const f32x16_t zero = {};
+    f32x16_t a0 = stage(0, -1, zero, zc[0]);
+    f32x16_t a1 = stage(1, 0, a0, zc[0]);
+    a0 = stage(2, 1, a1, zc[1]);
+    a1 = stage(3, 2, a0, zc[2]);
+    a0 = stage(4, 3, a1, zc[3]);
+    epilogue(nt, 4, a0, zc[4]);
+    // this wave's gather of N-tile nt + 1 (and its base-logit loads, issued
+    // with it) are complete; after the barrier every wave's rows are in and no
+    // wave reads cur any more
+    wait_vmem();
+    barrier_lds_only();
+    if ((nt & 3) == 3 || !more) merge(k, nt >> 2);
+  };
+
+  uint4 zA[kPMt][2], zB[kPMt][2];
+  zload(1, 0, zA);
+
+  unsigned epoch = 0;
+  for (int k = 1; k <= K; ++k) {
+    // 1. the previous tokens of all 256 rows (rows past B: token 0), then
+    // the E rows of N-tile 0
+    {
+      int x = 0;
+      if (tid < B) x = k == 1 ? a.anchor[tid] : (int)ld_agent(reinterpret_cast<const unsigned*>(a.ptok + tid));
+      s_tok[tid] = clamp_id(x, V);
+    }
+    __syncthreads();
+    gather(0, s_b0);
+    wait_vmem();
+    __syncthreads();
+
+    // 2-3. the vocabulary stream, N-tile after N-tile, base-logit registers
+    // alternating between zA and zB
+    for (int nt = 0; nt < NT; nt += 2) {
+      tile(k, nt, zA, zB, s_b0, s_b1);
+      if (nt + 1 < NT) tile(k, nt + 1, zB, zA, s_b1, s_b0);
+    }
+
+    // 4. every workgroup's partials of position k are out
+    grid_arrive(a.sync, epoch);
+    grid_wait(a.sync, (unsigned)G, epoch);
+
+    // 5. selection of rows g, g + G, ...
+    for (int b = g; b < B; b += G) {
+      const int c = tid % PR, grp = tid / PR;
+      float4 p = make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
+      if (tid < G) p = ld_agent4(a.part + (size_t)b * G + tid);
+      // the winning chunk: argmax of the chunk scores, smallest chunk id on ties
+      float best = -INFINITY;
+      int bc = 0x7fffffff;
+      if (tid < G && better(p.z, __float_as_int(p.w), best, bc)) {
+        best = p.z;
+        bc = __float_as_int(p.w);
+      }
+      wave_argmax(best, bc);
+      float lm = -INFINITY, ls = 0.f;
+      if (tid < G) lse2_merge(lm, ls, p.x, p.y);
+      wave_lse2_merge(lm, ls);
+      if (lane == 0) {
+        s_best[wave] = best;
+        s_bi[wave] = bc;
+        s_bm[wave] = lm;
+        s_bs[wave] = ls;
+      }
+      __syncthreads();
+      float B0 = s_best[0];
+      int C0 = s_bi[0];
+      for (int w = 1; w < kPWaves; ++w)
+        if (better(s_best[w], s_bi[w], B0, C0)) {
+          B0 = s_best[w];
+          C0 = s_bi[w];
+        }
+      const int cstar = (C0 >= 0 && C0 * kChunk < V) ? C0 : 0;
+      const int v0 = cstar * kChunk;
+      const int nrow = V - v0 < kChunk ? V - v0 : kChunk;
+      // the chunk's Wt block (consecutive threads on consecutive 16-byte
+      // pieces), this thread's piece of E[prev], the entry's base logit and Gumbel
+      const uint16_t* blk = Wt + (size_t)v0 * R;
+      uint4 w[NP];
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int rr = i * RG + grp;
+        w[i] = *reinterpret_cast<const uint4*>(blk + (size_t)(rr < nrow ? rr : 0) * R + 8 * c);
+      }
+      const uint4 ep = *reinterpret_cast<const uint4*>(E + (size_t)s_tok[b] * R + 8 * c);
+      const int r = tid & (kChunk - 1);
+      const int v = v0 + r;
+      const bool inside = tid < kChunk && r < nrow;
+      const float zb = bf16_to_f32(Z[((size_t)b * K + (k - 1)) * V + (r < nrow ? v : v0)]);
+      const float gum = gumbel_from_word(draw_word(a.key, (uint32_t)v, (uint32_t)b, (uint32_t)k, kDraftElem));
+      __syncthreads();  // s_tp is reused for the dot partials
+      float* s_part = reinterpret_cast<float*>(s_tp);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) s_part[(i * RG + grp) * STR + c] = dot8(ep, w[i]);
+      __syncthreads();
+      float score = -INFINITY;
+      int idx = 0x7fffffff;
+      if (inside) {
+        float dot = 0.f;
+        const float4* q4 = reinterpret_cast<const float4*>(s_part + r * STR);
+#pragma unroll
+        for (int j = 0; j < PR / 4; ++j) {
+          const float4 x = q4[j];
+          dot += x.x;
+          dot += x.y;
+          dot += x.z;
+          dot += x.w;
+        }
+        const float ell = (zb + dot) * a.inv_T;
+        s_ell[r] = ell;
+        score = ell + gum;
+        idx = v;
+      }
+      wave_argmax(score, idx);
+      __syncthreads();  // every wave's LDS reads of the maxima above are done
+      if (lane == 0) {
+        s_best[wave] = score;
+        s_bi[wave] = idx;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        float B1 = s_best[0];
+        int X = s_bi[0];
+        for (int ww = 1; ww < kPWaves; ++ww)
+          if (better(s_best[ww], s_bi[ww], B1, X)) {
+            B1 = s_best[ww];
+            X = s_bi[ww];
+          }
+        float M = s_bm[0], Sm = s_bs[0];
+        for (int ww = 1; ww < kPWaves; ++ww) lse2_merge(M, Sm, s_bm[ww], s_bs[ww]);
+        const float lse = (M + log2f(Sm)) * kLn2;
+        if (X < v0 || X >= v0 + kChunk || X >= V) X = v0;  // no finite score
+        const size_t o = (size_t)b * K + (k - 1);
+        a.tok[o] = X;
+        a.logq[o] = s_ell[X - v0] - lse;
+        a.lse[o] = lse;
+        st_agent(reinterpret_cast<unsigned*>(a.ptok + b), (unsigned)X);
+      }
+      __syncthreads();
+    }
+
+    // 6. every token of position k is out; while the other workgroups arrive,
+    // the next position's first base logits (they do not depend on the tokens)
+    grid_arrive(a.sync, epoch);
+    if (k < K) zload(k + 1, 0, zA);
+    grid_wait(a.sync, (unsigned)G, epoch);
+  }
+}
+
+__global__ __launch_bounds__(64) void k_persist_init(unsigned* sync) {
+  sync[threadIdx.x] = 0u;
+}
+
+}  // namespace
+
+int persist_grid(int V) {
+  const int nc = n_chunks(V);
+  return nc < kStreamGridMax ? nc : kStreamGridMax;
+}
+
+bool draft_persistent_supported(const dspark_problem& P) {
+  if (P.logits_dtype != DSPARK_BF16 || P.weight_dtype != DSPARK_BF16 || P.r != 256 || P.B > kPRows) return false;
+  if ((size_t)P.B * P.K * P.V * 2 > 0xFFFFFFFFull || (size_t)P.V * 512 > 0xFFFFFFFFull) return false;  // 32-bit buffer offsets
+  const int nc = n_chunks(P.V);
+  const int G = persist_grid(P.V);
+  if ((nc + G - 1) / G > kPMtWg / 4) return false;
+  static int capable = -1;  // whether one workgroup per CU fits and the device launches cooperatively
+  if (capable < 0) {
+    int dev = 0, coop = 0, ncu = 0, per_cu = 0;
+    capable = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_draft_persist<256>),
+                                                     kPThreads, 0) == hipSuccess)
+      capable = coop && per_cu >= 1 && ncu >= kStreamGridMax ? 1 : 0;
+    (void)hipGetLastError();
+  }
+  return capable == 1;
+}
+
+hipError_t launch_draft_persistent(const dspark_problem& P, const PersistArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_persist_init, 1, 64, 0, s, a.sync);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  PersistArgs arg = a;
+  void* args[] = {&arg};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_draft_persist<256>),
+                                    dim3(persist_grid(P.V)), dim3(kPThreads), args, 0, s);
+}
+
+}  // namespace dspark

@@ -16,11 +16,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdspark.so")
 
 OK, E_INVALID, E_DTYPE, E_UNSUPPORTED, E_WORKSPACE, E_LAUNCH, E_POINTER = 0, -1, -2, -3, -4, -5, -6
+DRAFT_AUTO, DRAFT_PER_POSITION, DRAFT_PERSISTENT = 0, 1, 2  # schedules of the draft phase (dspark_instr.h)
 F32, BF16 = 0, 1
 _DT = {"f32": F32, "bf16": BF16}
 _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 
-SYMBOLS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft", "dspark_draft_timed",
+SYMBOLS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft", "dspark_draft_timed", "dspark_draft_path",
            "dspark_schedule", "dspark_schedule_async", "dspark_schedule_fixed", "dspark_schedule_threshold",
            "dspark_sts_workspace_bytes", "dspark_sts_fit", "dspark_verify", "dspark_rnn_workspace_bytes",
            "dspark_draft_rnn", "dspark_verify_rnn", "dspark_schedule_noalloc",
@@ -71,8 +72,10 @@ def load() -> ctypes.CDLL:
     lib.dspark_status_string.restype = ctypes.c_char_p
     lib.dspark_draft.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_draft.restype = i32
-    lib.dspark_draft_timed.argtypes = lib.dspark_draft.argtypes + [vp]
+    lib.dspark_draft_timed.argtypes = lib.dspark_draft.argtypes + [vp, i32]
     lib.dspark_draft_timed.restype = i32
+    lib.dspark_draft_path.argtypes = [ctypes.POINTER(Problem)]
+    lib.dspark_draft_path.restype = i32
     lib.dspark_schedule.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_schedule.restype = i32
     lib.dspark_probe_draws.argtypes = [ctypes.c_uint64, vp, i32, vp, vp, i32, vp, vp, vp]
@@ -150,9 +153,10 @@ def draft(P: Problem, Z, E, Wt, h, w_conf, b_conf: float, tau, anchor,
 
 
 def draft_timed(P: Problem, Z, E, Wt, h, w_conf, b_conf: float, tau, anchor,
-                draft_tok, draft_logq, draft_lse, conf, surv, workspace, events, stream=None) -> None:
-    """dspark_draft recording events[2i], events[2i+1] (raw hipEvent_t handles, a ctypes
-    array of 2K c_void_p) around the stream kernel of draft step i+1."""
+                draft_tok, draft_logq, draft_lse, conf, surv, workspace, events=None, stream=None,
+                path: int = DRAFT_AUTO) -> None:
+    """dspark_draft_timed: dspark_draft with schedule `path` (DRAFT_*), recording events[0] and
+    events[1] (raw hipEvent_t handles, a ctypes array of 2 c_void_p, or None) around the draft phase."""
     lt, wt, ht = _TORCH_DT[P.logits_dtype], _TORCH_DT[P.weight_dtype], _TORCH_DT[P.hidden_dtype]
     st = load().dspark_draft_timed(
         ctypes.byref(P), _ptr(Z, lt, "Z"), _ptr(E, wt, "E"), _ptr(Wt, wt, "Wt"), _ptr(h, ht, "h"),
@@ -161,8 +165,16 @@ def draft_timed(P: Problem, Z, E, Wt, h, w_conf, b_conf: float, tau, anchor,
         _ptr(draft_logq, torch.float32, "draft_logq"), _ptr(draft_lse, torch.float32, "draft_lse"),
         _ptr(conf, torch.float32, "conf"), _ptr(surv, torch.float32, "surv"),
         _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
-        _stream(stream), ctypes.cast(events, ctypes.c_void_p))
+        _stream(stream), None if events is None else ctypes.cast(events, ctypes.c_void_p), ctypes.c_int32(path))
     _check("dspark_draft_timed", st)
+
+
+def draft_path(P: Problem) -> int:
+    """dspark_draft_path: the schedule dspark_draft takes for P (DRAFT_PERSISTENT or DRAFT_PER_POSITION)."""
+    r = load().dspark_draft_path(ctypes.byref(P))
+    if r < 0:
+        raise DsparkError("dspark_draft_path", r)
+    return r
 
 
 def schedule(P: Problem, surv, T_table, n_sched, n_total, workspace, stream=None) -> None:

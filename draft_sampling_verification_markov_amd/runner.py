@@ -75,9 +75,13 @@ class CycleOutputs:
         return {k: v.cpu().numpy() for k, v in vars(self).items() if k != "workspace"}
 
 
-def draft(P, x: CycleInputs, o: CycleOutputs, stream=None):
-    dspark.draft(P, x.Z, x.E, x.Wt, x.h, x.w_c, x.b_c, x.tau, x.anchor,
-                 o.tok, o.logq, o.lse, o.conf, o.surv, o.workspace, stream)
+def draft(P, x: CycleInputs, o: CycleOutputs, stream=None, path: int = dspark.DRAFT_AUTO):
+    if path == dspark.DRAFT_AUTO:
+        dspark.draft(P, x.Z, x.E, x.Wt, x.h, x.w_c, x.b_c, x.tau, x.anchor,
+                     o.tok, o.logq, o.lse, o.conf, o.surv, o.workspace, stream)
+    else:
+        dspark.draft_timed(P, x.Z, x.E, x.Wt, x.h, x.w_c, x.b_c, x.tau, x.anchor,
+                           o.tok, o.logq, o.lse, o.conf, o.surv, o.workspace, None, stream, path=path)
 
 
 def schedule(P, x: CycleInputs, o: CycleOutputs, stream=None):
@@ -89,7 +93,7 @@ def verify(P, x: CycleInputs, o: CycleOutputs, stream=None):
                   o.out_tok, o.n_acc, o.next_anchor, o.logp, o.resid_mass, o.workspace, stream)
 
 
-def run_cycle(P, x: CycleInputs, o: CycleOutputs, stream=None):
-    draft(P, x, o, stream)
+def run_cycle(P, x: CycleInputs, o: CycleOutputs, stream=None, path: int = dspark.DRAFT_AUTO):
+    draft(P, x, o, stream, path)
     schedule(P, x, o, stream)
     verify(P, x, o, stream)

@@ -16,13 +16,33 @@
 extern "C" {
 #endif
 
+/* The two schedules of the K-position draft phase (Method > Semi-autoregressive
+ * generation: the same sequential computation either way, with identical
+ * results up to floating-point summation order):
+ *   DSPARK_DRAFT_PER_POSITION  one stream kernel and one selection kernel per
+ *                              position, each re-reading Wt;
+ *   DSPARK_DRAFT_PERSISTENT    one cooperative launch for all K positions, each
+ *                              CU's slice of Wt held on chip for the cycle
+ *                              (bf16 logits and factors, r = 256, B <= 256, a
+ *                              device that launches cooperatively; not under
+ *                              stream capture, not for the RNN head).
+ * dspark_draft takes DSPARK_DRAFT_AUTO: the persistent schedule where it applies
+ * and B <= 48, else the per-position one (the measured crossover). */
+enum {
+  DSPARK_DRAFT_AUTO = 0,
+  DSPARK_DRAFT_PER_POSITION = 1,
+  DSPARK_DRAFT_PERSISTENT = 2
+};
+
 /*
- * dspark_draft_timed -- dspark_draft, plus instrumentation: events[2i] and
- * events[2i+1] (caller-created HIP events, 2*K of them) are recorded on
- * `stream` immediately before and after the vocabulary-stream kernel of draft
- * step i+1, so that the caller can read that kernel's duration with
- * hipEventElapsedTime.  Same inputs, outputs and errors as dspark_draft;
- * DSPARK_E_POINTER if events is NULL.
+ * dspark_draft_timed -- dspark_draft with a chosen schedule and optional
+ * timing.  `path` is one of the DSPARK_DRAFT_* values above.  If `events` is
+ * not NULL, events[0] and events[1] (caller-created HIP events) are recorded on
+ * `stream` immediately before the first and after the last kernel of the
+ * K-position draft phase, before the confidence head, so that the caller can
+ * read the phase's duration with hipEventElapsedTime.  Same inputs, outputs
+ * and errors as dspark_draft, plus DSPARK_E_INVALID for an unknown `path` and
+ * DSPARK_E_UNSUPPORTED for DSPARK_DRAFT_PERSISTENT where it does not apply.
  */
 dspark_status dspark_draft_timed(const dspark_problem* P,
                                  const void* Z, const void* E, const void* Wt, const void* h,
@@ -31,7 +51,15 @@ dspark_status dspark_draft_timed(const dspark_problem* P,
                                  int32_t* draft_tok, float* draft_logq, float* draft_lse,
                                  float* conf, float* surv,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                 hipEvent_t* events);
+                                 hipEvent_t* events, int32_t path);
+
+/*
+ * dspark_draft_path -- the schedule dspark_draft takes for problem P outside
+ * stream capture: DSPARK_DRAFT_PERSISTENT or DSPARK_DRAFT_PER_POSITION, or a
+ * negative dspark_status if P is invalid.  The first call may query the
+ * device (cooperative launch support and occupancy).
+ */
+int32_t dspark_draft_path(const dspark_problem* P);
 
 /*
  * dspark_probe_draws -- the device's random draws on given inputs, for

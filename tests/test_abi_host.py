@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
                                           "dspark_status_string", "dspark_rnn_workspace_bytes", "dspark_draft_rnn",
                                           "dspark_verify_rnn", "dspark_schedule_noalloc"])
     # instrumentation, outside the step's contract
-    assert _declared([HEADERS[1]]) == ["dspark_draft_timed", "dspark_probe_draws"]
+    assert _declared([HEADERS[1]]) == ["dspark_draft_path", "dspark_draft_timed", "dspark_probe_draws"]
 
 
 def test_status_codes_are_the_contract(ds):
@@ -105,6 +105,23 @@ def test_draft_rejects_bad_problems(ds, kw, code):
     P = _P(ds, **kw)
     st = lib.dspark_draft(ctypes.byref(P), *([None] * 5), ctypes.c_float(0), *([None] * 8), 0, None)
     assert st == code, ds.status_string(st)
+
+
+def test_draft_schedule_arguments(ds):
+    # an unknown schedule is rejected before anything else; the schedule query
+    # rejects what dspark_draft rejects and reports the per-position schedule
+    # where the persistent one cannot apply (fp32 logits, rank 128, 257 rows)
+    lib = ds.load()
+    P = _P(ds)
+    for bad in (-1, 3, 7):
+        st = lib.dspark_draft_timed(ctypes.byref(P), *([None] * 5), ctypes.c_float(0), *([None] * 8), 0, None,
+                                    None, bad)
+        assert st == ds.E_INVALID, ds.status_string(st)
+    assert lib.dspark_draft_path(ctypes.byref(_P(ds, B=0))) == ds.E_INVALID
+    assert lib.dspark_draft_path(ctypes.byref(_P(ds, r=48))) == ds.E_UNSUPPORTED
+    for kw in (dict(logits="f32"), dict(r=128), dict(B=257)):
+        assert lib.dspark_draft_path(ctypes.byref(_P(ds, **kw))) == ds.DRAFT_PER_POSITION
+    assert (ds.DRAFT_AUTO, ds.DRAFT_PER_POSITION, ds.DRAFT_PERSISTENT) == (0, 1, 2)
 
 
 def test_bad_dtype_code(ds):

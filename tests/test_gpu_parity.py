@@ -36,12 +36,12 @@ def lib():
     return dspark, runner
 
 
-def gpu_cycle(lib, cfg, inp):
+def gpu_cycle(lib, cfg, inp, path=0):
     dspark, runner = lib
     P = dspark.Problem.from_config(cfg)
     x = runner.CycleInputs.upload(inp)
     o = runner.CycleOutputs(P)
-    runner.run_cycle(P, x, o)
+    runner.run_cycle(P, x, o, path=path)
     torch.cuda.synchronize()
     return o.host()
 
@@ -128,3 +128,38 @@ def test_full_size(lib, name):
     _say("[gpu]   GPU cycle done; oracle cycle running")
     counts = check(cfg, inp, g)
     _say(f"[gpu]   low-margin differences {counts}; N = {int(g['n_total'][0])}")
+
+
+# Both schedules of the draft phase (dspark_instr.h) where dspark_draft would
+# take the other one: the persistent kernel at the full batch, and with a
+# ragged batch and vocabulary and more rows than workgroups; the per-position
+# kernels at a small bf16 batch.
+SCHEDULES = [
+    ("high_concurrency", 2),
+    ("persist_ragged", 2),
+    ("tbias_bf16", 1),
+]
+
+
+def _schedule_cfg(name):
+    if name == "persist_ragged":
+        # 33 rows (a ragged N-tile), V = 1000 (a ragged last chunk and M-tile), 8 chunks: 8 workgroups
+        # selecting 4-5 rows each
+        return synth.get_config("tbias_bf16").replace(name="persist_ragged", B=33, K=3, V=1000, r=256, d=64,
+                                                      seed=15)
+    return synth.get_config(name)
+
+
+@pytest.mark.parametrize("name,path", SCHEDULES, ids=[f"{n}-{'persistent' if p == 2 else 'per_position'}"
+                                                      for n, p in SCHEDULES])
+def test_draft_schedules(lib, name, path):
+    dspark, _ = lib
+    cfg = _schedule_cfg(name)
+    P = dspark.Problem.from_config(cfg)
+    auto = dspark.draft_path(P)
+    _say(f"[gpu] schedule {path} on {name} B={cfg.B} K={cfg.K} V={cfg.V} (dspark_draft takes {auto})")
+    assert auto != path or name == "persist_ragged"
+    inp = synth.make_inputs(cfg)
+    g = gpu_cycle(lib, cfg, inp, path=path)
+    counts = check(cfg, inp, g)
+    _say(f"[gpu]   low-margin differences {counts}")
