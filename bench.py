@@ -266,12 +266,12 @@ def _pmc_means(directory: str, counter: str):
 
 
 PROFILE_COMMANDS = """cd /tmp && export TMPDIR=/tmp; R=<repository root>; OUT=<output directory>
-rocprofv3 --kernel-trace --stats -T -d $OUT/trace -o trace --output-format csv -- python3 $R/bench.py --main-only --steps 5 --warmup 2 --no-cpu-baseline
-rocprofv3 --pmc FETCH_SIZE -d $OUT/fetch -o fetch --output-format csv -- python3 $R/bench.py --main-only --steps 2 --warmup 1 --no-cpu-baseline
-rocprofv3 --pmc WRITE_SIZE -d $OUT/write -o write --output-format csv -- python3 $R/bench.py --main-only --steps 2 --warmup 1 --no-cpu-baseline
+rocprofv3 --kernel-trace --stats -T -d $OUT/trace -o trace --output-format csv -- python3 $R/bench.py --main-only --steps 5 --warmup 2 --no-cpu-baseline --no-schedule-compare
+rocprofv3 --pmc FETCH_SIZE -d $OUT/fetch -o fetch --output-format csv -- python3 $R/bench.py --main-only --steps 2 --warmup 1 --no-cpu-baseline --no-schedule-compare
+rocprofv3 --pmc WRITE_SIZE -d $OUT/write -o write --output-format csv -- python3 $R/bench.py --main-only --steps 2 --warmup 1 --no-cpu-baseline --no-schedule-compare
 rocprofv3 --pmc FETCH_SIZE -d $OUT/cfetch -o cfetch --output-format csv -- python3 $R/bench.py --calibrate-copy
 rocprofv3 --pmc WRITE_SIZE -d $OUT/cwrite -o cwrite --output-format csv -- python3 $R/bench.py --calibrate-copy
-rocprofv3 --pmc MfmaFlopsBF16 MfmaUtil -d $OUT/mfma -o mfma --output-format csv -- python3 $R/bench.py --main-only --steps 2 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc MfmaFlopsBF16 MfmaUtil -d $OUT/mfma -o mfma --output-format csv -- python3 $R/bench.py --main-only --steps 2 --warmup 1 --no-cpu-baseline --no-schedule-compare
 python3 $R/bench.py --summarize-profiles $OUT"""
 
 
@@ -368,6 +368,9 @@ def main() -> int:
     ap.add_argument("--cpu-requests", type=int, default=0,
                     help="requests in the oracle's timed sample (default: the whole batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-schedule-compare", action="store_true",
+                    help="skip timing the draft schedule dspark_draft does not take (profiled runs: rocprofv3 "
+                         "ends with a fault after a cooperative launch and then writes no results)")
     ap.add_argument("--main-only", action="store_true",
                     help="time the first-drop step alone (no graph replay, asynchronous scheduler, baselines, "
                          "STS fit or RNN head): the run the profiling commands use")
@@ -628,11 +631,14 @@ def main() -> int:
     lib_path = dspark.draft_path(P)
     assert (lib_path == dspark.DRAFT_PERSISTENT) == draft_persistent(cfg), "bench's rule differs from the library's"
     # both schedules of the draft phase on the same inputs (the dispatch evidence)
-    schedules = {"per_position": draft_phase_ms(dspark.DRAFT_PER_POSITION, 20)}
-    try:
-        schedules["persistent"] = draft_phase_ms(dspark.DRAFT_PERSISTENT, 20)
-    except dspark.DsparkError:
-        schedules["persistent"] = None  # not applicable to this workload
+    schedules = {"per_position": None, "persistent": None}
+    if not args.no_schedule_compare or lib_path == dspark.DRAFT_PER_POSITION:
+        schedules["per_position"] = draft_phase_ms(dspark.DRAFT_PER_POSITION, 20)
+    if not args.no_schedule_compare or lib_path == dspark.DRAFT_PERSISTENT:
+        try:
+            schedules["persistent"] = draft_phase_ms(dspark.DRAFT_PERSISTENT, 20)
+        except dspark.DsparkError:
+            schedules["persistent"] = None  # not applicable to this workload
     log(f"draft phase: {schedules} ms (dspark_draft takes "
         f"{'persistent' if lib_path == dspark.DRAFT_PERSISTENT else 'per_position'})")
 

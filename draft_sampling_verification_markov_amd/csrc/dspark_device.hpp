@@ -86,13 +86,11 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t w) {
   return -logf(e);
 }
 
-// 2^x - 1 for 0 <= x <= 1/2 without the cancellation of exp2(x) - 1: the power
-// series of e^y - 1 at y = x ln 2 through y^8 (coefficients (ln 2)^k / k!; the
-// remainder is below 2e-9 of the result on this range), in Horner form.
+// 2^x - 1 for 0 <= x <= 1/4 without the cancellation of exp2(x) - 1: the power
+// series of e^y - 1 at y = x ln 2 through y^6 (coefficients (ln 2)^k / k!; the
+// remainder is below 6e-9 of the result on this range), in Horner form.
 __device__ __forceinline__ float exp2m1_small(float x) {
-  float p = 1.3215486790144307e-06f;
-  p = fmaf(x, p, 1.525273380405984e-05f);
-  p = fmaf(x, p, 1.5403530393381608e-04f);
+  float p = 1.5403530393381608e-04f;
   p = fmaf(x, p, 1.3333558146428443e-03f);
   p = fmaf(x, p, 9.618129107628477e-03f);
   p = fmaf(x, p, 5.550410866482158e-02f);
@@ -110,8 +108,8 @@ __device__ __forceinline__ float exp2m1_small(float x) {
 // ((t - z) - bias) s2 - (lp2 - lq2) with t - z exact, so neither carries a
 // rounding at the logits' magnitude (a bias accumulated onto the logit would
 // round at every step of the contraction).  The weight is q^ (2^d - 1) for
-// 0 < d <= 1/2 (no cancellation where p and q are close), p^ - q^ for d > 1/2
-// and 0 otherwise.  dlp = lp2 - lq2; a row without a draft term (a bonus row)
+// 0 < d <= 1/4 (no cancellation where p and q are close), p^ - q^ for d > 1/4
+// (where 2^d - 1 > 0.189 bounds the cancellation to a few ulps) and 0 otherwise.  dlp = lp2 - lq2; a row without a draft term (a bonus row)
 // passes lq2 = +inf and dlp = -inf, and gets r = p^; an entry past the end of
 // the row passes t = z = -inf and gets zeros.  Every kernel that forms residual
 // weights uses this function, so the chunk masses of the resample pass and the
@@ -129,7 +127,7 @@ __device__ __forceinline__ ResidEntry resid_entry(float t, float z, float bias, 
   e.q = __builtin_amdgcn_exp2f(fmaf(bias, s2, fmaf(z, s2, -lq2)));
   const float d = fmaf((t - z) - bias, s2, -dlp);
   const float small = e.q * exp2m1_small(d);
-  e.r = d > 0.5f ? e.p - e.q : (d > 0.f ? small : 0.f);
+  e.r = d > 0.25f ? e.p - e.q : (d > 0.f ? small : 0.f);
   e.qa = d > 0.f ? e.q : 0.f;
   return e;
 }

@@ -1254,7 +1254,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
     ChunkGumbels cg;
     const bool any_bonus = __builtin_amdgcn_ballot_w64(!resid) != 0;  // this wave holds a bonus row
 
-    auto step = [&](int u, unsigned char* cur, unsigned char* nxt, const u32x4_t (&zc)[4], u32x4_t (&zn)[4]) {
+    // z: this unit's draft logits on entry, the next unit's requested into the same registers at the end
+    auto step = [&](int u, unsigned char* cur, unsigned char* nxt, u32x4_t (&z)[4]) {
       wait_vmem();          // unit u's tiles and draft logits have landed
       barrier_lds_only();   // everyone's have; unit u - 1's stage is free
       // the next unit's requests in two bursts: its target tile now, its Wt
@@ -1262,7 +1263,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
       // block in issue before computing
       dma.stage_t(nxt, tr, unit_v0(u + 1), wave);
       if (u >= nunits) {
-        zload(u + 1, zn);
+        zload(u + 1, z);
         dma.stage_w(nxt, wr, unit_v0(u + 1), wave);
         return;
       }
@@ -1303,12 +1304,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
       // is the target weight relative to that maximum, merged into the chunk's
       // log-partition once per unit.  Entries past V hold -inf targets and draft
       // logits: every weight 0.
-      // draft logit of entry i of M-tile mt (residual rows; zeros for a bonus row), -inf past V
-      const bool ragged = v0 + T::kUnit > V;
+      // draft logit of entry i of M-tile mt (residual rows; zeros for a bonus row); in
+      // the ragged last unit the 16-byte pieces past V (wholly past it, V % 8 == 0)
+      // are set to -inf once, so that the entries need no test
+      if (v0 + T::kUnit > V) {
+#pragma unroll
+        for (int pc = 0; pc < 4; ++pc)
+          if (v0 + (pc >> 1) * 32 + 16 * h + 8 * (pc & 1) >= V)
+            z[pc] = u32x4_t{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
+      }
       auto zl = [&](int mt, int i) {
-        const uint32_t w = zc[2 * mt + (i >> 3)][(i >> 1) & 3];
-        const float z = (i & 1) ? bf16_hi(w) : bf16_lo(w);
-        return ragged && v0 + mt * 32 + 16 * h + i >= V ? -INFINITY : z;
+        const uint32_t w = z[2 * mt + (i >> 3)][(i >> 1) & 3];
+        return (i & 1) ? bf16_hi(w) : bf16_lo(w);
       };
       float off = lsp2, mb = -INFINITY;
       if (any_bonus) {
@@ -1364,13 +1371,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
       }
       // the next unit's draft logits once this unit's are consumed (one
       // register set for both)
-      zload(u + 1, zn);
+      zload(u + 1, z);
     };
     // the first step is peeled (the fragments are first used outside the loop)
-    step(0, buf0, buf1, zA, zA);
+    step(0, buf0, buf1, zA);
     for (int u = 1; u < nunits; u += 2) {
-      step(u, buf1, buf0, zA, zA);
-      step(u + 1, buf0, buf1, zA, zA);
+      step(u, buf1, buf0, zA);
+      step(u + 1, buf0, buf1, zA);
     }
     wait_vmem();         // the dummy stages have landed
     barrier_lds_only();  // the next pass restages the ring and the row offsets
