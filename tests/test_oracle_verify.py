@@ -16,6 +16,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 import scipy.special
+import scipy.stats
 
 from oracle import conf, philox, sched, verify
 from oracle.draft import draft
@@ -302,3 +303,83 @@ def test_logp_is_the_target_log_probability_of_each_verified_token():
         ref = scipy.special.log_softmax(Zt[0, k].astype(np.float64) / 0.8)[d["x"][0, k]]
         assert abs(res["logp"][k] - ref) < 1e-12
     assert np.isnan(res["logp"][3])
+
+
+def _markov_mc(n_runs, V=10, K=3, r=4, seed=21):
+    """Draft + verify_request of the full oracle on one request whose draft rows
+    depend on the prefix through a strong Markov bias (E[x_{k-1}] . Wt^T, std
+    about 1.5 nats), every position verified; returns the emitted sequences,
+    the outcome kinds and the target rows."""
+    rng = np.random.default_rng(seed)
+    Z = rng.normal(0, 1.0, (1, K, V)).astype(np.float32)
+    E = rng.normal(0, 1.0, (V, r)).astype(np.float32)
+    Wt = rng.normal(0, 0.75, (V, r)).astype(np.float32)
+    Zt = np.concatenate([Z, rng.normal(0, 1.0, (1, 1, V)).astype(np.float32)], axis=1)
+    Zt = (Zt + rng.normal(0, 0.7, Zt.shape)).astype(np.float32)
+    p = scipy.special.softmax(Zt[0].astype(np.float64), axis=1)
+    E64, W64 = E.astype(np.float64), Wt.astype(np.float64)
+    anchor = 4
+    seqs, kinds = [], []
+    for s in range(n_runs):
+        d = draft(Z, E, Wt, np.array([anchor]), 1.0, s)
+        res = verify.verify_request(0, K, d["x"][0], Zt[0], Z[0], E64, W64, anchor, 1.0, s)
+        seqs.append(res["tokens"])
+        kinds.append((res["kind"], res["accepted"]))
+    return seqs, kinds, p, (Z, E, Wt, anchor)
+
+
+def test_monte_carlo_markov_bias_emitted_tokens_follow_the_target():
+    # Prefix-dependent draft rows through the oracle's own draft and
+    # verify_request (DSpark page, Overview: the output law is the target's
+    # whatever the drafter).  The target rows do not depend on the prefix, so
+    # the j-th emitted token, over the runs that emit it, has law p_j, and
+    # given the first emitted token (the position-1 draft token accepted) the
+    # second has law p_2 whatever the first was.  A verifier that used any
+    # other draft row for the acceptance test or the residual (the bias of
+    # another previous token, or none) would bend these laws.
+    K = 3
+    seqs, kinds, p, (Z, E, Wt, anchor) = _markov_mc(3000, K=K)
+    V = p.shape[1]
+    # the bias really moves the draft rows: the first draft row differs from softmax(Z_1) by a visible margin
+    ell = Z[0, 0].astype(np.float64) + E[anchor].astype(np.float64) @ Wt.astype(np.float64).T
+    q1 = scipy.special.softmax(ell)
+    assert 0.5 * np.abs(q1 - scipy.special.softmax(Z[0, 0].astype(np.float64))).sum() > 0.15
+    # every outcome occurs: rejections at each position (residual draws) and the bonus
+    seen = set(kinds)
+    for k in range(K):
+        assert ("resid", k) in seen, k
+    assert ("bonus", K) in seen
+    for j in range(K + 1):
+        ys = [s[j] for s in seqs if len(s) > j]
+        assert len(ys) > 150, j
+        assert _chi2_pvalue(np.bincount(ys, minlength=V).astype(float), p[j]) > 1e-3, j
+    # y_2 given y_1 = a, for every a with enough runs: one chi-square over all
+    # of them (the emission of y_2 selects y_1, never y_2)
+    table = np.zeros((V, V))
+    for s in seqs:
+        if len(s) > 1:
+            table[s[0], s[1]] += 1
+    stat, dof, rows = 0.0, 0, 0
+    for a in range(V):
+        n = table[a].sum()
+        if n < 60:
+            continue
+        rows += 1
+        exp = p[1] * n
+        order = np.argsort(exp)
+        obs_c, exp_c, acc_o, acc_e = [], [], 0.0, 0.0
+        for i in order:
+            acc_o += table[a, i]
+            acc_e += exp[i]
+            if acc_e >= 5.0:
+                obs_c.append(acc_o)
+                exp_c.append(acc_e)
+                acc_o = acc_e = 0.0
+        if acc_e > 0:
+            obs_c[-1] += acc_o
+            exp_c[-1] += acc_e
+        obs_c, exp_c = np.array(obs_c), np.array(exp_c)
+        stat += ((obs_c - exp_c) ** 2 / exp_c).sum()
+        dof += len(obs_c) - 1
+    assert rows >= 3
+    assert scipy.stats.chi2.sf(stat, dof) > 1e-3, (stat, dof)
