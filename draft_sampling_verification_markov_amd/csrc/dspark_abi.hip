@@ -2,11 +2,23 @@
 // kernel sequence of each call.  See include/dspark.h for the contract.
 #include <math.h>
 
+#include <float.h>
+
 #include <mutex>
 
 #include "dspark_internal.hpp"
 
 namespace dspark {
+
+// The library built with DSPARK_DEBUG_CHECKS scans every call's inputs before
+// its kernels and its outputs after them (k_debug.hip); the scans raise bits of
+// the flag word that dspark_debug_flags reads.  Compiled in both builds, run
+// only in that one.
+#ifdef DSPARK_DEBUG_CHECKS
+constexpr bool kDebugChecks = true;
+#else
+constexpr bool kDebugChecks = false;
+#endif
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -100,6 +112,46 @@ struct RnnDraft {
   float* state;
 };
 
+// Debug scans (run only with kDebugChecks): false if a scan could not be launched.
+static bool debug_draft_inputs(const dspark_problem& p, const void* Z, const void* E, const void* Wt, const void* h,
+                               const float* w_conf, const float* tau, const int32_t* anchor, hipStream_t s) {
+  const bool zb = p.logits_dtype == DSPARK_BF16, wb = p.weight_dtype == DSPARK_BF16, hb = p.hidden_dtype == DSPARK_BF16;
+  return debug_scan_nonfinite(Z, (size_t)p.B * p.K * p.V, zb, DSPARK_DEBUG_LOGITS, s) == hipSuccess &&
+         debug_scan_nonfinite(E, (size_t)p.V * p.r, wb, DSPARK_DEBUG_FACTORS, s) == hipSuccess &&
+         debug_scan_nonfinite(Wt, (size_t)p.V * p.r, wb, DSPARK_DEBUG_FACTORS, s) == hipSuccess &&
+         debug_scan_nonfinite(h, (size_t)p.B * p.K * p.d, hb, DSPARK_DEBUG_FACTORS, s) == hipSuccess &&
+         debug_scan_nonfinite(w_conf, (size_t)(p.d + p.r), false, DSPARK_DEBUG_FACTORS, s) == hipSuccess &&
+         debug_scan_range_f32(tau, (size_t)p.K, FLT_MIN, FLT_MAX, DSPARK_DEBUG_FACTORS, s) == hipSuccess &&
+         debug_scan_range_i32(anchor, (size_t)p.B, 0, p.V - 1, DSPARK_DEBUG_IDS, s) == hipSuccess;
+}
+static bool debug_draft_outputs(const dspark_problem& p, const int32_t* tok, const float* logq, const float* conf,
+                                const float* surv, hipStream_t s) {
+  const size_t n = (size_t)p.B * p.K;
+  return debug_scan_range_i32(tok, n, 0, p.V - 1, DSPARK_DEBUG_OUTPUT, s) == hipSuccess &&
+         debug_scan_range_f32(logq, n, -FLT_MAX, 1e-5f, DSPARK_DEBUG_OUTPUT, s) == hipSuccess &&
+         debug_scan_range_f32(conf, n, 0.f, 1.f, DSPARK_DEBUG_OUTPUT, s) == hipSuccess &&
+         debug_scan_range_f32(surv, n, 0.f, 1.f, DSPARK_DEBUG_OUTPUT, s) == hipSuccess;
+}
+static bool debug_schedule_inputs(const dspark_problem& p, const float* surv, const float* T_table, hipStream_t s) {
+  const size_t n = (size_t)p.B * p.K;
+  return (!surv || debug_scan_range_f32(surv, n, 0.f, 1.f, DSPARK_DEBUG_SCHEDULE_INPUT, s) == hipSuccess) &&
+         (!T_table ||
+          debug_scan_range_f32(T_table, n + (size_t)p.B + 1, FLT_MIN, FLT_MAX, DSPARK_DEBUG_SCHEDULE_INPUT, s) ==
+              hipSuccess);
+}
+static bool debug_verify_inputs(const dspark_problem& p, const void* target, const void* Z, const void* E,
+                                const void* Wt, const int32_t* anchor, const int32_t* tok, const int32_t* n_sched,
+                                hipStream_t s) {
+  const bool zb = p.logits_dtype == DSPARK_BF16, wb = p.weight_dtype == DSPARK_BF16;
+  return debug_scan_nonfinite(target, (size_t)p.B * (p.K + 1) * p.V, zb, DSPARK_DEBUG_LOGITS, s) == hipSuccess &&
+         debug_scan_nonfinite(Z, (size_t)p.B * p.K * p.V, zb, DSPARK_DEBUG_LOGITS, s) == hipSuccess &&
+         debug_scan_nonfinite(E, (size_t)p.V * p.r, wb, DSPARK_DEBUG_FACTORS, s) == hipSuccess &&
+         debug_scan_nonfinite(Wt, (size_t)p.V * p.r, wb, DSPARK_DEBUG_FACTORS, s) == hipSuccess &&
+         debug_scan_range_i32(anchor, (size_t)p.B, 0, p.V - 1, DSPARK_DEBUG_IDS, s) == hipSuccess &&
+         debug_scan_range_i32(tok, (size_t)p.B * p.K, 0, p.V - 1, DSPARK_DEBUG_IDS, s) == hipSuccess &&
+         debug_scan_range_i32(n_sched, (size_t)p.B, 0, p.K, DSPARK_DEBUG_SCHEDULE_INPUT, s) == hipSuccess;
+}
+
 static dspark_status draft_impl(const dspark_problem* P, const void* Z, const void* E, const void* Wt,
                                 const void* h, const float* w_conf, float b_conf, const float* tau,
                                 const int32_t* anchor, int32_t* draft_tok, float* draft_logq, float* draft_lse,
@@ -128,6 +180,7 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
   if (st != DSPARK_OK) return st;
   if (rnn && workspace_bytes < make_layout(p).total + rnn_extra_bytes(p)) return DSPARK_E_WORKSPACE;
   (void)hipGetLastError();
+  if (kDebugChecks && !debug_draft_inputs(p, Z, E, Wt, h, w_conf, tau, anchor, stream)) return DSPARK_E_LAUNCH;
 
   const Layout L = make_layout(p);
   float4* part = at<float4>(workspace, L.part);
@@ -236,6 +289,7 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
   ca.d = p.d;
   ca.r = p.r;
   if (launch_conf(p, ca, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+  if (kDebugChecks && !debug_draft_outputs(p, draft_tok, draft_logq, conf, surv, stream)) return DSPARK_E_LAUNCH;
   return DSPARK_OK;
 }
 
@@ -244,6 +298,7 @@ extern "C" dspark_status dspark_draft(const dspark_problem* P, const void* Z, co
                                       const int32_t* anchor, int32_t* draft_tok, float* draft_logq,
                                       float* draft_lse, float* conf, float* surv, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream) {
+  const AbiRange range("dspark_draft");
   return draft_impl(P, Z, E, Wt, h, w_conf, b_conf, tau, anchor, draft_tok, draft_logq, draft_lse, conf, surv,
                     workspace, workspace_bytes, stream, nullptr);
 }
@@ -254,6 +309,7 @@ extern "C" dspark_status dspark_draft_timed(const dspark_problem* P, const void*
                                             float* draft_lse, float* conf, float* surv, void* workspace,
                                             size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
                                             int32_t path) {
+  const AbiRange range("dspark_draft_timed");
   if (path != DSPARK_DRAFT_AUTO && path != DSPARK_DRAFT_PER_POSITION && path != DSPARK_DRAFT_PERSISTENT)
     return DSPARK_E_INVALID;
   return draft_impl(P, Z, E, Wt, h, w_conf, b_conf, tau, anchor, draft_tok, draft_logq, draft_lse, conf, surv,
@@ -277,6 +333,7 @@ extern "C" dspark_status dspark_draft_rnn(const dspark_problem* P, const void* Z
                                           const int32_t* anchor, int32_t* draft_tok, float* draft_logq,
                                           float* draft_lse, float* conf, float* surv, float* state, void* workspace,
                                           size_t workspace_bytes, hipStream_t stream) {
+  const AbiRange range("dspark_draft_rnn");
   const RnnDraft rnn{W_ih, b_ih, W_hh, b_hh, state};
   return draft_impl(P, Z, E, Wt, h, w_conf, b_conf, tau, anchor, draft_tok, draft_logq, draft_lse, conf, surv,
                     workspace, workspace_bytes, stream, nullptr, &rnn);
@@ -285,6 +342,7 @@ extern "C" dspark_status dspark_draft_rnn(const dspark_problem* P, const void* Z
 extern "C" dspark_status dspark_schedule(const dspark_problem* P, const float* surv, const float* T_table,
                                          int32_t* n_sched, int32_t* n_total, void* workspace,
                                          size_t workspace_bytes, hipStream_t stream) {
+  const AbiRange range("dspark_schedule");
   dspark_status st = check_problem(P);
   if (st != DSPARK_OK) return st;
   if (!surv || !T_table || !n_sched || !n_total) return DSPARK_E_POINTER;
@@ -293,9 +351,12 @@ extern "C" dspark_status dspark_schedule(const dspark_problem* P, const float* s
   st = check_workspace(*P, workspace, workspace_bytes);
   if (st != DSPARK_OK) return st;
   (void)hipGetLastError();
+  if (kDebugChecks && !debug_schedule_inputs(*P, surv, T_table, stream)) return DSPARK_E_LAUNCH;
   const Layout L = make_layout(*P);
   if (launch_schedule(*P, surv, T_table, n_sched, n_total, at<int32_t>(workspace, L.rpart),
                       at<float>(workspace, L.sorts), at<int32_t>(workspace, L.sorti), stream) != hipSuccess)
+    return DSPARK_E_LAUNCH;
+  if (kDebugChecks && debug_check_schedule(n_sched, n_total, P->B, P->K, DSPARK_DEBUG_OUTPUT, stream) != hipSuccess)
     return DSPARK_E_LAUNCH;
   return DSPARK_OK;
 }
@@ -341,6 +402,7 @@ static hipError_t scratch_for_current_device(unsigned char** out) {
 
 extern "C" dspark_status dspark_schedule_noalloc(const dspark_problem* P, const float* surv, const float* T_table,
                                                  int32_t* n_sched, int32_t* n_total, hipStream_t stream) {
+  const AbiRange range("dspark_schedule_noalloc");
   dspark_status st = check_problem(P);
   if (st != DSPARK_OK) return st;
   if ((long long)P->B * P->K > kNoAllocCandidates) return DSPARK_E_WORKSPACE;
@@ -353,13 +415,17 @@ extern "C" dspark_status dspark_schedule_noalloc(const dspark_problem* P, const 
   int32_t* rpart = reinterpret_cast<int32_t*>(ws);
   float* sorted_s = reinterpret_cast<float*>(ws + kNoAllocRankBytes);
   int32_t* sorted_i = reinterpret_cast<int32_t*>(ws + kNoAllocRankBytes + (size_t)kNoAllocCandidates * sizeof(float));
+  if (kDebugChecks && !debug_schedule_inputs(*P, surv, T_table, stream)) return DSPARK_E_LAUNCH;
   if (launch_schedule(*P, surv, T_table, n_sched, n_total, rpart, sorted_s, sorted_i, stream) != hipSuccess)
+    return DSPARK_E_LAUNCH;
+  if (kDebugChecks && debug_check_schedule(n_sched, n_total, P->B, P->K, DSPARK_DEBUG_OUTPUT, stream) != hipSuccess)
     return DSPARK_E_LAUNCH;
   return DSPARK_OK;
 }
 
 extern "C" dspark_status dspark_schedule_fixed(const dspark_problem* P, int32_t gamma, int32_t* n_sched,
                                                int32_t* n_total, hipStream_t stream) {
+  const AbiRange range("dspark_schedule_fixed");
   dspark_status st = check_problem(P);
   if (st != DSPARK_OK) return st;
   if (gamma < 0 || gamma > P->K) return DSPARK_E_INVALID;
@@ -368,11 +434,14 @@ extern "C" dspark_status dspark_schedule_fixed(const dspark_problem* P, int32_t 
   (void)hipGetLastError();
   if (launch_schedule_static(*P, nullptr, 0, gamma, 0.f, n_sched, n_total, stream) != hipSuccess)
     return DSPARK_E_LAUNCH;
+  if (kDebugChecks && debug_check_schedule(n_sched, n_total, P->B, P->K, DSPARK_DEBUG_OUTPUT, stream) != hipSuccess)
+    return DSPARK_E_LAUNCH;
   return DSPARK_OK;
 }
 
 extern "C" dspark_status dspark_schedule_threshold(const dspark_problem* P, const float* surv, float theta,
                                                    int32_t* n_sched, int32_t* n_total, hipStream_t stream) {
+  const AbiRange range("dspark_schedule_threshold");
   dspark_status st = check_problem(P);
   if (st != DSPARK_OK) return st;
   if (!isfinite(theta)) return DSPARK_E_INVALID;
@@ -380,7 +449,10 @@ extern "C" dspark_status dspark_schedule_threshold(const dspark_problem* P, cons
   for (const void* q : {(const void*)surv, (const void*)n_sched, (const void*)n_total})
     if (!aligned(q, 4)) return DSPARK_E_POINTER;
   (void)hipGetLastError();
+  if (kDebugChecks && !debug_schedule_inputs(*P, surv, nullptr, stream)) return DSPARK_E_LAUNCH;
   if (launch_schedule_static(*P, surv, 1, 0, theta, n_sched, n_total, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+  if (kDebugChecks && debug_check_schedule(n_sched, n_total, P->B, P->K, DSPARK_DEBUG_OUTPUT, stream) != hipSuccess)
+    return DSPARK_E_LAUNCH;
   return DSPARK_OK;
 }
 
@@ -399,6 +471,7 @@ extern "C" dspark_status dspark_sts_fit(int32_t M, int32_t K, const float* conf_
                                         int32_t n_bins, double* tau, int32_t* tau_idx, double* ece_fit,
                                         double* ece_raw, void* workspace, size_t workspace_bytes,
                                         hipStream_t stream) {
+  const AbiRange range("dspark_sts_fit");
   if (!sts_sizes_ok(M, K, G, n_bins)) return DSPARK_E_INVALID;
   if (!tau_grid || !tau || !tau_idx || !ece_fit || !ece_raw) return DSPARK_E_POINTER;
   if (M > 0 && (!conf_raw || !acc_len || !n_verified)) return DSPARK_E_POINTER;
@@ -418,6 +491,7 @@ extern "C" dspark_status dspark_sts_fit(int32_t M, int32_t K, const float* conf_
 extern "C" dspark_status dspark_schedule_async(const dspark_problem* P, const float* surv_lag, const float* surv,
                                                const float* T_table, int32_t* n_sched, int32_t* n_total,
                                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const AbiRange range("dspark_schedule_async");
   dspark_status st = check_problem(P);
   if (st != DSPARK_OK) return st;
   if (!surv_lag || !surv || !T_table || !n_sched || !n_total) return DSPARK_E_POINTER;
@@ -429,9 +503,14 @@ extern "C" dspark_status dspark_schedule_async(const dspark_problem* P, const fl
   (void)hipGetLastError();
   const Layout L = make_layout(*P);
   int32_t* lag = at<int32_t>(workspace, L.lagn);
+  if (kDebugChecks && !(debug_schedule_inputs(*P, surv_lag, T_table, stream) &&
+                        debug_schedule_inputs(*P, surv, nullptr, stream)))
+    return DSPARK_E_LAUNCH;
   if (launch_schedule_async(*P, surv_lag, surv, T_table, n_sched, n_total, at<int32_t>(workspace, L.rpart),
                             at<float>(workspace, L.sorts), at<int32_t>(workspace, L.sorti), lag, lag + P->B,
                             stream) != hipSuccess)
+    return DSPARK_E_LAUNCH;
+  if (kDebugChecks && debug_check_schedule(n_sched, n_total, P->B, P->K, DSPARK_DEBUG_OUTPUT, stream) != hipSuccess)
     return DSPARK_E_LAUNCH;
   return DSPARK_OK;
 }
@@ -462,6 +541,8 @@ static dspark_status verify_impl(const dspark_problem* P, const void* target, co
   st = check_workspace(p, workspace, workspace_bytes);
   if (st != DSPARK_OK) return st;
   (void)hipGetLastError();
+  if (kDebugChecks && !debug_verify_inputs(p, target, Z, E, Wt, anchor, draft_tok, n_sched, stream))
+    return DSPARK_E_LAUNCH;
 
   const Layout L = make_layout(p);
   VerifyArgs va{};
@@ -522,6 +603,9 @@ static dspark_status verify_impl(const dspark_problem* P, const void* target, co
   sa.key = va.key;
   if (launch_stream_verify(p, sa, L.G, stream) != hipSuccess) return DSPARK_E_LAUNCH;
   if (launch_verify_finish(p, va, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+  if (kDebugChecks && debug_check_verify(n_sched, out_tok, n_accepted, next_anchor, resid_mass, p.B, p.K, p.V,
+                                         DSPARK_DEBUG_OUTPUT, stream) != hipSuccess)
+    return DSPARK_E_LAUNCH;
   return DSPARK_OK;
 }
 
@@ -531,6 +615,7 @@ extern "C" dspark_status dspark_verify(const dspark_problem* P, const void* targ
                                        int32_t* out_tok, int32_t* n_accepted, int32_t* next_anchor, float* logp,
                                        float* resid_mass, void* workspace, size_t workspace_bytes,
                                        hipStream_t stream) {
+  const AbiRange range("dspark_verify");
   return verify_impl(P, target, Z, E, Wt, anchor, draft_tok, draft_logq, draft_lse, n_sched, out_tok, n_accepted,
                      next_anchor, logp, resid_mass, workspace, workspace_bytes, stream, nullptr);
 }
@@ -541,7 +626,46 @@ extern "C" dspark_status dspark_verify_rnn(const dspark_problem* P, const void* 
                                            const float* state, const int32_t* n_sched, int32_t* out_tok,
                                            int32_t* n_accepted, int32_t* next_anchor, float* logp, float* resid_mass,
                                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const AbiRange range("dspark_verify_rnn");
   if (!state) return DSPARK_E_POINTER;
   return verify_impl(P, target, Z, E, Wt, anchor, draft_tok, draft_logq, draft_lse, n_sched, out_tok, n_accepted,
                      next_anchor, logp, resid_mass, workspace, workspace_bytes, stream, state);
+}
+
+extern "C" dspark_status dspark_debug_flags(uint32_t* flags, int32_t clear) {
+  if (!kDebugChecks) return DSPARK_E_UNSUPPORTED;
+  if (!flags) return DSPARK_E_POINTER;
+  const AbiRange range("dspark_debug_flags");
+  unsigned* w = nullptr;
+  if (debug_word(&w) != hipSuccess || hipDeviceSynchronize() != hipSuccess) return DSPARK_E_LAUNCH;
+  unsigned v = 0;
+  if (hipMemcpy(&v, w, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return DSPARK_E_LAUNCH;
+  if (clear) {
+    const unsigned zero = 0;
+    if (hipMemcpy(w, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return DSPARK_E_LAUNCH;
+  }
+  *flags = v;
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status dspark_debug_check_inputs(const dspark_problem* P, const void* Z, const void* target,
+                                                   const int32_t* anchor, const float* T_table, hipStream_t stream) {
+  if (!kDebugChecks) return DSPARK_E_UNSUPPORTED;
+  const dspark_status st = check_problem(P);
+  if (st != DSPARK_OK) return st;
+  for (const void* q : {Z, target})
+    if (q && !aligned(q, 16)) return DSPARK_E_POINTER;
+  for (const void* q : {(const void*)anchor, (const void*)T_table})
+    if (q && !aligned(q, 4)) return DSPARK_E_POINTER;
+  const AbiRange range("dspark_debug_check_inputs");
+  (void)hipGetLastError();
+  const dspark_problem& p = *P;
+  const bool zb = p.logits_dtype == DSPARK_BF16;
+  if ((Z && debug_scan_nonfinite(Z, (size_t)p.B * p.K * p.V, zb, DSPARK_DEBUG_LOGITS, stream) != hipSuccess) ||
+      (target &&
+       debug_scan_nonfinite(target, (size_t)p.B * (p.K + 1) * p.V, zb, DSPARK_DEBUG_LOGITS, stream) != hipSuccess) ||
+      (anchor && debug_scan_range_i32(anchor, (size_t)p.B, 0, p.V - 1, DSPARK_DEBUG_IDS, stream) != hipSuccess) ||
+      !debug_schedule_inputs(p, nullptr, T_table, stream))
+    return DSPARK_E_LAUNCH;
+  return DSPARK_OK;
 }

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "../../include/dspark.h"
 #include "../../include/dspark_instr.h"
 #include "dspark_device.hpp"
@@ -197,6 +199,27 @@ hipError_t launch_select(const dspark_problem& P, const SelectArgs& a, hipStream
 // The persistent draft kernel: true when it serves P (bf16 logits and factors,
 // r = 256, B <= 256 and at most 5 chunks of the vocabulary per workgroup) and
 // the device can hold its whole grid at once.
+// One roctx range per ABI call (rocprofv3 --marker-trace shows them around the
+// call's kernels); pushed on entry, popped on every return.
+struct AbiRange {
+  explicit AbiRange(const char* name) { roctxRangePushA(name); }
+  ~AbiRange() { roctxRangePop(); }
+  AbiRange(const AbiRange&) = delete;
+  AbiRange& operator=(const AbiRange&) = delete;
+};
+
+// Debug checks (k_debug.hip): scans that raise bits of the current device's flag
+// word (whose address debug_word returns) instead of trapping.
+hipError_t debug_word(unsigned** out);
+hipError_t debug_scan_nonfinite(const void* x, size_t n, bool bf16, unsigned bit, hipStream_t s);
+hipError_t debug_scan_range_i32(const int32_t* x, size_t n, int32_t lo, int32_t hi, unsigned bit, hipStream_t s);
+hipError_t debug_scan_range_f32(const float* x, size_t n, float lo, float hi, unsigned bit, hipStream_t s);
+hipError_t debug_check_schedule(const int32_t* n_sched, const int32_t* n_total, int B, int K, unsigned bit,
+                                hipStream_t s);
+hipError_t debug_check_verify(const int32_t* n_sched, const int32_t* out_tok, const int32_t* n_acc,
+                              const int32_t* next_anchor, const float* resid_mass, int B, int K, int V, unsigned bit,
+                              hipStream_t s);
+
 // workgroups of the persistent draft launch: one per vocabulary chunk up to kStreamGridMax
 int persist_grid(int V);
 // dspark_draft takes the persistent draft where it applies and the batch is at

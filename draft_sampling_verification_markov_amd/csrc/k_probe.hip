@@ -32,6 +32,7 @@ using namespace dspark;
 extern "C" dspark_status dspark_probe_draws(uint64_t seed, const uint32_t* ctr, int32_t n, uint32_t* out_words,
                                             const uint32_t* w, int32_t m, float* uniform, float* gumbel,
                                             hipStream_t stream) {
+  const AbiRange range("dspark_probe_draws");
   if (n < 0 || m < 0) return DSPARK_E_INVALID;
   if (n > 0 && (!ctr || !out_words || (uintptr_t)ctr % 16 || (uintptr_t)out_words % 16)) return DSPARK_E_POINTER;
   if (m > 0 && (!w || !uniform || !gumbel || (uintptr_t)w % 4 || (uintptr_t)uniform % 4 || (uintptr_t)gumbel % 4))

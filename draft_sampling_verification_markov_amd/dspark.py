@@ -14,14 +14,18 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdspark.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libdspark_debug.so")  # built with DSPARK_DEBUG_CHECKS
 
 OK, E_INVALID, E_DTYPE, E_UNSUPPORTED, E_WORKSPACE, E_LAUNCH, E_POINTER = 0, -1, -2, -3, -4, -5, -6
 DRAFT_AUTO, DRAFT_PER_POSITION, DRAFT_PERSISTENT = 0, 1, 2  # schedules of the draft phase (dspark_instr.h)
+# flag bits of the debug build's checks (dspark_instr.h)
+DEBUG_LOGITS, DEBUG_FACTORS, DEBUG_IDS, DEBUG_SCHEDULE_INPUT, DEBUG_OUTPUT = 1, 2, 4, 8, 16
 F32, BF16 = 0, 1
 _DT = {"f32": F32, "bf16": BF16}
 _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 
-SYMBOLS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft", "dspark_draft_timed", "dspark_draft_path",
+SYMBOLS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft", "dspark_draft_timed", "dspark_draft_path", "dspark_debug_flags",
+           "dspark_debug_check_inputs",
            "dspark_schedule", "dspark_schedule_async", "dspark_schedule_fixed", "dspark_schedule_threshold",
            "dspark_sts_workspace_bytes", "dspark_sts_fit", "dspark_verify", "dspark_rnn_workspace_bytes",
            "dspark_draft_rnn", "dspark_verify_rnn", "dspark_schedule_noalloc",
@@ -52,18 +56,28 @@ class DsparkError(RuntimeError):
         self.status = status
 
 
-_lib = None
+_libs = {}
+_use_debug = False
 
 
-def load() -> ctypes.CDLL:
-    """Load libdspark.so (built by draft_sampling_verification_markov_amd.build); raises if absent."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise FileNotFoundError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+def use_debug_library(on: bool) -> None:
+    """Route every binding of this module through libdspark_debug.so (the same
+    kernels with input and output scans around each call) or back to libdspark.so."""
+    global _use_debug
+    _use_debug = bool(on)
+
+
+def load(debug: bool | None = None) -> ctypes.CDLL:
+    """Load libdspark.so, or libdspark_debug.so (both built by
+    draft_sampling_verification_markov_amd.build); raises if absent."""
+    debug = _use_debug if debug is None else debug
+    if debug in _libs:
+        return _libs[debug]
+    path = DEBUG_LIB_PATH if debug else LIB_PATH
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is missing: build it with __graft_entry__.build() "
                                 "or python -m draft_sampling_verification_markov_amd.build")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P = ctypes.POINTER(Problem)
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     lib.dspark_workspace_bytes.argtypes = [P]
@@ -100,7 +114,11 @@ def load() -> ctypes.CDLL:
     lib.dspark_draft_rnn.restype = i32
     lib.dspark_verify_rnn.argtypes = [P] + [vp] * 15 + [vp, sz, vp]
     lib.dspark_verify_rnn.restype = i32
-    _lib = lib
+    lib.dspark_debug_flags.argtypes = [vp, i32]
+    lib.dspark_debug_flags.restype = i32
+    lib.dspark_debug_check_inputs.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.dspark_debug_check_inputs.restype = i32
+    _libs[debug] = lib
     return lib
 
 
@@ -297,3 +315,20 @@ def verify_rnn(P: Problem, target, Z, E, Wt, anchor, draft_tok, draft_logq, draf
         _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
         _stream(stream))
     _check("dspark_verify_rnn", st)
+
+
+def debug_flags(clear: bool = True) -> int:
+    """dspark_debug_flags of libdspark_debug.so: the current device's flag word (synchronises)."""
+    v = ctypes.c_uint32()
+    _check("dspark_debug_flags", load(True).dspark_debug_flags(ctypes.byref(v), 1 if clear else 0))
+    return v.value
+
+
+def debug_check_inputs(P: Problem, Z=None, target=None, anchor=None, T_table=None, stream=None) -> None:
+    """dspark_debug_check_inputs of libdspark_debug.so: the input scans alone (None: not scanned)."""
+    lt = _TORCH_DT[P.logits_dtype]
+    st = load(True).dspark_debug_check_inputs(
+        ctypes.byref(P), None if Z is None else _ptr(Z, lt, "Z"), None if target is None else _ptr(target, lt, "target"),
+        None if anchor is None else _ptr(anchor, torch.int32, "anchor"),
+        None if T_table is None else _ptr(T_table, torch.float32, "T_table"), _stream(stream))
+    _check("dspark_debug_check_inputs", st)

@@ -3,9 +3,10 @@
  *
  * Not part of the draft -> schedule -> verify contract of dspark.h: these calls
  * exist so that a benchmark can time the library's kernels on the stream they
- * are launched on, and so that a test can read the device's random draws.  They
- * follow dspark.h's conventions (device pointers, caller-owned buffers, no
- * allocation, asynchronous on `stream`, validation before any launch).
+ * are launched on, so that a test can read the device's random draws, and for
+ * the debug build's checks.  They follow dspark.h's conventions (device
+ * pointers, caller-owned buffers, no allocation, asynchronous on `stream`,
+ * validation before any launch), except where a call says it synchronises.
  */
 #ifndef DSPARK_INSTR_H
 #define DSPARK_INSTR_H
@@ -78,6 +79,51 @@ int32_t dspark_draft_path(const dspark_problem* P);
  */
 dspark_status dspark_probe_draws(uint64_t seed, const uint32_t* ctr, int32_t n, uint32_t* out_words,
                                  const uint32_t* w, int32_t m, float* uniform, float* gumbel, hipStream_t stream);
+
+/*
+ * Debug checks.  The library built with DSPARK_DEBUG_CHECKS (libdspark_debug.so)
+ * scans every call's inputs before its kernels and its outputs after them with
+ * kernels of its own, on `stream`, and raises bits of a per-device flag word
+ * (never a trap; the call's results are those of the ordinary library, which
+ * these scans do not touch):
+ *   DSPARK_DEBUG_LOGITS          a non-finite base or target logit (NaN or infinity)
+ *   DSPARK_DEBUG_FACTORS         a non-finite entry of E, Wt, h or w_conf, or a tau
+ *                                outside (0, FLT_MAX]
+ *   DSPARK_DEBUG_IDS             an anchor or draft token outside [0, V)
+ *   DSPARK_DEBUG_SCHEDULE_INPUT  a survival outside [0, 1], a step-time entry not
+ *                                positive and finite, or an n_sched outside [0, K]
+ *   DSPARK_DEBUG_OUTPUT          an output outside its documented range (a token
+ *                                outside [0, V), log q > 0, a confidence or survival
+ *                                outside [0, 1], an n_sched outside [0, K] or an
+ *                                n_total other than B plus their sum, an accepted length above the
+ *                                schedule, a residual mass outside [0, 1])
+ * dspark.h leaves calls on inputs that break its contract undefined; these flags
+ * report them.  The ordinary library returns DSPARK_E_UNSUPPORTED from both calls.
+ */
+enum {
+  DSPARK_DEBUG_LOGITS = 1,
+  DSPARK_DEBUG_FACTORS = 2,
+  DSPARK_DEBUG_IDS = 4,
+  DSPARK_DEBUG_SCHEDULE_INPUT = 8,
+  DSPARK_DEBUG_OUTPUT = 16
+};
+
+/*
+ * dspark_debug_flags -- synchronises the current device, stores its flag word in
+ * *flags and, if `clear` is non-zero, resets it.  DSPARK_E_POINTER if flags is
+ * NULL.
+ */
+dspark_status dspark_debug_flags(uint32_t* flags, int32_t clear);
+
+/*
+ * dspark_debug_check_inputs -- the input scans alone, no other kernel: Z
+ * [B][K][V] and target [B][K+1][V] (logits dtype, 16-byte aligned) for
+ * non-finite logits, anchor [B] for ids outside [0, V), T_table [B*(K+1)+1] for
+ * entries not positive and finite.  Any of the four may be NULL (not scanned).
+ * Problem errors as dspark_draft.
+ */
+dspark_status dspark_debug_check_inputs(const dspark_problem* P, const void* Z, const void* target,
+                                        const int32_t* anchor, const float* T_table, hipStream_t stream);
 
 #ifdef __cplusplus
 }

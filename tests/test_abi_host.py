@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
                                           "dspark_status_string", "dspark_rnn_workspace_bytes", "dspark_draft_rnn",
                                           "dspark_verify_rnn", "dspark_schedule_noalloc"])
     # instrumentation, outside the step's contract
-    assert _declared([HEADERS[1]]) == ["dspark_draft_path", "dspark_draft_timed", "dspark_probe_draws"]
+    assert _declared([HEADERS[1]]) == ["dspark_debug_check_inputs", "dspark_debug_flags", "dspark_draft_path",
+                                       "dspark_draft_timed", "dspark_probe_draws"]
 
 
 def test_status_codes_are_the_contract(ds):
@@ -51,13 +52,35 @@ def test_status_codes_are_the_contract(ds):
     assert ds.status_string(-6) == "null or misaligned pointer argument"
 
 
-def test_library_exports_every_declared_symbol(ds):
-    out = subprocess.run(["nm", "-D", "--defined-only", ds.LIB_PATH], capture_output=True, text=True, check=True)
+@pytest.mark.parametrize("debug", [False, True], ids=["libdspark", "libdspark_debug"])
+def test_library_exports_every_declared_symbol(ds, debug):
+    path = ds.DEBUG_LIB_PATH if debug else ds.LIB_PATH
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True)
     exported = set(re.findall(r"\sT\s(dspark_\w+)", out.stdout))
     for name in _declared():
         assert name in exported, name
-        assert hasattr(ds.load(), name)
+        assert hasattr(ds.load(debug), name)
     assert set(ds.SYMBOLS) == set(_declared())
+    # one roctx range per ABI call
+    undefined = subprocess.run(["nm", "-D", "--undefined-only", path], capture_output=True, text=True,
+                               check=True).stdout
+    assert "roctxRangePushA" in undefined and "roctxRangePop" in undefined
+
+
+def test_debug_entry_points(ds):
+    # the ordinary library has no debug checks; the debug library validates
+    # before touching a device
+    plain, debug = ds.load(False), ds.load(True)
+    flags = ctypes.c_uint32()
+    assert plain.dspark_debug_flags(ctypes.byref(flags), 0) == ds.E_UNSUPPORTED
+    assert plain.dspark_debug_check_inputs(ctypes.byref(_P(ds)), None, None, None, None, None) == ds.E_UNSUPPORTED
+    assert debug.dspark_debug_flags(None, 0) == ds.E_POINTER
+    assert debug.dspark_debug_check_inputs(None, None, None, None, None, None) == ds.E_POINTER
+    assert debug.dspark_debug_check_inputs(ctypes.byref(_P(ds, B=0)), None, None, None, None, None) == ds.E_INVALID
+    assert debug.dspark_debug_check_inputs(ctypes.byref(_P(ds)), ctypes.c_void_p(0x1008), None, None, None,
+                                           None) == ds.E_POINTER
+    assert (ds.DEBUG_LOGITS, ds.DEBUG_FACTORS, ds.DEBUG_IDS, ds.DEBUG_SCHEDULE_INPUT, ds.DEBUG_OUTPUT) == \
+        (1, 2, 4, 8, 16)
 
 
 def test_header_compiles_as_c():
