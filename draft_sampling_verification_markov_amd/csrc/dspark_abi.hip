@@ -19,6 +19,9 @@ constexpr bool kDebugChecks = true;
 #else
 constexpr bool kDebugChecks = false;
 #endif
+// debug build: the persistent draft's barrier waits are made to time out
+// (dspark_debug_force_barrier_timeout), to exercise the bounded-wait path
+static bool g_debug_force_timeout = false;
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -243,11 +246,21 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
     pa.V = p.V;
     pa.nchunks = n_chunks(p.V);
     pa.z_bytes = (uint32_t)((size_t)p.B * p.K * p.V * 2);
+    pa.spin_limit = kPersistSpinLimit;
+    pa.arrive_extra = 0;
+    if (kDebugChecks && g_debug_force_timeout) {  // every barrier wait times out after a few polls
+      pa.spin_limit = 64;
+      pa.arrive_extra = 1;
+    }
     pa.scale2 = sa.scale2;
     pa.inv_T = se.inv_T;
     pa.key = sa.key;
     if (events && hipEventRecord(events[0], stream) != hipSuccess) return DSPARK_E_LAUNCH;
     if (launch_draft_persistent(p, pa, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+    // a barrier time-out (the flag word the kernel sets) raises its debug bit
+    if (kDebugChecks && debug_scan_range_i32(reinterpret_cast<const int32_t*>(pa.sync) + 16, 1, 0, 0,
+                                             DSPARK_DEBUG_BARRIER_TIMEOUT, stream) != hipSuccess)
+      return DSPARK_E_LAUNCH;
     if (events && hipEventRecord(events[1], stream) != hipSuccess) return DSPARK_E_LAUNCH;
   } else {
   float* Gh = rnn ? at<float>(workspace, L.total) : nullptr;
@@ -667,5 +680,11 @@ extern "C" dspark_status dspark_debug_check_inputs(const dspark_problem* P, cons
       (anchor && debug_scan_range_i32(anchor, (size_t)p.B, 0, p.V - 1, DSPARK_DEBUG_IDS, stream) != hipSuccess) ||
       !debug_schedule_inputs(p, nullptr, T_table, stream))
     return DSPARK_E_LAUNCH;
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status dspark_debug_force_barrier_timeout(int32_t on) {
+  if (!kDebugChecks) return DSPARK_E_UNSUPPORTED;
+  g_debug_force_timeout = on != 0;
   return DSPARK_OK;
 }

@@ -98,6 +98,8 @@ struct PersistArgs {
   int32_t* ptok;         // [B] tokens of the latest position
   unsigned* sync;        // [0] barrier counter (zero at launch), [16] time-out flag
   uint32_t z_bytes;      // bytes of Z (below 2^32)
+  uint32_t spin_limit;   // polls of a barrier wait before it gives up (kPersistSpinLimit)
+  uint32_t arrive_extra; // arrivals a barrier waits for beyond the grid's (0; 1 makes every wait time out)
   int B, K, V, nchunks;
   float scale2, inv_T;
   Key key;
@@ -225,6 +227,8 @@ int persist_grid(int V);
 // dspark_draft takes the persistent draft where it applies and the batch is at
 // most this (above it the per-position kernels, with two waves per SIMD, are faster)
 constexpr int kPersistMaxB = 48;
+// polls of a persistent-draft barrier wait before it sets the time-out flag
+constexpr uint32_t kPersistSpinLimit = 1u << 20;
 bool draft_persistent_supported(const dspark_problem& P);
 hipError_t launch_draft_persistent(const dspark_problem& P, const PersistArgs& a, hipStream_t s);
 hipError_t launch_conf(const dspark_problem& P, const ConfArgs& a, hipStream_t s);

@@ -50,7 +50,6 @@ constexpr int kPMt = 5;                  // M-tiles of 32 entries per wave
 constexpr int kPMtWg = kPWaves * kPMt;   // per workgroup: 5 chunks
 constexpr int kPRows = 256;              // rows of the batch at most
 constexpr int kPHalf = 128;              // rows whose M-tile partials are merged at once
-constexpr unsigned kSpinLimit = 1u << 20;
 
 // MFMA row rho of an M-tile -> vocabulary entry within it: in the 32x32
 // accumulator layout lane l then holds 16 consecutive entries 16*(l/32)..+15
@@ -91,20 +90,20 @@ __device__ __forceinline__ float4 ld_agent4(const float4* p) {
 // Grid barrier on a monotonic arrival counter, in two halves so that loads
 // independent of the other workgroups can be issued between them: arrive
 // (this workgroup's stores past the L2 complete, then one atomic add) and wait
-// (until all G workgroups of the epoch have arrived).  Bounded: past kSpinLimit
-// polls the flag is set and this and every later wait return at once.
+// (until `expect` arrivals per epoch: the G workgroups).  Bounded: past
+// `limit` polls the flag is set and this and every later wait return at once.
 __device__ __forceinline__ void grid_arrive(unsigned* sync, unsigned& epoch) {
   wait_vmem();
   __syncthreads();
   epoch += 1;
   if (threadIdx.x == 0) __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void grid_wait(unsigned* sync, unsigned G, unsigned epoch) {
+__device__ __forceinline__ void grid_wait(unsigned* sync, unsigned expect, unsigned epoch, unsigned limit) {
   if (threadIdx.x == 0) {
-    const unsigned target = epoch * G;
-    unsigned spins = ld_agent(sync + 16) ? kSpinLimit : 0u;
+    const unsigned target = epoch * expect;
+    unsigned spins = ld_agent(sync + 16) ? limit : 0u;
     while (ld_agent(sync) < target) {
-      if (++spins > kSpinLimit) {
+      if (++spins > limit) {
         st_agent(sync + 16, 1u);
         break;
       }
@@ -398,7 +397,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
 
     // 4. every workgroup's partials of position k are out
     grid_arrive(a.sync, epoch);
-    grid_wait(a.sync, (unsigned)G, epoch);
+    grid_wait(a.sync, (unsigned)G + a.arrive_extra, epoch, a.spin_limit);
 
     // 5. selection of rows g, g + G, ...
     for (int b = g; b < B; b += G) {
@@ -503,7 +502,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
     // the next position's first base logits (they do not depend on the tokens)
     grid_arrive(a.sync, epoch);
     if (k < K) zload(k + 1, 0, zA);
-    grid_wait(a.sync, (unsigned)G, epoch);
+    grid_wait(a.sync, (unsigned)G + a.arrive_extra, epoch, a.spin_limit);
   }
 }
 

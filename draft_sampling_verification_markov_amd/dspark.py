@@ -20,12 +20,13 @@ OK, E_INVALID, E_DTYPE, E_UNSUPPORTED, E_WORKSPACE, E_LAUNCH, E_POINTER = 0, -1,
 DRAFT_AUTO, DRAFT_PER_POSITION, DRAFT_PERSISTENT = 0, 1, 2  # schedules of the draft phase (dspark_instr.h)
 # flag bits of the debug build's checks (dspark_instr.h)
 DEBUG_LOGITS, DEBUG_FACTORS, DEBUG_IDS, DEBUG_SCHEDULE_INPUT, DEBUG_OUTPUT = 1, 2, 4, 8, 16
+DEBUG_BARRIER_TIMEOUT = 32
 F32, BF16 = 0, 1
 _DT = {"f32": F32, "bf16": BF16}
 _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 
-SYMBOLS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft", "dspark_draft_timed", "dspark_draft_path", "dspark_debug_flags",
-           "dspark_debug_check_inputs",
+SYMBOLS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft", "dspark_draft_timed", "dspark_draft_path",
+           "dspark_debug_flags", "dspark_debug_check_inputs", "dspark_debug_force_barrier_timeout",
            "dspark_schedule", "dspark_schedule_async", "dspark_schedule_fixed", "dspark_schedule_threshold",
            "dspark_sts_workspace_bytes", "dspark_sts_fit", "dspark_verify", "dspark_rnn_workspace_bytes",
            "dspark_draft_rnn", "dspark_verify_rnn", "dspark_schedule_noalloc",
@@ -118,6 +119,8 @@ def load(debug: bool | None = None) -> ctypes.CDLL:
     lib.dspark_debug_flags.restype = i32
     lib.dspark_debug_check_inputs.argtypes = [P, vp, vp, vp, vp, vp]
     lib.dspark_debug_check_inputs.restype = i32
+    lib.dspark_debug_force_barrier_timeout.argtypes = [i32]
+    lib.dspark_debug_force_barrier_timeout.restype = i32
     _libs[debug] = lib
     return lib
 
@@ -332,3 +335,8 @@ def debug_check_inputs(P: Problem, Z=None, target=None, anchor=None, T_table=Non
         None if anchor is None else _ptr(anchor, torch.int32, "anchor"),
         None if T_table is None else _ptr(T_table, torch.float32, "T_table"), _stream(stream))
     _check("dspark_debug_check_inputs", st)
+
+
+def debug_force_barrier_timeout(on: bool) -> None:
+    """dspark_debug_force_barrier_timeout of libdspark_debug.so."""
+    _check("dspark_debug_force_barrier_timeout", load(True).dspark_debug_force_barrier_timeout(1 if on else 0))

@@ -97,6 +97,8 @@ dspark_status dspark_probe_draws(uint64_t seed, const uint32_t* ctr, int32_t n, 
  *                                outside [0, 1], an n_sched outside [0, K] or an
  *                                n_total other than B plus their sum, an accepted length above the
  *                                schedule, a residual mass outside [0, 1])
+ *   DSPARK_DEBUG_BARRIER_TIMEOUT a grid-barrier wait of the persistent draft gave up
+ *                                (its results are then unspecified)
  * dspark.h leaves calls on inputs that break its contract undefined; these flags
  * report them.  The ordinary library returns DSPARK_E_UNSUPPORTED from both calls.
  */
@@ -105,7 +107,8 @@ enum {
   DSPARK_DEBUG_FACTORS = 2,
   DSPARK_DEBUG_IDS = 4,
   DSPARK_DEBUG_SCHEDULE_INPUT = 8,
-  DSPARK_DEBUG_OUTPUT = 16
+  DSPARK_DEBUG_OUTPUT = 16,
+  DSPARK_DEBUG_BARRIER_TIMEOUT = 32
 };
 
 /*
@@ -124,6 +127,16 @@ dspark_status dspark_debug_flags(uint32_t* flags, int32_t clear);
  */
 dspark_status dspark_debug_check_inputs(const dspark_problem* P, const void* Z, const void* target,
                                         const int32_t* anchor, const float* T_table, hipStream_t stream);
+
+/*
+ * dspark_debug_force_barrier_timeout -- with on != 0, every later persistent
+ * draft of this process makes its grid-barrier waits unreachable and bounded by
+ * a few polls, so that each wait gives up, sets the time-out flag and every
+ * workgroup still runs to the end (the draft's results are then unspecified and
+ * DSPARK_DEBUG_BARRIER_TIMEOUT is raised); on == 0 restores normal waits.  A
+ * test of the bounded-wait path; debug build only.
+ */
+dspark_status dspark_debug_force_barrier_timeout(int32_t on);
 
 #ifdef __cplusplus
 }

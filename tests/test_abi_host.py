@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
                                           "dspark_status_string", "dspark_rnn_workspace_bytes", "dspark_draft_rnn",
                                           "dspark_verify_rnn", "dspark_schedule_noalloc"])
     # instrumentation, outside the step's contract
-    assert _declared([HEADERS[1]]) == ["dspark_debug_check_inputs", "dspark_debug_flags", "dspark_draft_path",
+    assert _declared([HEADERS[1]]) == ["dspark_debug_check_inputs", "dspark_debug_flags",
+                                       "dspark_debug_force_barrier_timeout", "dspark_draft_path",
                                        "dspark_draft_timed", "dspark_probe_draws"]
 
 
@@ -74,13 +75,15 @@ def test_debug_entry_points(ds):
     flags = ctypes.c_uint32()
     assert plain.dspark_debug_flags(ctypes.byref(flags), 0) == ds.E_UNSUPPORTED
     assert plain.dspark_debug_check_inputs(ctypes.byref(_P(ds)), None, None, None, None, None) == ds.E_UNSUPPORTED
+    assert plain.dspark_debug_force_barrier_timeout(1) == ds.E_UNSUPPORTED
+    assert debug.dspark_debug_force_barrier_timeout(0) == ds.OK
     assert debug.dspark_debug_flags(None, 0) == ds.E_POINTER
     assert debug.dspark_debug_check_inputs(None, None, None, None, None, None) == ds.E_POINTER
     assert debug.dspark_debug_check_inputs(ctypes.byref(_P(ds, B=0)), None, None, None, None, None) == ds.E_INVALID
     assert debug.dspark_debug_check_inputs(ctypes.byref(_P(ds)), ctypes.c_void_p(0x1008), None, None, None,
                                            None) == ds.E_POINTER
-    assert (ds.DEBUG_LOGITS, ds.DEBUG_FACTORS, ds.DEBUG_IDS, ds.DEBUG_SCHEDULE_INPUT, ds.DEBUG_OUTPUT) == \
-        (1, 2, 4, 8, 16)
+    assert (ds.DEBUG_LOGITS, ds.DEBUG_FACTORS, ds.DEBUG_IDS, ds.DEBUG_SCHEDULE_INPUT, ds.DEBUG_OUTPUT,
+            ds.DEBUG_BARRIER_TIMEOUT) == (1, 2, 4, 8, 16, 32)
 
 
 def test_header_compiles_as_c():

@@ -4,7 +4,9 @@ A whole cycle through it gives bit-identical results to the ordinary library and
 raises no flag; its input scans, run alone (no other kernel sees the planted
 values), raise exactly the flag of each planted contract violation: a NaN or an
 infinity among bf16 and fp32 logits, an anchor outside [0, V), a step-time
-entry that is zero or NaN.
+entry that is zero or NaN.  The persistent draft's bounded barrier waits, made
+unreachable from the host, give up, raise their flag and let every workgroup
+run to the end; normal waits afterwards give the ordinary library's tokens.
 """
 from __future__ import annotations
 
@@ -104,3 +106,36 @@ def test_debug_input_scans_flag_planted_violations(lib, logits):
         assert flags_of(T_table=t) == dspark.DEBUG_SCHEDULE_INPUT, bad
     # several at once: their bits together
     assert flags_of(Z=Zn, anchor=torch.full_like(anchor, V)) == dspark.DEBUG_LOGITS | dspark.DEBUG_IDS
+
+
+def test_persistent_barrier_timeout_ends_and_is_flagged(lib):
+    dspark, runner = lib
+    cfg = synth.get_config("tbias_bf16")
+    P = dspark.Problem.from_config(cfg)
+    assert dspark.draft_path(P) == dspark.DRAFT_PERSISTENT
+    _say(f"[gpu] persistent draft with unreachable barriers, B={cfg.B} K={cfg.K} V={cfg.V}")
+    inp = synth.make_inputs(cfg)
+    x = runner.CycleInputs.upload(inp)
+    o = runner.CycleOutputs(P)
+    runner.draft(P, x, o)
+    torch.cuda.synchronize()
+    ref = o.tok.cpu().numpy().copy()
+    dspark.use_debug_library(True)
+    try:
+        dspark.debug_flags(clear=True)
+        dspark.debug_force_barrier_timeout(True)
+        try:
+            runner.draft(P, x, o)
+            torch.cuda.synchronize()
+        finally:
+            dspark.debug_force_barrier_timeout(False)
+        flags = dspark.debug_flags(clear=True)
+        assert flags & dspark.DEBUG_BARRIER_TIMEOUT, flags
+        tok = o.tok.cpu().numpy()
+        assert ((tok >= 0) & (tok < cfg.V)).all()   # every workgroup ran to its end
+        runner.draft(P, x, o)
+        torch.cuda.synchronize()
+        assert dspark.debug_flags(clear=True) == 0
+        np.testing.assert_array_equal(o.tok.cpu().numpy(), ref)
+    finally:
+        dspark.use_debug_library(False)

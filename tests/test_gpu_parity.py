@@ -130,23 +130,40 @@ def test_full_size(lib, name):
     _say(f"[gpu]   low-margin differences {counts}; N = {int(g['n_total'][0])}")
 
 
-# Both schedules of the draft phase (dspark_instr.h) where dspark_draft would
-# take the other one: the persistent kernel at the full batch, and with a
-# ragged batch and vocabulary and more rows than workgroups; the per-position
-# kernels at a small bf16 batch.
+# Both schedules of the draft phase (dspark_instr.h): each where dspark_draft
+# would take the other one (the persistent kernel at the full batch, the
+# per-position kernels at a small bf16 batch), and the persistent kernel at its
+# edges: one request, one position, a vocabulary of one chunk (one workgroup
+# selecting every row) and of one chunk plus a ragged 8 entries, a ragged batch
+# with more rows than workgroups, and the largest batch it takes by default.
 SCHEDULES = [
     ("high_concurrency", 2),
-    ("persist_ragged", 2),
     ("tbias_bf16", 1),
+    ("persist_ragged", 2),
+    ("persist_b1", 2),
+    ("persist_k1", 2),
+    ("persist_v128", 2),
+    ("persist_v136", 2),
+    ("persist_b48", 2),
 ]
 
 
 def _schedule_cfg(name):
+    base = synth.get_config("tbias_bf16")
     if name == "persist_ragged":
         # 33 rows (a ragged N-tile), V = 1000 (a ragged last chunk and M-tile), 8 chunks: 8 workgroups
         # selecting 4-5 rows each
-        return synth.get_config("tbias_bf16").replace(name="persist_ragged", B=33, K=3, V=1000, r=256, d=64,
-                                                      seed=15)
+        return base.replace(name=name, B=33, K=3, V=1000, r=256, d=64, seed=15)
+    if name == "persist_b1":
+        return base.replace(name=name, B=1, K=5, seed=16)
+    if name == "persist_k1":
+        return base.replace(name=name, K=1, seed=17)
+    if name == "persist_v128":
+        return base.replace(name=name, B=20, K=3, V=128, d=64, seed=18)
+    if name == "persist_v136":
+        return base.replace(name=name, B=20, K=3, V=136, d=64, seed=19)
+    if name == "persist_b48":
+        return synth.get_config("high_concurrency").replace(name=name, B=48, K=4, seed=20)
     return synth.get_config(name)
 
 
@@ -158,7 +175,8 @@ def test_draft_schedules(lib, name, path):
     P = dspark.Problem.from_config(cfg)
     auto = dspark.draft_path(P)
     _say(f"[gpu] schedule {path} on {name} B={cfg.B} K={cfg.K} V={cfg.V} (dspark_draft takes {auto})")
-    assert auto != path or name == "persist_ragged"
+    if name in ("high_concurrency", "tbias_bf16"):
+        assert auto != path   # the schedule dspark_draft does not take there
     inp = synth.make_inputs(cfg)
     g = gpu_cycle(lib, cfg, inp, path=path)
     counts = check(cfg, inp, g)
