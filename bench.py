@@ -109,18 +109,18 @@ class Hip:
             self.lib.hipEventDestroy(h)
 
 
-PERSIST_MAX_B = 48  # dspark_draft's batch limit for the persistent schedule
+PERSIST_MAX_B = {"bf16": 48, "f32": 96}  # dspark_draft's batch limits for the persistent schedule, by logits dtype
 
 
 def draft_persistent(cfg) -> bool:
     """Whether dspark_draft takes the persistent draft schedule for this workload
-    (the library's rule, which dspark_draft_path reports on the GPU: bf16 logits
-    and factors, rank 256, at most 5 vocabulary chunks per workgroup, and at most
-    PERSIST_MAX_B requests)."""
+    (the library's rule, which dspark_draft_path reports on the GPU: bf16 or fp32
+    logits, bf16 factors, rank 256, at most 5 vocabulary chunks per workgroup, and
+    at most PERSIST_MAX_B requests)."""
     nc = (cfg.V + 127) // 128
     G = min(nc, 256)
-    return (cfg.logits_dtype == "bf16" and cfg.weight_dtype == "bf16" and cfg.r == 256
-            and cfg.B <= PERSIST_MAX_B and -(-nc // G) <= 5)
+    return (cfg.logits_dtype in ("bf16", "f32") and cfg.weight_dtype == "bf16" and cfg.r == 256
+            and cfg.B <= PERSIST_MAX_B[cfg.logits_dtype] and -(-nc // G) <= 5)
 
 
 DOMINANT = "k_draft_persist"  # the kernel of the draft phase (all K positions in one launch)

@@ -228,7 +228,7 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
   (void)hipGetLastError();
   const bool persist_ok = !rnn && capture == hipStreamCaptureStatusNone && draft_persistent_supported(p);
   if (path == DSPARK_DRAFT_PERSISTENT && !persist_ok) return DSPARK_E_UNSUPPORTED;
-  if (path == DSPARK_DRAFT_PERSISTENT || (path == DSPARK_DRAFT_AUTO && persist_ok && p.B <= kPersistMaxB)) {
+  if (path == DSPARK_DRAFT_PERSISTENT || (path == DSPARK_DRAFT_AUTO && persist_ok && p.B <= persist_max_b(p))) {
     // every position in one cooperative launch, Wt slices held on chip
     PersistArgs pa{};
     pa.Z = Z;
@@ -245,7 +245,7 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
     pa.K = p.K;
     pa.V = p.V;
     pa.nchunks = n_chunks(p.V);
-    pa.z_bytes = (uint32_t)((size_t)p.B * p.K * p.V * 2);
+    pa.z_bytes = (uint32_t)((size_t)p.B * p.K * p.V * (p.logits_dtype == DSPARK_F32 ? 4 : 2));
     pa.spin_limit = kPersistSpinLimit;
     pa.arrive_extra = 0;
     if (kDebugChecks && g_debug_force_timeout) {  // every barrier wait times out after a few polls
@@ -332,7 +332,7 @@ extern "C" dspark_status dspark_draft_timed(const dspark_problem* P, const void*
 extern "C" int32_t dspark_draft_path(const dspark_problem* P) {
   const dspark_status st = check_problem(P);
   if (st != DSPARK_OK) return st;
-  return draft_persistent_supported(*P) && P->B <= kPersistMaxB ? DSPARK_DRAFT_PERSISTENT : DSPARK_DRAFT_PER_POSITION;
+  return draft_persistent_supported(*P) && P->B <= persist_max_b(*P) ? DSPARK_DRAFT_PERSISTENT : DSPARK_DRAFT_PER_POSITION;
 }
 
 extern "C" size_t dspark_rnn_workspace_bytes(const dspark_problem* P) {

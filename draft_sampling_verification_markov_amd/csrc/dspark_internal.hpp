@@ -225,8 +225,9 @@ hipError_t debug_check_verify(const int32_t* n_sched, const int32_t* out_tok, co
 // workgroups of the persistent draft launch: one per vocabulary chunk up to kStreamGridMax
 int persist_grid(int V);
 // dspark_draft takes the persistent draft where it applies and the batch is at
-// most this (above it the per-position kernels, with two waves per SIMD, are faster)
-constexpr int kPersistMaxB = 48;
+// most this (the measured crossovers: above them the per-position kernels, with
+// two waves per SIMD, are faster; with fp32 logits they stream twice the bytes)
+inline int persist_max_b(const dspark_problem& P) { return P.logits_dtype == DSPARK_F32 ? 96 : 48; }
 // polls of a persistent-draft barrier wait before it sets the time-out flag
 constexpr uint32_t kPersistSpinLimit = 1u << 20;
 bool draft_persistent_supported(const dspark_problem& P);

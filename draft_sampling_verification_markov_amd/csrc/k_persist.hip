@@ -133,9 +133,19 @@ __device__ __forceinline__ uint32_t quad_pick(const Words4& q, int i) {
   return (i & 2) ? hi : lo;
 }
 
-template <int R>
+// Word i (0..3, a constant after unrolling) of a 16-byte piece.
+__device__ __forceinline__ uint32_t u4get(const uint4& q, int i) { return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w; }
+
+// ZT: the base logits' type (uint16_t: bf16; float: fp32)
+template <int R, typename ZT>
 __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
   static_assert(R == 256, "one factor row per 32 lanes of a gather instruction");
+  // fp32 base logits: one register set of 16-byte pieces per M-tile, refilled
+  // in place as each M-tile's epilogue has read it (two sets would not fit
+  // beside the 256 registers of Wt); bf16: two sets, the next N-tile's loaded whole
+  constexpr bool kF32 = sizeof(ZT) == 4;
+  constexpr int ZP = (int)sizeof(ZT);             // 16-byte pieces of a lane's 16 entries: 2 (bf16) or 4 (fp32)
+  constexpr int EPP = 16 / (int)sizeof(ZT);      // entries per piece
   constexpr int S = R / 16;          // MFMA K-steps (16 ranks each)
   constexpr int ROWB = R * 2;        // bytes of a factor row
   constexpr int PR = R / 8;          // 16-byte pieces of a factor row
@@ -166,7 +176,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
   const int V = a.V, K = a.K, B = a.B;
   const uint16_t* Wt = static_cast<const uint16_t*>(a.Wt);
   const uint16_t* E = static_cast<const uint16_t*>(a.E);
-  const uint16_t* Z = static_cast<const uint16_t*>(a.Z);
+  const ZT* Z = static_cast<const ZT*>(a.Z);
   const float scale2 = a.scale2;
   const int vbase = c_begin * kChunk;
 
@@ -190,29 +200,38 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
     }
   }
 
-  // base logits of this lane's 16 entries of each of the wave's M-tiles of
-  // N-tile nt at position kk: ten 16-byte buffer loads, always issued (rows
-  // past B read row B - 1).  A piece past V (wholly past it, as V % 8 == 0) is
-  // read at an offset past the end of Z, where the buffer returns zeros; its
-  // bits are set to -inf where it is used.
+  // base logits of this lane's 16 entries of M-tile j of N-tile nt at position
+  // kk: ZP 16-byte buffer loads, always issued (rows past B read row B - 1).
+  // A piece past V (wholly past it, as V % 8 == 0) is read at an offset past
+  // the end of Z, where the buffer returns zeros; its bits are set to -inf
+  // where it is used.
   const int NT = (B + 31) / 32;
   const __amdgpu_buffer_rsrc_t zrs = make_rsrc(Z, a.z_bytes);
   const __amdgpu_buffer_rsrc_t ers = make_rsrc(E, (uint32_t)V * ROWB);
   const int vlane = vbase + wave * kPMt * 32 + 16 * h;  // this lane's first entry of the wave's M-tiles
   const int vleft = V - vlane;
-  auto zload = [&](int kk, int nt, uint4 (&z)[kPMt][2]) {
+  auto zload_one = [&](int kk, int nt, int j, uint4 (&zj)[ZP]) {
     const int row = nt * 32 + l32;
     const int zr = row < B ? row : B - 1;
-    const uint32_t off = (uint32_t)((((size_t)zr * K + (kk - 1)) * V + vlane) * 2);
+    const uint32_t off = (uint32_t)((((size_t)zr * K + (kk - 1)) * V + vlane) * sizeof(ZT));
 #pragma unroll
-    for (int j = 0; j < kPMt; ++j)
+    for (int p = 0; p < ZP; ++p) {
+      const bool in = j * 32 + EPP * p < vleft;
+      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(
+          zrs, (int)(in ? off + (uint32_t)(j * 32 * (int)sizeof(ZT) + 16 * p) : a.z_bytes), 0, 0);
+      zj[p] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
+  };
+  auto zload = [&](int kk, int nt, uint4 (&z)[kPMt][ZP]) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const bool in = j * 32 + 8 * p < vleft;
-        const u32x4_t x =
-            __builtin_amdgcn_raw_buffer_load_b128(zrs, (int)(in ? off + (uint32_t)(j * 64 + 16 * p) : a.z_bytes), 0, 0);
-        z[j][p] = make_uint4(x[0], x[1], x[2], x[3]);
-      }
+    for (int j = 0; j < kPMt; ++j) zload_one(kk, nt, j, z[j]);
+  };
+  // entry e (0..15) of M-tile j from its pieces, -inf past V
+  auto zval = [&](int j, const uint4 (&zj)[ZP], int e) -> float {
+    const int p = e / EPP;
+    if (kF32) return __uint_as_float(u4get(zj[p], e & 3) | (j * 32 + EPP * p < vleft ? 0u : 0xFF800000u));
+    const uint32_t w = u4get(zj[p], (e >> 1) & 3) | (j * 32 + EPP * p < vleft ? 0u : 0xFF80FF80u);
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
   };
   // E rows of N-tile nt's previous tokens into dst, by LDS DMA: instruction q
   // fills slots 64q .. 64q + 63, lane i slot 64q + i (a padding slot loads
@@ -263,16 +282,13 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
   };
   // the reduction of one (N-tile, M-tile) accumulator: logits = base + Markov
   // term (one rounding), then (max, sum of 2^(x - max)) in base 2 into LDS
-  auto epilogue = [&](int nt, int j, const f32x16_t& acc, const uint4 (&zj)[2]) {
-    const uint32_t n0 = j * 32 < vleft ? 0u : 0xFF80FF80u, n1 = j * 32 + 8 < vleft ? 0u : 0xFF80FF80u;
-    const uint32_t zw[8] = {zj[0].x | n0, zj[0].y | n0, zj[0].z | n0, zj[0].w | n0,
-                            zj[1].x | n1, zj[1].y | n1, zj[1].z | n1, zj[1].w | n1};
+  auto epilogue = [&](int nt, int j, const f32x16_t& acc, const uint4 (&zj)[ZP]) {
     float ell[16];
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      ell[2 * i] = bf16_lo(zw[i]) + acc[2 * i];
-      ell[2 * i + 1] = bf16_hi(zw[i]) + acc[2 * i + 1];
+      ell[2 * i] = zval(j, zj, 2 * i) + acc[2 * i];
+      ell[2 * i + 1] = zval(j, zj, 2 * i + 1) + acc[2 * i + 1];
       m = fmaxf(m, fmaxf(ell[2 * i], ell[2 * i + 1]));
     }
     m = halves32_max(m);
@@ -285,35 +301,33 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
     s_tp[((nt & 3) * 32 + l32) * kPMtWg + wave * kPMt + j] = make_float2(m * scale2, sm);
   };
   // N-tile nt of position k: its E rows are in cur and its base logits in
-  // zc; the next N-tile's rows (into nxt) and base logits (into zn) are
-  // requested first, a whole N-tile of MFMA work ahead of their use
-  auto tile = [&](int k, int nt, uint4 (&zc)[kPMt][2], uint4 (&zn)[kPMt][2], const unsigned char* cur,
+  // zc; the next N-tile's rows (into nxt) are requested first, and its base
+  // logits (bf16: into zn, at once; fp32: into zc, each M-tile's as soon as its
+  // epilogue has read them, always issued) well ahead of their use
+  auto tile = [&](int k, int nt, uint4 (&zc)[kPMt][ZP], uint4 (&zn)[kPMt][ZP], const unsigned char* cur,
                   unsigned char* nxt) {
     const bool more = nt + 1 < NT;
-    if (more) {
-      gather(nt + 1, nxt);
-      zload(k, nt + 1, zn);
-    }
+    if (more) gather(nt + 1, nxt);
+    if (!kF32 && more) zload(k, nt + 1, zn);
     const unsigned char* brow = cur + (l32 * RS + h) * 16;
     auto bfrag = [&](int t) { return *reinterpret_cast<const bf16x8_t*>(brow + 32 * t); };
     // Every M-tile is computed (a missing one has zero fragments and its
     // result is never read).  Stage j chains M-tile j's 16 MFMAs, its LDS
-    // fragments read three K-steps ahead, and gives each K-step a fixed slice
+    // fragments read D K-steps ahead, and gives each K-step a fixed slice
     // of M-tile j-1's epilogue: steps 0-7 form the logits and their maximum,
     // step 8 merges the column halves, steps 9-15 the exponentials and sums.
     // Scheduling barriers keep the slices where they are written.
-    auto stage = [&](int j, int pj, const f32x16_t& pacc, const uint4 (&pz)[2]) {
+    auto stage = [&](int j, int pj, const f32x16_t& pacc, uint4 (&pz)[ZP]) {
       f32x16_t acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      constexpr int D = 3;
+      constexpr int D = kF32 ? 2 : 3;  // fp32: a shorter ring leaves the registers the refills need
       bf16x8_t bq[D + 1], aq[D + 1];
 #pragma unroll
       for (int t = 0; t < D; ++t) {
         bq[t] = bfrag(t);
         if (j >= JR) aq[t] = s_a[wave][t][lane];
       }
-      const uint32_t n0 = pj * 32 < vleft ? 0u : 0xFF80FF80u, n1 = pj * 32 + 8 < vleft ? 0u : 0xFF80FF80u;
       float ell[16], m = -INFINITY, off = 0.f, s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int t = 0; t < S; ++t) {
@@ -325,15 +339,13 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
                                                       bq[t % (D + 1)], acc, 0, 0, 0);
         if (pj >= 0) {
           if (t < 8) {
-            const uint32_t w = (t < 4 ? (t == 0 ? pz[0].x : t == 1 ? pz[0].y : t == 2 ? pz[0].z : pz[0].w)
-                                      : (t == 4 ? pz[1].x : t == 5 ? pz[1].y : t == 6 ? pz[1].z : pz[1].w)) |
-                               (t < 4 ? n0 : n1);
-            ell[2 * t] = bf16_lo(w) + pacc[2 * t];
-            ell[2 * t + 1] = bf16_hi(w) + pacc[2 * t + 1];
+            ell[2 * t] = zval(pj, pz, 2 * t) + pacc[2 * t];
+            ell[2 * t + 1] = zval(pj, pz, 2 * t + 1) + pacc[2 * t + 1];
             m = fmaxf(m, fmaxf(ell[2 * t], ell[2 * t + 1]));
           } else if (t == 8) {
             m = halves32_max(m);
             off = m == -INFINITY ? 0.f : -m * scale2;
+            if (kF32) zload_one(k, nt + 1, pj, pz);  // read: refill with the next N-tile's
           } else {
             // steps 9..14 two entries each, step 15 the last four
             const int e0 = 2 * (t - 9), e1 = t == 15 ? 16 : e0 + 2;
@@ -363,15 +375,21 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
     a1 = stage(3, 2, a0, zc[2]);
     a0 = stage(4, 3, a1, zc[3]);
     epilogue(nt, 4, a0, zc[4]);
-    // this wave's gather of N-tile nt + 1 (and its base-logit loads, issued
-    // with it) are complete; after the barrier every wave's rows are in and no
+    // this wave's gather of N-tile nt + 1 is complete (bf16: and the base
+    // logits loaded with it; fp32: the kPMt * ZP refills issued after it may
+    // still be in flight); after the barrier every wave's rows are in and no
     // wave reads cur any more
-    wait_vmem();
+    if (kF32) {
+      zload_one(k, nt + 1, kPMt - 1, zc[kPMt - 1]);
+      wait_vmem_n<kPMt * ZP>();
+    } else {
+      wait_vmem();
+    }
     barrier_lds_only();
     if ((nt & 3) == 3 || !more) merge(k, nt >> 2);
   };
 
-  uint4 zA[kPMt][2], zB[kPMt][2];
+  uint4 zA[kPMt][ZP], zB[kPMt][kF32 ? 1 : ZP];
   zload(1, 0, zA);
 
   unsigned epoch = 0;
@@ -388,11 +406,16 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
     wait_vmem();
     __syncthreads();
 
-    // 2-3. the vocabulary stream, N-tile after N-tile, base-logit registers
-    // alternating between zA and zB
+    // 2-3. the vocabulary stream, N-tile after N-tile (bf16: base-logit
+    // registers alternating between zA and zB; fp32: zA refilled in place)
     for (int nt = 0; nt < NT; nt += 2) {
-      tile(k, nt, zA, zB, s_b0, s_b1);
-      if (nt + 1 < NT) tile(k, nt + 1, zB, zA, s_b1, s_b0);
+      if constexpr (kF32) {
+        tile(k, nt, zA, zA, s_b0, s_b1);
+        if (nt + 1 < NT) tile(k, nt + 1, zA, zA, s_b1, s_b0);
+      } else {
+        tile(k, nt, zA, zB, s_b0, s_b1);
+        if (nt + 1 < NT) tile(k, nt + 1, zB, zA, s_b1, s_b0);
+      }
     }
 
     // 4. every workgroup's partials of position k are out
@@ -445,7 +468,8 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
       const int r = tid & (kChunk - 1);
       const int v = v0 + r;
       const bool inside = tid < kChunk && r < nrow;
-      const float zb = bf16_to_f32(Z[((size_t)b * K + (k - 1)) * V + (r < nrow ? v : v0)]);
+      const ZT zraw = Z[((size_t)b * K + (k - 1)) * V + (r < nrow ? v : v0)];
+      const float zb = kF32 ? (float)zraw : bf16_to_f32((uint16_t)zraw);
       const float gum = gumbel_from_word(draw_word(a.key, (uint32_t)v, (uint32_t)b, (uint32_t)k, kDraftElem));
       __syncthreads();  // s_tp is reused for the dot partials
       float* s_part = reinterpret_cast<float*>(s_tp);
@@ -518,21 +542,26 @@ int persist_grid(int V) {
 }
 
 bool draft_persistent_supported(const dspark_problem& P) {
-  if (P.logits_dtype != DSPARK_BF16 || P.weight_dtype != DSPARK_BF16 || P.r != 256 || P.B > kPRows) return false;
-  if ((size_t)P.B * P.K * P.V * 2 > 0xFFFFFFFFull || (size_t)P.V * 512 > 0xFFFFFFFFull) return false;  // 32-bit buffer offsets
+  if ((P.logits_dtype != DSPARK_BF16 && P.logits_dtype != DSPARK_F32) || P.weight_dtype != DSPARK_BF16 ||
+      P.r != 256 || P.B > kPRows)
+    return false;
+  const size_t zsize = P.logits_dtype == DSPARK_F32 ? 4 : 2;
+  if ((size_t)P.B * P.K * P.V * zsize > 0xFFFFFFFFull || (size_t)P.V * 512 > 0xFFFFFFFFull) return false;  // 32-bit buffer offsets
   const int nc = n_chunks(P.V);
   const int G = persist_grid(P.V);
   if ((nc + G - 1) / G > kPMtWg / 4) return false;
   static int capable = -1;  // whether one workgroup per CU fits and the device launches cooperatively
   if (capable < 0) {
-    int dev = 0, coop = 0, ncu = 0, per_cu = 0;
+    int dev = 0, coop = 0, ncu = 0, per_cu16 = 0, per_cu32 = 0;
     capable = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_draft_persist<256>),
-                                                     kPThreads, 0) == hipSuccess)
-      capable = coop && per_cu >= 1 && ncu >= kStreamGridMax ? 1 : 0;
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu16, reinterpret_cast<const void*>(k_draft_persist<256, uint16_t>), kPThreads, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu32, reinterpret_cast<const void*>(k_draft_persist<256, float>), kPThreads, 0) == hipSuccess)
+      capable = coop && per_cu16 >= 1 && per_cu32 >= 1 && ncu >= kStreamGridMax ? 1 : 0;
     (void)hipGetLastError();
   }
   return capable == 1;
@@ -544,8 +573,9 @@ hipError_t launch_draft_persistent(const dspark_problem& P, const PersistArgs& a
   if (e != hipSuccess) return e;
   PersistArgs arg = a;
   void* args[] = {&arg};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_draft_persist<256>),
-                                    dim3(persist_grid(P.V)), dim3(kPThreads), args, 0, s);
+  const void* kernel = P.logits_dtype == DSPARK_F32 ? reinterpret_cast<const void*>(k_draft_persist<256, float>)
+                                                    : reinterpret_cast<const void*>(k_draft_persist<256, uint16_t>);
+  return hipLaunchCooperativeKernel(kernel, dim3(persist_grid(P.V)), dim3(kPThreads), args, 0, s);
 }
 
 }  // namespace dspark

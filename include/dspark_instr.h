@@ -24,11 +24,12 @@ extern "C" {
  *                              position, each re-reading Wt;
  *   DSPARK_DRAFT_PERSISTENT    one cooperative launch for all K positions, each
  *                              CU's slice of Wt held on chip for the cycle
- *                              (bf16 logits and factors, r = 256, B <= 256, a
+ *                              (bf16 or fp32 logits, bf16 factors, r = 256, B <= 256, a
  *                              device that launches cooperatively; not under
  *                              stream capture, not for the RNN head).
  * dspark_draft takes DSPARK_DRAFT_AUTO: the persistent schedule where it applies
- * and B <= 48, else the per-position one (the measured crossover). */
+ * and B <= 48 (bf16 logits) or B <= 96 (fp32 logits), else the per-position one
+ * (the measured crossovers). */
 enum {
   DSPARK_DRAFT_AUTO = 0,
   DSPARK_DRAFT_PER_POSITION = 1,

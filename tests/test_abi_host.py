@@ -136,7 +136,8 @@ def test_draft_rejects_bad_problems(ds, kw, code):
 def test_draft_schedule_arguments(ds):
     # an unknown schedule is rejected before anything else; the schedule query
     # rejects what dspark_draft rejects and reports the per-position schedule
-    # where the persistent one cannot apply (fp32 logits, rank 128, 257 rows)
+    # where the persistent one cannot apply or is slower (256 rows of fp32
+    # logits, rank 128, 257 rows)
     lib = ds.load()
     P = _P(ds)
     for bad in (-1, 3, 7):

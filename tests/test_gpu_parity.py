@@ -132,8 +132,8 @@ def test_full_size(lib, name):
 
 # Both schedules of the draft phase (dspark_instr.h): each where dspark_draft
 # would take the other one (the persistent kernel at the full batch, the
-# per-position kernels at a small bf16 batch), and the persistent kernel at its
-# edges: one request, one position, a vocabulary of one chunk (one workgroup
+# per-position kernels at small bf16 and fp32-logit batches), and the persistent
+# kernel at its edges (fp32 logits with a ragged batch and vocabulary too): one request, one position, a vocabulary of one chunk (one workgroup
 # selecting every row) and of one chunk plus a ragged 8 entries, a ragged batch
 # with more rows than workgroups, and the largest batch it takes by default.
 SCHEDULES = [
@@ -145,6 +145,8 @@ SCHEDULES = [
     ("persist_v128", 2),
     ("persist_v136", 2),
     ("persist_b48", 2),
+    ("qwen3_4b", 1),
+    ("persist_f32_ragged", 2),
 ]
 
 
@@ -162,6 +164,9 @@ def _schedule_cfg(name):
         return base.replace(name=name, B=20, K=3, V=128, d=64, seed=18)
     if name == "persist_v136":
         return base.replace(name=name, B=20, K=3, V=136, d=64, seed=19)
+    if name == "persist_f32_ragged":
+        # fp32 base logits (the in-place refill of the base-logit registers), ragged batch and vocabulary
+        return base.replace(name=name, B=33, K=3, V=1000, r=256, d=64, logits_dtype="f32", seed=21)
     if name == "persist_b48":
         return synth.get_config("high_concurrency").replace(name=name, B=48, K=4, seed=20)
     return synth.get_config(name)
@@ -175,7 +180,7 @@ def test_draft_schedules(lib, name, path):
     P = dspark.Problem.from_config(cfg)
     auto = dspark.draft_path(P)
     _say(f"[gpu] schedule {path} on {name} B={cfg.B} K={cfg.K} V={cfg.V} (dspark_draft takes {auto})")
-    if name in ("high_concurrency", "tbias_bf16"):
+    if name in ("high_concurrency", "tbias_bf16", "qwen3_4b"):
         assert auto != path   # the schedule dspark_draft does not take there
     inp = synth.make_inputs(cfg)
     g = gpu_cycle(lib, cfg, inp, path=path)
