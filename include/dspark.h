@@ -39,6 +39,12 @@
  *   library allocates, frees and synchronises nothing and keeps no state
  *   between calls, so calls can be captured in a HIP graph.  Work is enqueued
  *   on `stream` (NULL = the default stream) and is asynchronous.
+ * - dspark_draft runs one of two schedules of the same computation
+ *   (dspark_instr.h): outside capture, for small batches, one cooperative
+ *   launch over all K positions; under capture, and otherwise, a launch per
+ *   position.  Tokens agree between them except at near-ties; log q and the
+ *   log-partitions agree up to fp32 summation order (a few ulps).  Results are
+ *   bit-reproducible for a given schedule.
  * - Logit, weight and hidden arrays must be 16-byte aligned; int32/float
  *   arrays 4-byte aligned.
  * - Validation runs on the host before anything is enqueued and returns a

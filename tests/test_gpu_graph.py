@@ -4,7 +4,10 @@ several times with eager work and synchronisation between the replays, new
 inputs copied into the captured input buffers between replays; every replay
 must reproduce the eager cycle on the same inputs bit for bit.  The library
 records no memset and no host synchronisation, so nothing in the graph
-depends on host state."""
+depends on host state.  Under capture the draft runs its per-position
+schedule (a cooperative launch is not captured), so the eager references take
+that schedule explicitly; outside capture small batches take the persistent
+one, equal up to fp32 summation order."""
 from __future__ import annotations
 
 import sys
@@ -58,11 +61,12 @@ def test_cycle_graph_replays(lib, name):
         import dataclasses
         c = dataclasses.replace(cfg, seed=cfg.seed + seed_shift)
         sets.append(runner.CycleInputs.upload(synth.make_inputs(c)))
-    # eager references
+    # eager references, on the schedule capture records
+    per_position = dspark.DRAFT_PER_POSITION
     refs = []
     for x in sets:
         o = runner.CycleOutputs(P)
-        runner.run_cycle(P, x, o)
+        runner.run_cycle(P, x, o, path=per_position)
         torch.cuda.synchronize()
         refs.append(_host(o))
     assert not all(np.array_equal(refs[0][k], refs[1][k]) for k in refs[0])
@@ -86,7 +90,7 @@ def test_cycle_graph_replays(lib, name):
         og.tok.fill_(-3)
         og.n_acc.fill_(-3)
         g.replay()
-        runner.run_cycle(P, sets[1 - i], other)   # eager work between replays
+        runner.run_cycle(P, sets[1 - i], other, path=per_position)   # eager work between replays
         torch.cuda.synchronize()
         _same(_host(og), refs[i], f"replay {rep}")
         _same(_host(other), refs[1 - i], f"eager after replay {rep}")
