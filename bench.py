@@ -611,22 +611,31 @@ def main() -> int:
         ms_graph, ms_async, baselines, sts_line, rnn_line = secondary()
 
     # the draft phase (every position: the persistent kernel, or the per-position
-    # stream and selection kernels), timed by two events the library records
-    # around it on its own stream
+    # stream and selection kernels), timed by events the library records on its
+    # own stream around the phase and around each launch of its stream kernel
     hip = Hip()
+    K = cfg.K
 
-    def draft_phase_ms(path, n):
-        out = []
+    def draft_timing(path, n, per_launch):
+        # per_launch: 2 + 2K events (the phase and each stream-kernel launch),
+        # else 2 (the phase alone, without the launch events between its kernels)
+        phase, launches = [], []
         for i in range(n):
             xs = sets[i % 3]
-            evs = hip.events(2)
+            evs = hip.events(2 + 2 * K if per_launch else 2)
             dspark.draft_timed(P, xs.Z, xs.E, xs.Wt, xs.h, xs.w_c, xs.b_c, xs.tau, xs.anchor,
                                o.tok, o.logq, o.lse, o.conf, o.surv, o.workspace, evs, path=path)
             torch.cuda.synchronize()
-            out.append(hip.elapsed_ms(evs[0], evs[1]))
+            phase.append(hip.elapsed_ms(evs[0], evs[1]))
+            if per_launch:
+                launches.append([hip.elapsed_ms(evs[2 + 2 * j], evs[3 + 2 * j]) for j in range(K)])
             hip.destroy(evs)
-        return float(np.median(out))
+        return float(np.median(phase)), np.array(launches)
 
+    def draft_phase_ms(path, n):
+        return draft_timing(path, n, False)[0]
+
+    launch_ms_all = draft_timing(dspark.DRAFT_AUTO, args.steps, True)[1]
     k_ms = draft_phase_ms(dspark.DRAFT_AUTO, args.steps)
     lib_path = dspark.draft_path(P)
     assert (lib_path == dspark.DRAFT_PERSISTENT) == draft_persistent(cfg), "bench's rule differs from the library's"
@@ -656,9 +665,16 @@ def main() -> int:
     persistent = lib_path == dspark.DRAFT_PERSISTENT
     phase_bytes = cfg.K * stream_launch_bytes(cfg)            # Z once, Wt once, the E rows
     phase_bytes_full = cfg.K * stream_launch_bytes_full_wt(cfg, G)
-    achieved = phase_bytes / (k_ms / 1e3) / 1e9
+    # the dominant kernel's average launch (events around each launch): the
+    # persistent kernel's one launch per cycle, or k_draft at positions 2..K
+    # (position 1 runs k_draft_first)
+    if persistent or K == 1:
+        launch_ms = float(np.mean(launch_ms_all[:, 0]))
+    else:
+        launch_ms = float(np.mean(launch_ms_all[:, 1:]))
     # bytes of one launch of the dominant kernel (the whole phase, or one position)
     launch_bytes = phase_bytes if persistent else stream_launch_bytes(cfg)
+    achieved = launch_bytes / (launch_ms / 1e3) / 1e9
     traffic = traffic_from_profile(cfg.name)
     step_traffic = step_traffic_from_profile(cfg)
     mfma = mfma_from_profile(cfg.name)
@@ -700,25 +716,31 @@ def main() -> int:
             "kernel": f"{dominant(cfg)} (bias contraction E[x]·Wt^T on v_mfma_f32_32x32x16_bf16)",
             "gflop_per_launch_counted": mfma["gflop"],
             "gflop_per_launch_algorithmic": 2.0 * cfg.B * cfg.r * cfg.V * (cfg.K if persistent else 1) / 1e9,
-            "tflops": mfma["gflop"] * (1 if persistent else cfg.K) / k_ms,
-            "frac_of_bf16_peak": mfma["gflop"] * (1 if persistent else cfg.K) / k_ms / 2500.0,
+            "tflops": mfma["gflop"] / launch_ms,
+            "frac_of_bf16_peak": mfma["gflop"] / launch_ms / 2500.0,
             "mfma_busy_pct": mfma["busy_pct"],
             "source": f"profiles/cycle_{cfg.name}_hbm_counters.md"},
         "roofline": {
             "kernel": (f"{DOMINANT}: the draft phase, all {cfg.K} positions in one launch" if persistent else
-                       f"the draft phase: {cfg.K} launches of {DOMINANT_STEPWISE} and of the selection"),
+                       f"{DOMINANT_STEPWISE}: one draft position (vocabulary stream and bias contraction), "
+                       f"average over positions 2..{cfg.K}"),
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None if traffic is None else traffic * (1 if persistent else cfg.K),
+            "traffic": traffic,
             "traffic_over_algorithmic": None if traffic is None else traffic / launch_bytes,
+            "launch_ms": launch_ms,
+            "launch_bytes": launch_bytes,
+            "launch_bytes_note": ("K x (Z slab + E rows of the previous tokens) + Wt once per cycle" if persistent else
+                                  "Z slab + Wt / K (Wt once per cycle) + E rows of the previous tokens"),
+            "launch_bytes_full_wt": None if persistent else stream_launch_bytes_full_wt(cfg, G),
+            "frac_full_wt": None if persistent else
+            stream_launch_bytes_full_wt(cfg, G) / (launch_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
             "phase_ms": k_ms,
             "phase_bytes": phase_bytes,
-            "phase_bytes_note": "K x (Z slab + E rows of the previous tokens) + Wt once per cycle",
-            "phase_bytes_full_wt": phase_bytes_full,
-            "frac_full_wt": phase_bytes_full / (k_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "phase_frac": phase_bytes / (k_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         },
         "draft_phase_ms_by_schedule": schedules,
     }

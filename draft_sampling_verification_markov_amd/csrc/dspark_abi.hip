@@ -160,7 +160,10 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
                                 const int32_t* anchor, int32_t* draft_tok, float* draft_logq, float* draft_lse,
                                 float* conf, float* surv, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream, hipEvent_t* events, const RnnDraft* rnn = nullptr,
-                                int32_t path = DSPARK_DRAFT_AUTO) {
+                                int32_t path = DSPARK_DRAFT_AUTO, int32_t n_events = 0) {
+  // timing events: events[0] / events[1] around the draft phase; with 2 + 2K,
+  // events[2 + 2i] / events[3 + 2i] around the i-th launch of its stream kernel
+  const bool per_launch = events && n_events >= 2 + 2 * (P ? P->K : 0);
   dspark_status st = check_problem(P);
   if (st != DSPARK_OK) return st;
   const dspark_problem& p = *P;
@@ -256,7 +259,12 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
     pa.inv_T = se.inv_T;
     pa.key = sa.key;
     if (events && hipEventRecord(events[0], stream) != hipSuccess) return DSPARK_E_LAUNCH;
+    if (per_launch && hipEventRecord(events[2], stream) != hipSuccess) return DSPARK_E_LAUNCH;
     if (launch_draft_persistent(p, pa, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+    // one launch: the other per-launch events all right after it
+    if (per_launch)
+      for (int i = 3; i < 2 + 2 * p.K; ++i)
+        if (hipEventRecord(events[i], stream) != hipSuccess) return DSPARK_E_LAUNCH;
     // a barrier time-out (the flag word the kernel sets) raises its debug bit
     if (kDebugChecks && debug_scan_range_i32(reinterpret_cast<const int32_t*>(pa.sync) + 16, 1, 0, 0,
                                              DSPARK_DEBUG_BARRIER_TIMEOUT, stream) != hipSuccess)
@@ -280,7 +288,9 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
                                stream) != hipSuccess)
       return DSPARK_E_LAUNCH;
     if (events && k == 1 && hipEventRecord(events[0], stream) != hipSuccess) return DSPARK_E_LAUNCH;
+    if (per_launch && hipEventRecord(events[2 * k], stream) != hipSuccess) return DSPARK_E_LAUNCH;
     if (launch_stream_draft(p, sa, L.G, stream) != hipSuccess) return DSPARK_E_LAUNCH;
+    if (per_launch && hipEventRecord(events[2 * k + 1], stream) != hipSuccess) return DSPARK_E_LAUNCH;
     if (launch_select(p, se, stream) != hipSuccess) return DSPARK_E_LAUNCH;
     if (events && k == p.K && hipEventRecord(events[1], stream) != hipSuccess) return DSPARK_E_LAUNCH;
   }
@@ -321,12 +331,13 @@ extern "C" dspark_status dspark_draft_timed(const dspark_problem* P, const void*
                                             const int32_t* anchor, int32_t* draft_tok, float* draft_logq,
                                             float* draft_lse, float* conf, float* surv, void* workspace,
                                             size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
-                                            int32_t path) {
+                                            int32_t n_events, int32_t path) {
   const AbiRange range("dspark_draft_timed");
   if (path != DSPARK_DRAFT_AUTO && path != DSPARK_DRAFT_PER_POSITION && path != DSPARK_DRAFT_PERSISTENT)
     return DSPARK_E_INVALID;
+  if (!events ? n_events != 0 : (n_events != 2 && (!P || n_events != 2 + 2 * P->K))) return DSPARK_E_INVALID;
   return draft_impl(P, Z, E, Wt, h, w_conf, b_conf, tau, anchor, draft_tok, draft_logq, draft_lse, conf, surv,
-                    workspace, workspace_bytes, stream, events, nullptr, path);
+                    workspace, workspace_bytes, stream, events, nullptr, path, n_events);
 }
 
 extern "C" int32_t dspark_draft_path(const dspark_problem* P) {

@@ -87,7 +87,7 @@ def load(debug: bool | None = None) -> ctypes.CDLL:
     lib.dspark_status_string.restype = ctypes.c_char_p
     lib.dspark_draft.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dspark_draft.restype = i32
-    lib.dspark_draft_timed.argtypes = lib.dspark_draft.argtypes + [vp, i32]
+    lib.dspark_draft_timed.argtypes = lib.dspark_draft.argtypes + [vp, i32, i32]
     lib.dspark_draft_timed.restype = i32
     lib.dspark_draft_path.argtypes = [ctypes.POINTER(Problem)]
     lib.dspark_draft_path.restype = i32
@@ -176,8 +176,9 @@ def draft(P: Problem, Z, E, Wt, h, w_conf, b_conf: float, tau, anchor,
 def draft_timed(P: Problem, Z, E, Wt, h, w_conf, b_conf: float, tau, anchor,
                 draft_tok, draft_logq, draft_lse, conf, surv, workspace, events=None, stream=None,
                 path: int = DRAFT_AUTO) -> None:
-    """dspark_draft_timed: dspark_draft with schedule `path` (DRAFT_*), recording events[0] and
-    events[1] (raw hipEvent_t handles, a ctypes array of 2 c_void_p, or None) around the draft phase."""
+    """dspark_draft_timed: dspark_draft with schedule `path` (DRAFT_*), recording `events` (raw
+    hipEvent_t handles, a ctypes array of 2 or 2 + 2K c_void_p, or None) around the draft phase and,
+    with 2 + 2K, around each launch of its stream kernel."""
     lt, wt, ht = _TORCH_DT[P.logits_dtype], _TORCH_DT[P.weight_dtype], _TORCH_DT[P.hidden_dtype]
     st = load().dspark_draft_timed(
         ctypes.byref(P), _ptr(Z, lt, "Z"), _ptr(E, wt, "E"), _ptr(Wt, wt, "Wt"), _ptr(h, ht, "h"),
@@ -186,7 +187,8 @@ def draft_timed(P: Problem, Z, E, Wt, h, w_conf, b_conf: float, tau, anchor,
         _ptr(draft_logq, torch.float32, "draft_logq"), _ptr(draft_lse, torch.float32, "draft_lse"),
         _ptr(conf, torch.float32, "conf"), _ptr(surv, torch.float32, "surv"),
         _ptr(workspace, None, "workspace"), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
-        _stream(stream), None if events is None else ctypes.cast(events, ctypes.c_void_p), ctypes.c_int32(path))
+        _stream(stream), None if events is None else ctypes.cast(events, ctypes.c_void_p),
+        ctypes.c_int32(0 if events is None else len(events)), ctypes.c_int32(path))
     _check("dspark_draft_timed", st)
 
 

@@ -38,13 +38,19 @@ enum {
 
 /*
  * dspark_draft_timed -- dspark_draft with a chosen schedule and optional
- * timing.  `path` is one of the DSPARK_DRAFT_* values above.  If `events` is
- * not NULL, events[0] and events[1] (caller-created HIP events) are recorded on
- * `stream` immediately before the first and after the last kernel of the
- * K-position draft phase, before the confidence head, so that the caller can
- * read the phase's duration with hipEventElapsedTime.  Same inputs, outputs
- * and errors as dspark_draft, plus DSPARK_E_INVALID for an unknown `path` and
- * DSPARK_E_UNSUPPORTED for DSPARK_DRAFT_PERSISTENT where it does not apply.
+ * timing.  `path` is one of the DSPARK_DRAFT_* values above.  `events` holds
+ * n_events caller-created HIP events, recorded on `stream`:
+ *   n_events = 0 (events NULL): no timing;
+ *   n_events = 2: events[0] / events[1] immediately before the first and after
+ *     the last kernel of the K-position draft phase, before the confidence head;
+ *   n_events = 2 + 2K: as for 2, and events[2 + 2i] / events[3 + 2i] around the
+ *     i-th launch of the phase's stream kernel: on the per-position schedule
+ *     position i + 1's (i = 0..K-1); on the persistent schedule its one launch
+ *     (i = 0), the later ones recorded right after it.
+ * The caller reads the intervals with hipEventElapsedTime.  Same inputs,
+ * outputs and errors as dspark_draft, plus DSPARK_E_INVALID for an unknown
+ * `path` or event count and DSPARK_E_UNSUPPORTED for DSPARK_DRAFT_PERSISTENT
+ * where it does not apply.
  */
 dspark_status dspark_draft_timed(const dspark_problem* P,
                                  const void* Z, const void* E, const void* Wt, const void* h,
@@ -53,7 +59,7 @@ dspark_status dspark_draft_timed(const dspark_problem* P,
                                  int32_t* draft_tok, float* draft_logq, float* draft_lse,
                                  float* conf, float* surv,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                 hipEvent_t* events, int32_t path);
+                                 hipEvent_t* events, int32_t n_events, int32_t path);
 
 /*
  * dspark_draft_path -- the schedule dspark_draft takes for problem P outside

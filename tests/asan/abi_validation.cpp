@@ -105,7 +105,7 @@ int main() {
   expect("draft_timed(bad path)",
          dspark_draft_timed(&ok, f[0], f[1], f[2], f[3], (const float*)f[4], 0.f, (const float*)f[5],
                             (const int32_t*)f[6], (int32_t*)f[7], (float*)f[8], (float*)f[9], (float*)f[10],
-                            (float*)f[11], ws, need, nullptr, nullptr, 9),
+                            (float*)f[11], ws, need, nullptr, nullptr, 0, 9),
          DSPARK_E_INVALID);
   expect("schedule(null T)", dspark_schedule(&ok, (const float*)f[0], nullptr, (int32_t*)f[2], (int32_t*)f[3], ws,
                                              need, nullptr),

@@ -142,8 +142,14 @@ def test_draft_schedule_arguments(ds):
     P = _P(ds)
     for bad in (-1, 3, 7):
         st = lib.dspark_draft_timed(ctypes.byref(P), *([None] * 5), ctypes.c_float(0), *([None] * 8), 0, None,
-                                    None, bad)
+                                    None, 0, bad)
         assert st == ds.E_INVALID, ds.status_string(st)
+    # event counts: 0 without events, else 2 or 2 + 2K
+    ev = (ctypes.c_void_p * 40)()
+    for n, events in ((2, None), (0, ev), (3, ev), (2 + 2 * 16 + 2, ev)):
+        st = lib.dspark_draft_timed(ctypes.byref(P), *([None] * 5), ctypes.c_float(0), *([None] * 8), 0, None,
+                                    events, n, 0)
+        assert st == ds.E_INVALID, (n, ds.status_string(st))
     assert lib.dspark_draft_path(ctypes.byref(_P(ds, B=0))) == ds.E_INVALID
     assert lib.dspark_draft_path(ctypes.byref(_P(ds, r=48))) == ds.E_UNSUPPORTED
     for kw in (dict(logits="f32"), dict(r=128), dict(B=257)):
