@@ -46,7 +46,7 @@ Layout make_layout(const dspark_problem& P) {
   L.lagn = off;   off = align_up(off + (B + 1) * sizeof(int32_t));
   L.efrag = off;  off = align_up(off + (size_t)((B + 31) / 32) * 32 * (size_t)P.r * 2);
   L.ptok = off;   off = align_up(off + B * sizeof(int32_t));
-  L.psync = off;  off = align_up(off + 64 * sizeof(uint32_t));
+  L.psync = off;  off = align_up(off + kPersistSyncWords * sizeof(uint32_t));
   L.total = off;
   return L;
 }
@@ -266,7 +266,7 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
       for (int i = 3; i < 2 + 2 * p.K; ++i)
         if (hipEventRecord(events[i], stream) != hipSuccess) return DSPARK_E_LAUNCH;
     // a barrier time-out (the flag word the kernel sets) raises its debug bit
-    if (kDebugChecks && debug_scan_range_i32(reinterpret_cast<const int32_t*>(pa.sync) + 16, 1, 0, 0,
+    if (kDebugChecks && debug_scan_range_i32(reinterpret_cast<const int32_t*>(pa.sync) + (size_t)kSyncFlag * kSyncStride, 1, 0, 0,
                                              DSPARK_DEBUG_BARRIER_TIMEOUT, stream) != hipSuccess)
       return DSPARK_E_LAUNCH;
     if (events && hipEventRecord(events[1], stream) != hipSuccess) return DSPARK_E_LAUNCH;

@@ -56,7 +56,7 @@ struct Layout {
   size_t lagn;  // int32 [B + 1]: the lagged schedule of the asynchronous scheduler (n_b, then N)
   size_t efrag; // uint4 [ceil(B/32)][r/16][64]: E rows of the previous draft tokens, B-fragment order
   size_t ptok;  // int32 [B]: the persistent draft's tokens of the latest position (read by every workgroup)
-  size_t psync; // uint32 [64]: the persistent draft's grid-barrier counter [0] and time-out flag [16]
+  size_t psync; // uint32 [kPersistSyncWords]: the persistent draft's grid-barrier words and time-out flag
   size_t total;
 };
 
@@ -96,7 +96,7 @@ struct PersistArgs {
   float* lse;
   float4* part;          // [B][G] per-(row, workgroup) partials of the latest position
   int32_t* ptok;         // [B] tokens of the latest position
-  unsigned* sync;        // [0] barrier counter (zero at launch), [16] time-out flag
+  unsigned* sync;        // [kPersistSyncWords] barrier words (zero at launch) and the time-out flag
   uint32_t z_bytes;      // bytes of Z (below 2^32)
   uint32_t spin_limit;   // polls of a barrier wait before it gives up (kPersistSpinLimit)
   uint32_t arrive_extra; // arrivals a barrier waits for beyond the grid's (0; 1 makes every wait time out)
@@ -225,11 +225,23 @@ hipError_t debug_check_verify(const int32_t* n_sched, const int32_t* out_tok, co
 // workgroups of the persistent draft launch: one per vocabulary chunk up to kStreamGridMax
 int persist_grid(int V);
 // dspark_draft takes the persistent draft where it applies and the batch is at
-// most this (the measured crossovers: above them the per-position kernels, with
-// two waves per SIMD, are faster; with fp32 logits they stream twice the bytes)
-inline int persist_max_b(const dspark_problem& P) { return P.logits_dtype == DSPARK_F32 ? 96 : 48; }
+// most this (the measured crossovers: with bf16 logits the per-position kernels,
+// with two waves per SIMD, are faster above it; with fp32 logits they stream
+// twice the bytes and the persistent draft is faster up to its limit of 256)
+inline int persist_max_b(const dspark_problem& P) { return P.logits_dtype == DSPARK_F32 ? 256 : 96; }
 // polls of a persistent-draft barrier wait before it sets the time-out flag
 constexpr uint32_t kPersistSpinLimit = 1u << 20;
+// The persistent draft's grid barrier: kSyncGroups arrival counters, as many
+// release words, one top-level counter and the time-out flag, each word
+// kSyncStride words (4 KiB) from the next so that no two share a cache line or
+// a memory channel's interleave unit.
+constexpr int kSyncGroups = 16;
+constexpr int kSyncStride = 1024;
+constexpr int kSyncRelease = kSyncGroups;      // release word j at (kSyncRelease + j) * kSyncStride
+constexpr int kSyncTop = 2 * kSyncGroups;      // top-level counter
+constexpr int kSyncFlag = 2 * kSyncGroups + 1; // time-out flag
+constexpr int kPersistSyncSlots = 2 * kSyncGroups + 2;
+constexpr size_t kPersistSyncWords = (size_t)kPersistSyncSlots * kSyncStride;
 bool draft_persistent_supported(const dspark_problem& P);
 hipError_t launch_draft_persistent(const dspark_problem& P, const PersistArgs& a, hipStream_t s);
 hipError_t launch_conf(const dspark_problem& P, const ConfArgs& a, hipStream_t s);

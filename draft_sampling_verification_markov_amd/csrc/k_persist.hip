@@ -34,7 +34,7 @@
 //  6. grid barrier, while the next position's first base logits are requested.
 // Records read after a barrier are read past the L2 as well (an XCD's L2 is
 // not kept coherent with another's).  Every barrier wait is bounded: past the
-// limit the flag sync[16] is set and the waits that follow return at once, so
+// limit the time-out flag is set and the waits that follow return at once, so
 // the kernel always ends (its results are then unspecified).
 #include "dspark_internal.hpp"
 
@@ -87,24 +87,42 @@ __device__ __forceinline__ float4 ld_agent4(const float4* p) {
                      __uint_as_float((unsigned)(hi >> 32)));
 }
 
-// Grid barrier on a monotonic arrival counter, in two halves so that loads
-// independent of the other workgroups can be issued between them: arrive
-// (this workgroup's stores past the L2 complete, then one atomic add) and wait
-// (until `expect` arrivals per epoch: the G workgroups).  Bounded: past
-// `limit` polls the flag is set and this and every later wait return at once.
-__device__ __forceinline__ void grid_arrive(unsigned* sync, unsigned& epoch) {
+// Grid barrier in two levels on monotonic counters, in two halves so that
+// loads independent of the other workgroups can be issued between them.
+// Arrive: this workgroup's stores past the L2 complete, then one atomic add on
+// its group's counter (workgroup g is in group g % ng, ng = min(kSyncGroups,
+// G)); the group's last arrival adds one to the top-level counter, and the last
+// of those stores the epoch into every group's release word.  Wait: until the
+// own group's release word holds the epoch.  Each counter then takes at most
+// G / ng + 1 atomics and each release word G / ng + 1 pollers per epoch, instead
+// of all G on one word.  `extra` > 0 makes the top level unreachable (every
+// wait then times out).  Bounded: past `limit` polls the flag is set and this
+// and every later wait return at once.
+__device__ __forceinline__ void grid_arrive(unsigned* sync, unsigned& epoch, int g, int G, unsigned extra) {
   wait_vmem();
   __syncthreads();
   epoch += 1;
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void grid_wait(unsigned* sync, unsigned expect, unsigned epoch, unsigned limit) {
   if (threadIdx.x == 0) {
-    const unsigned target = epoch * expect;
-    unsigned spins = ld_agent(sync + 16) ? limit : 0u;
-    while (ld_agent(sync) < target) {
+    const int ng = G < kSyncGroups ? G : kSyncGroups;
+    const int j = g % ng;
+    const unsigned members = (unsigned)(G / ng + (j < G % ng ? 1 : 0));
+    const unsigned before = __hip_atomic_fetch_add(sync + j * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before + 1u == epoch * members) {
+      const unsigned top =
+          __hip_atomic_fetch_add(sync + kSyncTop * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (top + 1u == epoch * ((unsigned)ng + extra))
+        for (int i = 0; i < ng; ++i) st_agent(sync + (kSyncRelease + i) * kSyncStride, epoch);
+    }
+  }
+}
+__device__ __forceinline__ void grid_wait(unsigned* sync, unsigned epoch, int g, int G, unsigned limit) {
+  if (threadIdx.x == 0) {
+    const int ng = G < kSyncGroups ? G : kSyncGroups;
+    const unsigned* rel = sync + (kSyncRelease + g % ng) * kSyncStride;
+    unsigned spins = ld_agent(sync + kSyncFlag * kSyncStride) ? limit : 0u;
+    while (ld_agent(rel) < epoch) {
       if (++spins > limit) {
-        st_agent(sync + 16, 1u);
+        st_agent(sync + kSyncFlag * kSyncStride, 1u);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -419,8 +437,8 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
     }
 
     // 4. every workgroup's partials of position k are out
-    grid_arrive(a.sync, epoch);
-    grid_wait(a.sync, (unsigned)G + a.arrive_extra, epoch, a.spin_limit);
+    grid_arrive(a.sync, epoch, g, G, a.arrive_extra);
+    grid_wait(a.sync, epoch, g, G, a.spin_limit);
 
     // 5. selection of rows g, g + G, ...
     for (int b = g; b < B; b += G) {
@@ -452,7 +470,9 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
           B0 = s_best[w];
           C0 = s_bi[w];
         }
-      const int cstar = (C0 >= 0 && C0 * kChunk < V) ? C0 : 0;
+      // a row without any finite chunk score keeps the sentinel id: chunk 0
+      // (compared with the chunk count: C0 * kChunk could wrap)
+      const int cstar = (C0 >= 0 && C0 < a.nchunks) ? C0 : 0;
       const int v0 = cstar * kChunk;
       const int nrow = V - v0 < kChunk ? V - v0 : kChunk;
       // the chunk's Wt block (consecutive threads on consecutive 16-byte
@@ -524,14 +544,15 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
 
     // 6. every token of position k is out; while the other workgroups arrive,
     // the next position's first base logits (they do not depend on the tokens)
-    grid_arrive(a.sync, epoch);
+    grid_arrive(a.sync, epoch, g, G, a.arrive_extra);
     if (k < K) zload(k + 1, 0, zA);
-    grid_wait(a.sync, (unsigned)G + a.arrive_extra, epoch, a.spin_limit);
+    grid_wait(a.sync, epoch, g, G, a.spin_limit);
   }
 }
 
+// zero the barrier's counters, release words and time-out flag
 __global__ __launch_bounds__(64) void k_persist_init(unsigned* sync) {
-  sync[threadIdx.x] = 0u;
+  if (threadIdx.x < kPersistSyncSlots) sync[threadIdx.x * kSyncStride] = 0u;
 }
 
 }  // namespace

@@ -1441,7 +1441,8 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
       }
     }
     // a row without any finite chunk score (non-finite logits) falls back to chunk 0
-    cstar = (C0 >= 0 && C0 * kChunk < V) ? C0 : 0;
+    // (compared with the chunk count: C0 * kChunk could wrap)
+    cstar = (C0 >= 0 && C0 < (V + kChunk - 1) / kChunk) ? C0 : 0;
   }
 
   // 2. recompute the winning chunk's logits and draw the entry
@@ -1579,7 +1580,8 @@ __global__ __launch_bounds__(256) void k_select_b16(SelectArgs a) {
       }
     }
     // a row without any finite chunk score (non-finite logits) falls back to chunk 0
-    cstar = (C0 >= 0 && C0 * kChunk < V) ? C0 : 0;
+    // (compared with the chunk count: C0 * kChunk could wrap)
+    cstar = (C0 >= 0 && C0 < (V + kChunk - 1) / kChunk) ? C0 : 0;
   }
 
   // 2. the chunk's Wt block, coalesced, and this thread's operand piece; for

@@ -313,11 +313,14 @@ __device__ int full_row_draw(const ZT* row, int V, float inv_T, Key key, int b, 
       B0 = s_best[w];
       C0 = s_idx[w];
     }
+  // a row without any finite chunk score (non-finite logits) keeps the sentinel
+  // id: chunk 0 (compared with the chunk count: C0 * kChunk could wrap)
+  const int cs = (C0 >= 0 && C0 < nc) ? C0 : 0;
   __syncthreads();
   float sc = -INFINITY;
   int idx = 0x7fffffff;
   if (tid < kChunk) {
-    const int v = C0 * kChunk + tid;
+    const int v = cs * kChunk + tid;
     if (v < V) {
       sc = logit_at<ZT>(row, v) * inv_T + gumbel_from_word(draw_word(key, (uint32_t)v, (uint32_t)b, (uint32_t)k, pe));
       idx = v;
@@ -337,7 +340,7 @@ __device__ int full_row_draw(const ZT* row, int V, float inv_T, Key key, int b, 
       X = s_idx[w];
     }
   __syncthreads();
-  return X;
+  return (X >= 0 && X < V) ? X : cs * kChunk;  // no finite score: the chunk's first entry
 }
 
 template <typename ZT, typename WT>
@@ -394,7 +397,7 @@ __global__ __launch_bounds__(256) void k_finish(VerifyArgs a) {
     for (int j = 0; j < 4; ++j) t[j] = (s_d[0][j] + s_d[1][j]) + (s_d[2][j] + s_d[3][j]);
     s_R = t[0];
     s_mass = resid_mass_normalised(t[0], t[1], t[2], t[3]);
-    s_cstar = (Bm == -INFINITY) ? -1 : C0;
+    s_cstar = (Bm == -INFINITY || C0 < 0 || C0 >= (V + kChunk - 1) / kChunk) ? -1 : C0;
   }
   __syncthreads();
   const int cstar = s_cstar;
@@ -559,7 +562,7 @@ __global__ __launch_bounds__(256) void k_finish_b16(VerifyArgs a) {
   double tot[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) tot[j] = (s_d[0][j] + s_d[1][j]) + (s_d[2][j] + s_d[3][j]);
-  const int cstar = (Bm == -INFINITY || C0 < 0 || C0 * kChunk >= V) ? -1 : C0;
+  const int cstar = (Bm == -INFINITY || C0 < 0 || C0 >= (V + kChunk - 1) / kChunk) ? -1 : C0;
   __syncthreads();  // s_best / s_idx are reused below (and by full_row_draw)
   const uint16_t* Zt = static_cast<const uint16_t*>(a.Zt);
   const int r = tid & (kChunk - 1);
