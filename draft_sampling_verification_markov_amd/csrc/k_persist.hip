@@ -266,35 +266,61 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
   };
   // per-row merge of the M-tile partials of N-tiles 4*half .. 4*half+3:
   // chunk log-masses, chunk Gumbels, best chunk, running log-partition, as one
-  // record per (row, workgroup) stored past the L2
+  // record per (row, workgroup) stored past the L2.  Two threads per row: the
+  // workgroup's at most five consecutive chunks span at most two Philox quads,
+  // and thread p takes the chunks of quad (c_begin / 4) + p (one draw each);
+  // the pair then combines over a lane swap.  Sums are taken against the
+  // maximum, so every exponent is at most 0 (the hardware exp2).
   auto merge = [&](int k, int half) {
     barrier_lds_only();
-    if (tid < kPHalf && half * kPHalf + tid < B) {
-      const int prow = half * kPHalf + tid;
-      float run_m = -INFINITY, run_s = 0.f, best = -INFINITY;
-      int best_c = 0x7fffffff, quad = -1;
-      Words4 w4 = {};
-      for (int cc = 0; cc < c_end - c_begin; ++cc) {
-        float cm = -INFINITY, cs = 0.f;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const float2 pt = s_tp[tid * kPMtWg + 4 * cc + tt];
-          lse2_merge(cm, cs, pt.x, pt.y);
-        }
-        const int c = c_begin + cc;
-        if ((c >> 2) != quad) {
-          quad = c >> 2;
-          w4 = draw_quad(a.key, (uint32_t)(quad * 4), (uint32_t)prow, (uint32_t)k, kDraftChunk);
-        }
-        const float gc = gumbel_from_word(quad_pick(w4, c & 3));
-        const float score = cs > 0.f ? (cm + log2f(cs)) * kLn2 + gc : -INFINITY;
-        lse2_merge(run_m, run_s, cm, cs);
-        if (score > best) {
-          best = score;
-          best_c = c;
+    const int r = tid >> 1, p = tid & 1;
+    const int prow = half * kPHalf + r;
+    const int qd = (c_begin >> 2) + p;
+    const int cb = c_begin > 4 * qd ? c_begin : 4 * qd;
+    const int ce = c_end < 4 * qd + 4 ? c_end : 4 * qd + 4;
+    float rm = -INFINITY, rs = 0.f, best = -INFINITY;
+    int best_c = 0x7fffffff;
+    if (prow < B && cb < ce) {
+      // (the counter words pass through an empty asm statement: the draw's
+      // arithmetic that does not depend on the position would otherwise be
+      // hoisted out of the position loop, where its registers spill)
+      int prow_v = prow, quad_v = qd * 4;
+      __asm__ volatile("" : "+v"(prow_v), "+v"(quad_v));
+      const Words4 w4 = draw_quad(a.key, (uint32_t)quad_v, (uint32_t)prow_v, (uint32_t)k, kDraftChunk);
+      for (int c = cb; c < ce; ++c) {
+        {
+          const float2* pt = &s_tp[r * kPMtWg + 4 * (c - c_begin)];
+          const float2 p0 = pt[0], p1 = pt[1], p2 = pt[2], p3 = pt[3];
+          const float m = fmaxf(fmaxf(p0.x, p1.x), fmaxf(p2.x, p3.x));
+          const float o = m == -INFINITY ? 0.f : m;
+          const float sm = p0.y * __builtin_amdgcn_exp2f(p0.x - o) + p1.y * __builtin_amdgcn_exp2f(p1.x - o) +
+                           p2.y * __builtin_amdgcn_exp2f(p2.x - o) + p3.y * __builtin_amdgcn_exp2f(p3.x - o);
+          const float gc = gumbel_from_word(quad_pick(w4, c & 3));
+          const float score = sm > 0.f ? (m + __builtin_amdgcn_logf(sm)) * kLn2 + gc : -INFINITY;
+          if (score > best) {
+            best = score;
+            best_c = c;
+          }
+          // running log-partition (base 2), online
+          const float mm = fmaxf(rm, m);
+          const float mo = mm == -INFINITY ? 0.f : mm;
+          rs = rs * __builtin_amdgcn_exp2f(rm - mo) + sm * __builtin_amdgcn_exp2f(m - mo);
+          rm = mm;
         }
       }
-      st_agent4(a.part + (size_t)prow * G + g, make_float4(run_m, run_s, best, __int_as_float(best_c)));
+    }
+    // the partner's (quad q0 + 1 - p) results
+    const float om = dpp_f<kDppXor1>(rm), os = dpp_f<kDppXor1>(rs), ob = dpp_f<kDppXor1>(best);
+    const int oc = dpp_i<kDppXor1>(best_c);
+    if (p == 0 && prow < B) {
+      const float mm = fmaxf(rm, om);
+      const float mo = mm == -INFINITY ? 0.f : mm;
+      const float ss = rs * __builtin_amdgcn_exp2f(rm - mo) + os * __builtin_amdgcn_exp2f(om - mo);
+      if (better(ob, oc, best, best_c)) {
+        best = ob;
+        best_c = oc;
+      }
+      st_agent4(a.part + (size_t)prow * G + g, make_float4(mm, ss, best, __int_as_float(best_c)));
     }
     barrier_lds_only();
   };
@@ -320,13 +346,14 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
   };
   // N-tile nt of position k: its E rows are in cur and its base logits in
   // zc; the next N-tile's rows (into nxt) are requested first, and its base
-  // logits (bf16: into zn, at once; fp32: into zc, each M-tile's as soon as its
-  // epilogue has read them, always issued) well ahead of their use
+  // logits one M-tile per stage (bf16: into zn; fp32: into zc, each M-tile's as
+  // soon as its epilogue has read them, always issued) well ahead of their use.
+  // Requesting all of them at once would stall the wave at issue while the
+  // earlier requests drain at the workgroup's share of the memory bandwidth.
   auto tile = [&](int k, int nt, uint4 (&zc)[kPMt][ZP], uint4 (&zn)[kPMt][ZP], const unsigned char* cur,
                   unsigned char* nxt) {
     const bool more = nt + 1 < NT;
     if (more) gather(nt + 1, nxt);
-    if (!kF32 && more) zload(k, nt + 1, zn);
     const unsigned char* brow = cur + (l32 * RS + h) * 16;
     auto bfrag = [&](int t) { return *reinterpret_cast<const bf16x8_t*>(brow + 32 * t); };
     // Every M-tile is computed (a missing one has zero fragments and its
@@ -377,6 +404,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
             }
           }
         }
+        if (!kF32 && t == 2 && more) zload_one(k, nt + 1, j, zn[j]);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (pj >= 0) {
