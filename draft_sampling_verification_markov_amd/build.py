@@ -31,6 +31,13 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+# Per-source additions.  The persistent draft keeps each wave's Wt fragments in
+# the accumulation registers (AGPRs) for the whole cycle; with the MFMA results
+# in ordinary registers its epilogue reads them directly (no accumulator copies)
+# and nothing spills.
+SOURCE_FLAGS = {
+    "k_persist.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def sources():
@@ -52,7 +59,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sources()
     objs = [os.path.join(OBJDIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
-    cmds = [[HIPCC, *CFLAGS, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
+    cmds = [[HIPCC, *CFLAGS, *SOURCE_FLAGS.get(os.path.basename(s), []), "-c", s, "-o", o] for s, o in zip(srcs, objs)]
     abi = os.path.join(CSRC, ABI_SOURCE)
     debug_obj = os.path.join(OBJDIR, "dspark_abi_debug.o")
     cmds.append([HIPCC, *CFLAGS, "-DDSPARK_DEBUG_CHECKS", "-c", abi, "-o", debug_obj])

@@ -160,6 +160,22 @@ __device__ __forceinline__ double resid_mass_normalised(double R, double QA, dou
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+// acc + (lo(a) lo(b) + hi(a) hi(b)) for two packed bf16 pairs: one v_dot2c_f32_bf16
+// (measured on this part: correctly rounded more often than two chained fmas)
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  bf16x2_t x, y;
+  __builtin_memcpy(&x, &a, 4);
+  __builtin_memcpy(&y, &b, 4);
+  return __builtin_amdgcn_fdot2_f32_bf16(x, y, acc, false);
+}
+// the dot product of two 16-byte pieces of bf16 rows (8 products, in order of the pairs)
+__device__ __forceinline__ float dot_bf16x8(uint4 e, uint4 w) {
+  float acc = dot2_bf16(e.x, w.x, 0.f);
+  acc = dot2_bf16(e.y, w.y, acc);
+  acc = dot2_bf16(e.z, w.z, acc);
+  return dot2_bf16(e.w, w.w, acc);
+}
 // Workgroup barrier ordering LDS only: this wave's LDS operations complete
 // first; vector-memory operations (LDS DMA included) are the caller's to wait
 // for.  __syncthreads() carries a release fence that drains every load of the

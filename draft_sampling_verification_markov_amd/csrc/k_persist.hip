@@ -131,20 +131,6 @@ __device__ __forceinline__ void grid_wait(unsigned* sync, unsigned epoch, int g,
   __syncthreads();
 }
 
-// one 16-byte piece of a factor row with one of E[prev] (8 products in order)
-__device__ __forceinline__ float dot8(uint4 e, uint4 w) {
-  float acc = 0.f;
-  acc = fmaf(bf16_lo(e.x), bf16_lo(w.x), acc);
-  acc = fmaf(bf16_hi(e.x), bf16_hi(w.x), acc);
-  acc = fmaf(bf16_lo(e.y), bf16_lo(w.y), acc);
-  acc = fmaf(bf16_hi(e.y), bf16_hi(w.y), acc);
-  acc = fmaf(bf16_lo(e.z), bf16_lo(w.z), acc);
-  acc = fmaf(bf16_hi(e.z), bf16_hi(w.z), acc);
-  acc = fmaf(bf16_lo(e.w), bf16_lo(w.w), acc);
-  acc = fmaf(bf16_hi(e.w), bf16_hi(w.w), acc);
-  return acc;
-}
-
 // Word i (0..3) of a Philox quad without indexing (an indexed pick can become a scratch access).
 __device__ __forceinline__ uint32_t quad_pick(const Words4& q, int i) {
   const uint32_t lo = (i & 1) ? q.w[1] : q.w[0], hi = (i & 1) ? q.w[3] : q.w[2];
@@ -522,7 +508,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
       __syncthreads();  // s_tp is reused for the dot partials
       float* s_part = reinterpret_cast<float*>(s_tp);
 #pragma unroll
-      for (int i = 0; i < NP; ++i) s_part[(i * RG + grp) * STR + c] = dot8(ep, w[i]);
+      for (int i = 0; i < NP; ++i) s_part[(i * RG + grp) * STR + c] = dot_bf16x8(ep, w[i]);
       __syncthreads();
       float score = -INFINITY;
       int idx = 0x7fffffff;

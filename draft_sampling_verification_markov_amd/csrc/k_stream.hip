@@ -1517,19 +1517,6 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
 // to bf16), one 16-byte load per thread instead of a half row per thread.  The
 // partial dot products go through LDS once: thread r < 128 sums the PR
 // partials of row r in column order (a cross-lane shuffle tree costs more).
-__device__ __forceinline__ float dot_bf16x8(uint4 e, uint4 w) {
-  float acc = 0.f;
-  acc = fmaf(bf16_lo(e.x), bf16_lo(w.x), acc);
-  acc = fmaf(bf16_hi(e.x), bf16_hi(w.x), acc);
-  acc = fmaf(bf16_lo(e.y), bf16_lo(w.y), acc);
-  acc = fmaf(bf16_hi(e.y), bf16_hi(w.y), acc);
-  acc = fmaf(bf16_lo(e.z), bf16_lo(w.z), acc);
-  acc = fmaf(bf16_hi(e.z), bf16_hi(w.z), acc);
-  acc = fmaf(bf16_lo(e.w), bf16_lo(w.w), acc);
-  acc = fmaf(bf16_hi(e.w), bf16_hi(w.w), acc);
-  return acc;
-}
-
 template <typename ZT, int R>
 __global__ __launch_bounds__(256) void k_select_b16(SelectArgs a) {
   constexpr int PR = R / 8;                         // 16-byte pieces per Wt row (2..32)
