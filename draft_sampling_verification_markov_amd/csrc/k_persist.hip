@@ -18,11 +18,10 @@
 //  1. the previous tokens of all rows into LDS;
 //  2. per N-tile of 32 rows: the E rows of its previous tokens arrive in LDS
 //     by DMA one N-tile ahead (two buffers, rows padded by 16 bytes); per
-//     M-tile the wave chains 16 MFMAs from a zero accumulator (the Markov term
-//     at its own magnitude) while its vector unit finishes the previous
-//     M-tile: logits = base logits (requested into registers one N-tile ahead)
-//     + Markov term, then (max, sum of 2^(x - max)) in base 2 per (row,
-//     M-tile), into LDS;
+//     M-tile the wave chains 16 MFMAs starting from the base logits (requested
+//     into registers one N-tile ahead), so the chain ends at the logits, while
+//     its vector unit finishes the previous M-tile: (max, sum of 2^(x - max))
+//     in base 2 per (row, M-tile), into LDS;
 //  3. per 128 rows: chunk log-masses, chunk Gumbels, the best chunk and the
 //     running log-partition, one partial record per (row, workgroup), stored
 //     past the L2;
@@ -310,15 +309,16 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
     }
     barrier_lds_only();
   };
-  // the reduction of one (N-tile, M-tile) accumulator: logits = base + Markov
-  // term (one rounding), then (max, sum of 2^(x - max)) in base 2 into LDS
-  auto epilogue = [&](int nt, int j, const f32x16_t& acc, const uint4 (&zj)[ZP]) {
+  // the reduction of one (N-tile, M-tile) accumulator (the logits: the
+  // chain started from the base logits): (max, sum of 2^(x - max)) in base 2
+  // into LDS
+  auto epilogue = [&](int nt, int j, const f32x16_t& acc) {
     float ell[16];
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      ell[2 * i] = zval(j, zj, 2 * i) + acc[2 * i];
-      ell[2 * i + 1] = zval(j, zj, 2 * i + 1) + acc[2 * i + 1];
+      ell[2 * i] = acc[2 * i];
+      ell[2 * i + 1] = acc[2 * i + 1];
       m = fmaxf(m, fmaxf(ell[2 * i], ell[2 * i + 1]));
     }
     m = halves32_max(m);
@@ -333,7 +333,8 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
   // N-tile nt of position k: its E rows are in cur and its base logits in
   // zc; the next N-tile's rows (into nxt) are requested first, and its base
   // logits one M-tile per stage (bf16: into zn; fp32: into zc, each M-tile's as
-  // soon as its epilogue has read them, always issued) well ahead of their use.
+  // soon as its stage has taken them into the accumulator, always issued) well
+  // ahead of their use.
   // Requesting all of them at once would stall the wave at issue while the
   // earlier requests drain at the workgroup's share of the memory bandwidth.
   auto tile = [&](int k, int nt, uint4 (&zc)[kPMt][ZP], uint4 (&zn)[kPMt][ZP], const unsigned char* cur,
@@ -343,15 +344,16 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
     const unsigned char* brow = cur + (l32 * RS + h) * 16;
     auto bfrag = [&](int t) { return *reinterpret_cast<const bf16x8_t*>(brow + 32 * t); };
     // Every M-tile is computed (a missing one has zero fragments and its
-    // result is never read).  Stage j chains M-tile j's 16 MFMAs, its LDS
-    // fragments read D K-steps ahead, and gives each K-step a fixed slice
-    // of M-tile j-1's epilogue: steps 0-7 form the logits and their maximum,
-    // step 8 merges the column halves, steps 9-15 the exponentials and sums.
-    // Scheduling barriers keep the slices where they are written.
-    auto stage = [&](int j, int pj, const f32x16_t& pacc, uint4 (&pz)[ZP]) {
+    // result is never read).  Stage j chains M-tile j's 16 MFMAs from its base
+    // logits (so the chain ends at the logits; entries past V start at -inf),
+    // its LDS fragments read D K-steps ahead, and gives each K-step a fixed
+    // slice of M-tile j-1's epilogue: steps 0-7 the maximum, step 8 merges the
+    // column halves, steps 9-15 the exponentials and sums.  Scheduling barriers
+    // keep the slices where they are written.
+    auto stage = [&](int j, int pj, const f32x16_t& pacc) {
       f32x16_t acc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[i] = zval(j, zc[j], i);
       constexpr int D = kF32 ? 2 : 3;  // fp32: a shorter ring leaves the registers the refills need
       bf16x8_t bq[D + 1], aq[D + 1];
 #pragma unroll
@@ -370,13 +372,12 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
                                                       bq[t % (D + 1)], acc, 0, 0, 0);
         if (pj >= 0) {
           if (t < 8) {
-            ell[2 * t] = zval(pj, pz, 2 * t) + pacc[2 * t];
-            ell[2 * t + 1] = zval(pj, pz, 2 * t + 1) + pacc[2 * t + 1];
+            ell[2 * t] = pacc[2 * t];
+            ell[2 * t + 1] = pacc[2 * t + 1];
             m = fmaxf(m, fmaxf(ell[2 * t], ell[2 * t + 1]));
           } else if (t == 8) {
             m = halves32_max(m);
             off = m == -INFINITY ? 0.f : -m * scale2;
-            if (kF32) zload_one(k, nt + 1, pj, pz);  // read: refill with the next N-tile's
           } else {
             // steps 9..14 two entries each, step 15 the last four
             const int e0 = 2 * (t - 9), e1 = t == 15 ? 16 : e0 + 2;
@@ -390,7 +391,9 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
             }
           }
         }
-        if (!kF32 && t == 2 && more) zload_one(k, nt + 1, j, zn[j]);
+        // the next N-tile's base logits of M-tile j (fp32: in place, read by the
+        // accumulator's start above)
+        if (t == 2 && (kF32 || more)) zload_one(k, nt + 1, j, kF32 ? zc[j] : zn[j]);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (pj >= 0) {
@@ -401,18 +404,17 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
       return acc;
     };
     const f32x16_t zero = {};
-    f32x16_t a0 = stage(0, -1, zero, zc[0]);
-    f32x16_t a1 = stage(1, 0, a0, zc[0]);
-    a0 = stage(2, 1, a1, zc[1]);
-    a1 = stage(3, 2, a0, zc[2]);
-    a0 = stage(4, 3, a1, zc[3]);
-    epilogue(nt, 4, a0, zc[4]);
+    f32x16_t a0 = stage(0, -1, zero);
+    f32x16_t a1 = stage(1, 0, a0);
+    a0 = stage(2, 1, a1);
+    a1 = stage(3, 2, a0);
+    a0 = stage(4, 3, a1);
+    epilogue(nt, 4, a0);
     // this wave's gather of N-tile nt + 1 is complete (bf16: and the base
     // logits loaded with it; fp32: the kPMt * ZP refills issued after it may
     // still be in flight); after the barrier every wave's rows are in and no
     // wave reads cur any more
     if (kF32) {
-      zload_one(k, nt + 1, kPMt - 1, zc[kPMt - 1]);
       wait_vmem_n<kPMt * ZP>();
     } else {
       wait_vmem();
