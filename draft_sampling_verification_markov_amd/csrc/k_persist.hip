@@ -239,15 +239,21 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
   // E rows of N-tile nt's previous tokens into dst, by LDS DMA: instruction q
   // fills slots 64q .. 64q + 63, lane i slot 64q + i (a padding slot loads
   // piece 0; lanes past the last slot are off)
+  // (the instruction index passes through an empty asm statement so that the
+  // slot and destination arithmetic stays where the request is issued: hoisted
+  // out of the N-tile loop it would hold registers per stage)
+  auto gather_one = [&](int nt, unsigned char* dst, int q) {
+    int qs = __builtin_amdgcn_readfirstlane(q);
+    __asm__ volatile("" : "+s"(qs));
+    const int sl = qs * 64 + lane;
+    const int row = sl / RS, piece = sl - row * RS;
+    if (sl < NSLOT)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ers, (__attribute__((address_space(3))) void*)(dst + qs * 1024), 16,
+          (int)((uint32_t)s_tok[nt * 32 + row] * ROWB + (uint32_t)(piece < PR ? piece : 0) * 16), 0, 0, 0);
+  };
   auto gather = [&](int nt, unsigned char* dst) {
-    for (int q = wave; q * 64 < NSLOT; q += kPWaves) {
-      const int sl = q * 64 + lane;
-      const int row = sl / RS, piece = sl - row * RS;
-      if (sl < NSLOT)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ers, (__attribute__((address_space(3))) void*)(dst + q * 1024), 16,
-            (int)((uint32_t)s_tok[nt * 32 + row] * ROWB + (uint32_t)(piece < PR ? piece : 0) * 16), 0, 0, 0);
-    }
+    for (int q = wave; q * 64 < NSLOT; q += kPWaves) gather_one(nt, dst, q);
   };
   // per-row merge of the M-tile partials of N-tiles 4*half .. 4*half+3:
   // chunk log-masses, chunk Gumbels, best chunk, running log-partition, as one
@@ -331,8 +337,8 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
     s_tp[((nt & 3) * 32 + l32) * kPMtWg + wave * kPMt + j] = make_float2(m * scale2, sm);
   };
   // N-tile nt of position k: its E rows are in cur and its base logits in
-  // zc; the next N-tile's rows (into nxt) are requested first, and its base
-  // logits one M-tile per stage (bf16: into zn; fp32: into zc, each M-tile's as
+  // zc; the next N-tile's rows (into nxt: gather instruction wave + 4j in
+  // stage j) and its base logits are requested one M-tile per stage (bf16: into zn; fp32: into zc, each M-tile's as
   // soon as its stage has taken them into the accumulator, always issued) well
   // ahead of their use.
   // Requesting all of them at once would stall the wave at issue while the
@@ -340,7 +346,6 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
   auto tile = [&](int k, int nt, uint4 (&zc)[kPMt][ZP], uint4 (&zn)[kPMt][ZP], const unsigned char* cur,
                   unsigned char* nxt) {
     const bool more = nt + 1 < NT;
-    if (more) gather(nt + 1, nxt);
     const unsigned char* brow = cur + (l32 * RS + h) * 16;
     auto bfrag = [&](int t) { return *reinterpret_cast<const bf16x8_t*>(brow + 32 * t); };
     // Every M-tile is computed (a missing one has zero fragments and its
@@ -393,6 +398,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
         }
         // the next N-tile's base logits of M-tile j (fp32: in place, read by the
         // accumulator's start above)
+        if (t == 1 && more && (wave + kPWaves * j) * 64 < NSLOT) gather_one(nt + 1, nxt, wave + kPWaves * j);
         if (t == 2 && (kF32 || more)) zload_one(k, nt + 1, j, kF32 ? zc[j] : zn[j]);
         __builtin_amdgcn_sched_barrier(0);
       }
