@@ -337,8 +337,10 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
     s_tp[((nt & 3) * 32 + l32) * kPMtWg + wave * kPMt + j] = make_float2(m * scale2, sm);
   };
   // N-tile nt of position k: its E rows are in cur and its base logits in
-  // zc; the next N-tile's rows (into nxt: gather instruction wave + 4j in
-  // stage j) and its base logits are requested one M-tile per stage (bf16: into zn; fp32: into zc, each M-tile's as
+  // zc; the next N-tile's rows (into nxt; bf16: gather instruction wave + 4j in
+  // stage j; fp32: all at the start, ahead of every refill, which the
+  // end-of-tile wait counts on) and its base logits are requested one M-tile
+  // per stage (bf16: into zn; fp32: into zc, each M-tile's as
   // soon as its stage has taken them into the accumulator, always issued) well
   // ahead of their use.
   // Requesting all of them at once would stall the wave at issue while the
@@ -346,6 +348,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
   auto tile = [&](int k, int nt, uint4 (&zc)[kPMt][ZP], uint4 (&zn)[kPMt][ZP], const unsigned char* cur,
                   unsigned char* nxt) {
     const bool more = nt + 1 < NT;
+    if (kF32 && more) gather(nt + 1, nxt);
     const unsigned char* brow = cur + (l32 * RS + h) * 16;
     auto bfrag = [&](int t) { return *reinterpret_cast<const bf16x8_t*>(brow + 32 * t); };
     // Every M-tile is computed (a missing one has zero fragments and its
@@ -398,7 +401,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
         }
         // the next N-tile's base logits of M-tile j (fp32: in place, read by the
         // accumulator's start above)
-        if (t == 1 && more && (wave + kPWaves * j) * 64 < NSLOT) gather_one(nt + 1, nxt, wave + kPWaves * j);
+        if (!kF32 && t == 1 && more && (wave + kPWaves * j) * 64 < NSLOT) gather_one(nt + 1, nxt, wave + kPWaves * j);
         if (t == 2 && (kF32 || more)) zload_one(k, nt + 1, j, kF32 ? zc[j] : zn[j]);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -417,9 +420,9 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
     a0 = stage(4, 3, a1);
     epilogue(nt, 4, a0);
     // this wave's gather of N-tile nt + 1 is complete (bf16: and the base
-    // logits loaded with it; fp32: the kPMt * ZP refills issued after it may
-    // still be in flight); after the barrier every wave's rows are in and no
-    // wave reads cur any more
+    // logits loaded with it; fp32: the kPMt * ZP refills, all issued after the
+    // gather, may still be in flight); after the barrier every wave's rows are
+    // in and no wave reads cur any more
     if (kF32) {
       wait_vmem_n<kPMt * ZP>();
     } else {

@@ -147,6 +147,8 @@ SCHEDULES = [
     ("persist_b48", 2),
     ("qwen3_4b", 1),
     ("persist_f32_ragged", 2),
+    ("persist_b150", 2),
+    ("persist_f32_b256", 2),
 ]
 
 
@@ -169,6 +171,12 @@ def _schedule_cfg(name):
         return base.replace(name=name, B=33, K=3, V=1000, r=256, d=64, logits_dtype="f32", seed=21)
     if name == "persist_b48":
         return synth.get_config("high_concurrency").replace(name=name, B=48, K=4, seed=20)
+    if name == "persist_b150":
+        # five N-tiles, the last ragged (22 rows), and the second half-batch merge on a partial half
+        return synth.get_config("high_concurrency").replace(name=name, B=150, K=3, seed=22)
+    if name == "persist_f32_b256":
+        # fp32 base logits at the full batch (dspark_draft takes the persistent schedule there)
+        return synth.get_config("high_concurrency").replace(name=name, K=2, logits_dtype="f32", seed=23)
     return synth.get_config(name)
 
 
