@@ -45,7 +45,8 @@ Layout make_layout(const dspark_problem& P) {
   L.sorti = off;  off = align_up(off + B * K * sizeof(int32_t));
   L.lagn = off;   off = align_up(off + (B + 1) * sizeof(int32_t));
   L.efrag = off;  off = align_up(off + (size_t)((B + 31) / 32) * 32 * (size_t)P.r * 2);
-  L.ptok = off;   off = align_up(off + B * sizeof(int32_t));
+  L.prec = off;   off = align_up(off + (B <= (size_t)kPersistMaxB ? B * (size_t)persist_grid(P.V) * 32 : 0));
+  L.ptok = off;   off = align_up(off + (size_t)kSyncGroups * kTokRepSlots * sizeof(unsigned long long));
   L.psync = off;  off = align_up(off + kPersistSyncWords * sizeof(uint32_t));
   L.total = off;
   return L;
@@ -241,8 +242,8 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
     pa.tok = draft_tok;
     pa.logq = draft_logq;
     pa.lse = draft_lse;
-    pa.part = part;
-    pa.ptok = at<int32_t>(workspace, L.ptok);
+    pa.rec = at<unsigned long long>(workspace, L.prec);
+    pa.tokrep = at<unsigned long long>(workspace, L.ptok);
     pa.sync = at<unsigned>(workspace, L.psync);
     pa.B = p.B;
     pa.K = p.K;
@@ -250,10 +251,10 @@ static dspark_status draft_impl(const dspark_problem* P, const void* Z, const vo
     pa.nchunks = n_chunks(p.V);
     pa.z_bytes = (uint32_t)((size_t)p.B * p.K * p.V * (p.logits_dtype == DSPARK_F32 ? 4 : 2));
     pa.spin_limit = kPersistSpinLimit;
-    pa.arrive_extra = 0;
+    pa.unreachable = 0;
     if (kDebugChecks && g_debug_force_timeout) {  // every barrier wait times out after a few polls
       pa.spin_limit = 64;
-      pa.arrive_extra = 1;
+      pa.unreachable = 1;
     }
     pa.scale2 = sa.scale2;
     pa.inv_T = se.inv_T;

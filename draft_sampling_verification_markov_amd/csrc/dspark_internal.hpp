@@ -55,8 +55,9 @@ struct Layout {
   size_t sorti; // int32 [B*K]: candidate indices in schedule order (same)
   size_t lagn;  // int32 [B + 1]: the lagged schedule of the asynchronous scheduler (n_b, then N)
   size_t efrag; // uint4 [ceil(B/32)][r/16][64]: E rows of the previous draft tokens, B-fragment order
-  size_t ptok;  // int32 [B]: the persistent draft's tokens of the latest position (read by every workgroup)
-  size_t psync; // uint32 [kPersistSyncWords]: the persistent draft's grid-barrier words and time-out flag
+  size_t prec;  // uint64 [B][persist_grid][4]: the persistent draft's tagged partial records (B <= 256)
+  size_t ptok;  // uint64 [kSyncGroups][kTokRepSlots]: the persistent draft's tagged tokens, one replica per group
+  size_t psync; // uint32 [kPersistSyncWords]: the persistent draft's time-out flag and launch generation
   size_t total;
 };
 
@@ -94,12 +95,12 @@ struct PersistArgs {
   int32_t* tok;          // [B][K] outputs
   float* logq;
   float* lse;
-  float4* part;          // [B][G] per-(row, workgroup) partials of the latest position
-  int32_t* ptok;         // [B] tokens of the latest position
-  unsigned* sync;        // [kPersistSyncWords] barrier words (zero at launch) and the time-out flag
+  unsigned long long* rec;    // [B][G][4] tagged partial records of the latest positions
+  unsigned long long* tokrep; // [kSyncGroups][kTokRepSlots] tagged tokens of the latest positions
+  unsigned* sync;        // [kPersistSyncWords] time-out flag (zeroed) and launch generation (advanced) at launch
   uint32_t z_bytes;      // bytes of Z (below 2^32)
-  uint32_t spin_limit;   // polls of a barrier wait before it gives up (kPersistSpinLimit)
-  uint32_t arrive_extra; // arrivals a barrier waits for beyond the grid's (0; 1 makes every wait time out)
+  uint32_t spin_limit;   // polls of a wait before it gives up (kPersistSpinLimit)
+  uint32_t unreachable;  // 0; nonzero makes every wait's expected tag one that is never written (all time out)
   int B, K, V, nchunks;
   float scale2, inv_T;
   Key key;
@@ -231,17 +232,19 @@ int persist_grid(int V);
 inline int persist_max_b(const dspark_problem& P) { return P.logits_dtype == DSPARK_F32 ? 256 : 160; }
 // polls of a persistent-draft barrier wait before it sets the time-out flag
 constexpr uint32_t kPersistSpinLimit = 1u << 20;
-// The persistent draft's grid barrier: kSyncGroups arrival counters, as many
-// release words, one top-level counter and the time-out flag, each word
-// kSyncStride words (4 KiB) from the next so that no two share a cache line or
-// a memory channel's interleave unit.
+// The persistent draft's hand-offs between workgroups carry their own tags
+// (launch generation x 128 + position), so that a wait polls the data it needs
+// instead of a barrier counter: the time-out flag and the generation each on
+// their own 4 KiB, and kSyncGroups replicas of the latest tokens (one per group
+// of workgroups, 4 KiB apart) so that no word has more than G / kSyncGroups + 1
+// pollers.
 constexpr int kSyncGroups = 16;
-constexpr int kSyncStride = 1024;
-constexpr int kSyncRelease = kSyncGroups;      // release word j at (kSyncRelease + j) * kSyncStride
-constexpr int kSyncTop = 2 * kSyncGroups;      // top-level counter
-constexpr int kSyncFlag = 2 * kSyncGroups + 1; // time-out flag
-constexpr int kPersistSyncSlots = 2 * kSyncGroups + 2;
-constexpr size_t kPersistSyncWords = (size_t)kPersistSyncSlots * kSyncStride;
+constexpr int kSyncStride = 1024;                // words between the flag and the generation
+constexpr int kSyncFlag = 0;                     // time-out flag at kSyncFlag * kSyncStride
+constexpr int kSyncGen = 1;                      // launch generation at kSyncGen * kSyncStride
+constexpr size_t kPersistSyncWords = 2 * (size_t)kSyncStride;
+constexpr int kTokRepSlots = 512;                // 8-byte slots per token replica (rows 0..255 used)
+constexpr int kPersistMaxB = 256;
 bool draft_persistent_supported(const dspark_problem& P);
 hipError_t launch_draft_persistent(const dspark_problem& P, const PersistArgs& a, hipStream_t s);
 hipError_t launch_conf(const dspark_problem& P, const ConfArgs& a, hipStream_t s);

@@ -15,7 +15,7 @@
 // in registers for the whole cycle (4 x 16 K-steps x 16 bytes per lane: 256
 // registers) and those of its fifth in LDS (64 KB for the workgroup).
 // Per position k:
-//  1. the previous tokens of all rows into LDS;
+//  1. the previous tokens of all rows into LDS (each awaited as in 6);
 //  2. per N-tile of 32 rows: the E rows of its previous tokens arrive in LDS
 //     by DMA one N-tile ahead (two buffers, rows padded by 16 bytes); per
 //     M-tile the wave chains 16 MFMAs starting from the base logits (requested
@@ -24,17 +24,22 @@
 //     in base 2 per (row, M-tile), into LDS;
 //  3. per 128 rows: chunk log-masses, chunk Gumbels, the best chunk and the
 //     running log-partition, one partial record per (row, workgroup), stored
-//     past the L2;
-//  4. grid barrier;
-//  5. selection: workgroup g takes rows g, g + G, ...: merges the row's G
-//     partials, reads the winning chunk's Wt block, recomputes its 128 logits,
-//     draws the entry, and writes the token, log q and the log-partition (the
-//     token also past the L2, for every workgroup's next gather);
-//  6. grid barrier, while the next position's first base logits are requested.
-// Records read after a barrier are read past the L2 as well (an XCD's L2 is
-// not kept coherent with another's).  Every barrier wait is bounded: past the
-// limit the time-out flag is set and the waits that follow return at once, so
-// the kernel always ends (its results are then unspecified).
+//     past the L2 as four tagged words;
+//  4. selection: workgroup g takes rows g, g + G, ...: thread t waits for
+//     workgroup t's record of the row, then the row's G records are merged,
+//     the winning chunk's Wt block read, its 128 logits recomputed, the entry
+//     drawn, and the token, log q and the log-partition written;
+//  5. the token, tagged, into each group's replica (16 groups of workgroups);
+//  6. while the next position's first base logits are requested, every
+//     workgroup waits for the B tokens in its group's replica.
+// No grid barrier: each wait is for the tagged words it needs (a tag is the
+// launch generation and the position, so a word left by an earlier position or
+// launch never satisfies it), read past the L2 (an XCD's L2 is not kept coherent
+// with another's).  A workgroup writes position k + 1's records only after
+// every token of position k, each written after its row's records of position
+// k were read, and so on: no word is overwritten before it is read.  Every wait
+// is bounded: past the limit the time-out flag is set and the waits that follow
+// return at once, so the kernel always ends (its results are then unspecified).
 #include "dspark_internal.hpp"
 
 namespace dspark {
@@ -70,64 +75,39 @@ __device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
 __device__ __forceinline__ void st_agent(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// a float4 record past the L2, as two 8-byte halves
-__device__ __forceinline__ void st_agent4(float4* p, float4 v) {
-  unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
-  const unsigned long long lo = ((unsigned long long)__float_as_uint(v.y) << 32) | __float_as_uint(v.x);
-  const unsigned long long hi = ((unsigned long long)__float_as_uint(v.w) << 32) | __float_as_uint(v.z);
-  __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// 8-byte words past the L2 (an XCD's L2 is not kept coherent with another's):
+// a 32-bit value in the low half and its tag in the high half, so that one
+// single-copy-atomic load returns the value together with the proof of which
+// position (and launch) wrote it
+__device__ __forceinline__ void st_tagged(unsigned long long* p, uint32_t v, uint32_t tag) {
+  __hip_atomic_store(p, ((unsigned long long)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float4 ld_agent4(const float4* p) {
-  const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
-  const unsigned long long lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const unsigned long long hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float4(__uint_as_float((unsigned)lo), __uint_as_float((unsigned)(lo >> 32)), __uint_as_float((unsigned)hi),
-                     __uint_as_float((unsigned)(hi >> 32)));
+__device__ __forceinline__ unsigned long long ld_tagged(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// Grid barrier in two levels on monotonic counters, in two halves so that
-// loads independent of the other workgroups can be issued between them.
-// Arrive: this workgroup's stores past the L2 complete, then one atomic add on
-// its group's counter (workgroup g is in group g % ng, ng = min(kSyncGroups,
-// G)); the group's last arrival adds one to the top-level counter, and the last
-// of those stores the epoch into every group's release word.  Wait: until the
-// own group's release word holds the epoch.  Each counter then takes at most
-// G / ng + 1 atomics and each release word G / ng + 1 pollers per epoch, instead
-// of all G on one word.  `extra` > 0 makes the top level unreachable (every
-// wait then times out).  Bounded: past `limit` polls the flag is set and this
-// and every later wait return at once.
-__device__ __forceinline__ void grid_arrive(unsigned* sync, unsigned& epoch, int g, int G, unsigned extra) {
-  wait_vmem();
-  __syncthreads();
-  epoch += 1;
-  if (threadIdx.x == 0) {
-    const int ng = G < kSyncGroups ? G : kSyncGroups;
-    const int j = g % ng;
-    const unsigned members = (unsigned)(G / ng + (j < G % ng ? 1 : 0));
-    const unsigned before = __hip_atomic_fetch_add(sync + j * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (before + 1u == epoch * members) {
-      const unsigned top =
-          __hip_atomic_fetch_add(sync + kSyncTop * kSyncStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (top + 1u == epoch * ((unsigned)ng + extra))
-        for (int i = 0; i < ng; ++i) st_agent(sync + (kSyncRelease + i) * kSyncStride, epoch);
+// Poll N consecutive tagged words of this lane until every tag is `expect`;
+// bounded: past `limit` polls (at once if the flag is already set) the
+// time-out flag is set and the words are returned as they are.  Lanes poll
+// independently; the wave leaves when every lane is done.
+template <int N>
+__device__ __forceinline__ void poll_tagged(const unsigned long long* p, uint32_t expect, unsigned* flag,
+                                            uint32_t limit, uint32_t (&v)[N]) {
+  unsigned spins = ld_agent(flag) ? limit : 0u;
+  for (;;) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const unsigned long long w = ld_tagged(p + i);
+      v[i] = (uint32_t)w;
+      ok = ok && (uint32_t)(w >> 32) == expect;
     }
-  }
-}
-__device__ __forceinline__ void grid_wait(unsigned* sync, unsigned epoch, int g, int G, unsigned limit) {
-  if (threadIdx.x == 0) {
-    const int ng = G < kSyncGroups ? G : kSyncGroups;
-    const unsigned* rel = sync + (kSyncRelease + g % ng) * kSyncStride;
-    unsigned spins = ld_agent(sync + kSyncFlag * kSyncStride) ? limit : 0u;
-    while (ld_agent(rel) < epoch) {
-      if (++spins > limit) {
-        st_agent(sync + kSyncFlag * kSyncStride, 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
+    if (ok) break;
+    if (++spins > limit) {
+      st_agent(flag, 1u);
+      break;
     }
+    __builtin_amdgcn_s_sleep(1);
   }
-  __syncthreads();
 }
 
 // Word i (0..3) of a Philox quad without indexing (an indexed pick can become a scratch access).
@@ -169,7 +149,7 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
   __shared__ __attribute__((aligned(16))) float2 s_tp[kPHalf * kPMtWg];
   __shared__ int s_tok[kPRows];
   __shared__ float s_ell[kChunk], s_bm[kPWaves], s_bs[kPWaves], s_best[kPWaves];
-  __shared__ int s_bi[kPWaves];
+  __shared__ int s_bi[kPWaves], s_x;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, h = lane >> 5;
   const int G = gridDim.x, g = blockIdx.x;
@@ -182,6 +162,14 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
   const ZT* Z = static_cast<const ZT*>(a.Z);
   const float scale2 = a.scale2;
   const int vbase = c_begin * kChunk;
+  // hand-offs: tags are generation * 128 + position (positions are at most 64,
+  // so no tag is 127 modulo 128 and 0xFFFFFFFF is an expectation no word ever
+  // meets: every wait then times out)
+  unsigned* const flag = a.sync + kSyncFlag * kSyncStride;
+  const uint32_t gen = ld_agent(a.sync + kSyncGen * kSyncStride);
+  const int ng = G < kSyncGroups ? G : kSyncGroups;
+  auto tag_of = [&](int kk) { return gen * 128u + (uint32_t)kk; };
+  auto expect_of = [&](int kk) { return a.unreachable ? 0xFFFFFFFFu : tag_of(kk); };
 
   // 0. this wave's A fragments (Wt rows of its M-tiles) for the whole cycle:
   // the first JR in registers, the last in LDS; a missing M-tile (past the
@@ -311,7 +299,12 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
         best = ob;
         best_c = oc;
       }
-      st_agent4(a.part + (size_t)prow * G + g, make_float4(mm, ss, best, __int_as_float(best_c)));
+      unsigned long long* rp = a.rec + ((size_t)prow * G + g) * 4;
+      const uint32_t tg = tag_of(k);
+      st_tagged(rp + 0, __float_as_uint(mm), tg);
+      st_tagged(rp + 1, __float_as_uint(ss), tg);
+      st_tagged(rp + 2, __float_as_uint(best), tg);
+      st_tagged(rp + 3, (uint32_t)best_c, tg);
     }
     barrier_lds_only();
   };
@@ -435,13 +428,21 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
   uint4 zA[kPMt][ZP], zB[kPMt][kF32 ? 1 : ZP];
   zload(1, 0, zA);
 
-  unsigned epoch = 0;
   for (int k = 1; k <= K; ++k) {
-    // 1. the previous tokens of all 256 rows (rows past B: token 0), then
-    // the E rows of N-tile 0
+    // 1. the previous tokens of all 256 rows (rows past B: token 0): the
+    // anchors, or this group's replica of the tokens of position k - 1 as each
+    // arrives (the wait for the previous position); then the E rows of N-tile 0
     {
       int x = 0;
-      if (tid < B) x = k == 1 ? a.anchor[tid] : (int)ld_agent(reinterpret_cast<const unsigned*>(a.ptok + tid));
+      if (tid < B) {
+        if (k == 1) {
+          x = a.anchor[tid];
+        } else {
+          uint32_t v[1];
+          poll_tagged<1>(a.tokrep + (size_t)(g % ng) * kTokRepSlots + tid, expect_of(k - 1), flag, a.spin_limit, v);
+          x = (int)v[0];
+        }
+      }
       s_tok[tid] = clamp_id(x, V);
     }
     __syncthreads();
@@ -461,15 +462,16 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
       }
     }
 
-    // 4. every workgroup's partials of position k are out
-    grid_arrive(a.sync, epoch, g, G, a.arrive_extra);
-    grid_wait(a.sync, epoch, g, G, a.spin_limit);
-
-    // 5. selection of rows g, g + G, ...
+    // 4-5. selection of rows g, g + G, ...: thread t < G waits for workgroup
+    // t's record of the row (its tags name position k)
     for (int b = g; b < B; b += G) {
       const int c = tid % PR, grp = tid / PR;
       float4 p = make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
-      if (tid < G) p = ld_agent4(a.part + (size_t)b * G + tid);
+      if (tid < G) {
+        uint32_t v[4];
+        poll_tagged<4>(a.rec + ((size_t)b * G + tid) * 4, expect_of(k), flag, a.spin_limit, v);
+        p = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+      }
       // the winning chunk: argmax of the chunk scores, smallest chunk id on ties
       float best = -INFINITY;
       int bc = 0x7fffffff;
@@ -562,22 +564,27 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
         a.tok[o] = X;
         a.logq[o] = s_ell[X - v0] - lse;
         a.lse[o] = lse;
-        st_agent(reinterpret_cast<unsigned*>(a.ptok + b), (unsigned)X);
+        s_x = X;
       }
+      __syncthreads();
+      // the token, tagged, into every group's replica
+      if (tid < ng) st_tagged(a.tokrep + (size_t)tid * kTokRepSlots + b, (uint32_t)s_x, tag_of(k));
       __syncthreads();
     }
 
-    // 6. every token of position k is out; while the other workgroups arrive,
-    // the next position's first base logits (they do not depend on the tokens)
-    grid_arrive(a.sync, epoch, g, G, a.arrive_extra);
+    // 6. the next position's first base logits (they do not depend on the
+    // tokens), in flight while its tokens are awaited
     if (k < K) zload(k + 1, 0, zA);
-    grid_wait(a.sync, epoch, g, G, a.spin_limit);
   }
 }
 
-// zero the barrier's counters, release words and time-out flag
+// clear the time-out flag and advance the launch generation (every tag of the
+// launch carries it, so no word left by an earlier launch can satisfy a wait)
 __global__ __launch_bounds__(64) void k_persist_init(unsigned* sync) {
-  if (threadIdx.x < kPersistSyncSlots) sync[threadIdx.x * kSyncStride] = 0u;
+  if (threadIdx.x == 0) {
+    sync[kSyncFlag * kSyncStride] = 0u;
+    sync[kSyncGen * kSyncStride] += 1u;
+  }
 }
 
 }  // namespace
