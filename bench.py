@@ -109,7 +109,7 @@ class Hip:
             self.lib.hipEventDestroy(h)
 
 
-PERSIST_MAX_B = {"bf16": 160, "f32": 256}  # dspark_draft's batch limits for the persistent schedule, by logits dtype
+PERSIST_MAX_B = {"bf16": 192, "f32": 256}  # dspark_draft's batch limits for the persistent schedule, by logits dtype
 
 
 def draft_persistent(cfg) -> bool:

@@ -229,7 +229,7 @@ int persist_grid(int V);
 // most this (the measured crossovers: with bf16 logits the per-position kernels,
 // with two waves per SIMD, are faster above it; with fp32 logits they stream
 // twice the bytes and the persistent draft is faster up to its limit of 256)
-inline int persist_max_b(const dspark_problem& P) { return P.logits_dtype == DSPARK_F32 ? 256 : 160; }
+inline int persist_max_b(const dspark_problem& P) { return P.logits_dtype == DSPARK_F32 ? 256 : 192; }
 // polls of a persistent-draft barrier wait before it sets the time-out flag
 constexpr uint32_t kPersistSpinLimit = 1u << 20;
 // The persistent draft's hand-offs between workgroups carry their own tags
