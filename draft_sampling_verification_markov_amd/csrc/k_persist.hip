@@ -578,13 +578,19 @@ __global__ __launch_bounds__(kPThreads, 1) void k_draft_persist(PersistArgs a) {
   }
 }
 
-// clear the time-out flag and advance the launch generation (every tag of the
-// launch carries it, so no word left by an earlier launch can satisfy a wait)
-__global__ __launch_bounds__(64) void k_persist_init(unsigned* sync) {
-  if (threadIdx.x == 0) {
+// Before each launch: clear the time-out flag, advance the launch generation
+// (every tag of the launch carries it) and clear every record and token word
+// (a cleared word's tag, 0, is no position's), so that no word left by an
+// earlier launch, or by other data in a reused workspace, satisfies a wait.
+__global__ __launch_bounds__(256) void k_persist_init(unsigned* sync, unsigned long long* rec, int n_rec,
+                                                      unsigned long long* tokrep, int n_tok) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i == 0) {
     sync[kSyncFlag * kSyncStride] = 0u;
     sync[kSyncGen * kSyncStride] += 1u;
   }
+  for (int j = i; j < n_rec; j += gridDim.x * 256) rec[j] = 0ull;
+  for (int j = i; j < n_tok; j += gridDim.x * 256) tokrep[j] = 0ull;
 }
 
 }  // namespace
@@ -621,7 +627,10 @@ bool draft_persistent_supported(const dspark_problem& P) {
 }
 
 hipError_t launch_draft_persistent(const dspark_problem& P, const PersistArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_persist_init, 1, 64, 0, s, a.sync);
+  const int n_rec = P.B * persist_grid(P.V) * 4;  // B <= 256: at most 256 x 256 x 4 words
+  const int n_tok = kSyncGroups * kTokRepSlots;
+  const int blocks = (n_rec + 256 * 8 - 1) / (256 * 8);  // about 8 words per thread
+  hipLaunchKernelGGL(k_persist_init, blocks, 256, 0, s, a.sync, a.rec, n_rec, a.tokrep, n_tok);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   PersistArgs arg = a;
