@@ -144,6 +144,14 @@ struct Logits<uint16_t> {  // bf16
     const uint32_t w = (i < 2) ? r.u[q].x : r.u[q].y;
     return (i & 1) ? bf16_hi(w) : bf16_lo(w);
   }
+  // the four groups of M-tile mt only, into groups 0..3 of r
+  __device__ __forceinline__ static void load_mt(Raw& r, const uint16_t* row, int v0, int V, int lane, int mt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = v0 + mt * 32 + j * 8 + 4 * (lane >> 5);
+      r.u[j] = v < V ? *reinterpret_cast<const uint2*>(row + v) : make_uint2(0u, 0u);
+    }
+  }
   __device__ __forceinline__ static float one(const uint16_t* row, int v) { return bf16_to_f32(row[v]); }
 };
 
@@ -161,6 +169,13 @@ struct Logits<float> {
   }
   __device__ __forceinline__ static float get(const Raw& r, int q, int i) {
     return i == 0 ? r.f[q].x : i == 1 ? r.f[q].y : i == 2 ? r.f[q].z : r.f[q].w;
+  }
+  __device__ __forceinline__ static void load_mt(Raw& r, const float* row, int v0, int V, int lane, int mt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = v0 + mt * 32 + j * 8 + 4 * (lane >> 5);
+      r.f[j] = v < V ? *reinterpret_cast<const float4*>(row + v) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
   __device__ __forceinline__ static float one(const float* row, int v) { return row[v]; }
 };
@@ -336,6 +351,170 @@ __global__ __launch_bounds__(kThreads, 1) void k_stream_generic(StreamArgs a) {
         a.zpart[(size_t)b * G + g] = make_float2((float)Zp_g, (float)Zq_g);
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------- verify, small batches
+// The resample pass of the generic path (fp32 logits or fp32 factors) for
+// B <= 64.  The all-rows mapping gives each wave 32 rows and every M-tile of a
+// chunk, so at B <= 32 one wave of eight does all the MFMAs and the whole
+// residual epilogue; here wave w takes rows 32 (w / 4) .. + 31 and M-tile w % 4
+// of each chunk, and the four M-tile waves of a row group exchange their
+// per-chunk results through LDS (the residual mass, or a bonus row's (max,
+// sum)), from which the first keeps the chunk score and the best chunk.  Same
+// per-entry arithmetic as k_stream_generic; the fp64 sums meet across the four
+// waves at the end.
+template <typename ZT, typename WT, int R>
+__global__ __launch_bounds__(kThreads, 1) void k_verify_smallb(StreamArgs a) {
+  using F = Frag<WT, R>;
+  using L = Logits<ZT>;
+  __shared__ __attribute__((aligned(16))) WT lds[F::kLdsElems];
+  __shared__ float s_x[2][4][2][32];   // [row group][M-tile][residual mass or max, sum][row]
+  __shared__ double s_d[2][4][4][32];  // [row group][M-tile][R, QA, Zp, Zq][row]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rg = wave >> 2, mt = wave & 3;
+  const int G = gridDim.x, g = blockIdx.x;
+  const int c_begin = (int)(((long long)g * a.nchunks) / G);
+  const int c_end = (int)(((long long)(g + 1) * a.nchunks) / G);
+  const ZT* Z = static_cast<const ZT*>(a.Z);
+  const ZT* Zt = static_cast<const ZT*>(a.Zt);
+  const int V = a.V, K = a.K;
+  const int b = rg * 32 + (lane & 31);
+  const bool rv = b < a.B;
+  const bool wave_on = rg * 32 < a.B;
+
+  // per-row set-up (the generic kernel's verify mode)
+  int prev = 0, kpos = 1;
+  uint32_t purpose = kBonusChunk;
+  const ZT* zrow = Z;
+  const ZT* trow = Zt;
+  bool resid = false;
+  float lsq2 = 0.f, lsp2 = 0.f, dlp = 0.f;
+  if (rv) {
+    const int ks = a.job[b];
+    if (ks > 0) {
+      resid = true;
+      kpos = ks;
+      purpose = kResidChunk;
+      prev = clamp_id(ks == 1 ? a.anchor[b] : a.tok[(size_t)b * K + ks - 2], V);
+      zrow = Z + ((size_t)b * K + (ks - 1)) * V;
+      trow = Zt + ((size_t)b * (K + 1) + (ks - 1)) * V;
+      lsq2 = a.lse_q[(size_t)b * K + ks - 1] * kLog2e;
+      lsp2 = a.lse_p[(size_t)b * K + ks - 1] * kLog2e;
+      dlp = lsp2 - lsq2;
+    } else {
+      int nb = a.n_sched[b];
+      nb = nb < 0 ? 0 : (nb > K ? K : nb);
+      kpos = nb + 1;
+      trow = Zt + ((size_t)b * (K + 1) + nb) * V;
+    }
+  }
+  F frag;
+  frag.load(static_cast<const WT*>(a.E), prev, rv && resid, lane);
+
+  float best = -INFINITY;
+  int best_c = 0x7fffffff;
+  int quad_id = -1;
+  Words4 quad = {};
+  double Rs = 0.0, QAs = 0.0, Zps = 0.0, Zqs = 0.0;
+
+  for (int c = c_begin; c < c_end; ++c) {
+    __syncthreads();
+    F::stage(lds, static_cast<const WT*>(a.Wt), c, V, tid);
+    __syncthreads();
+    const int v0 = c * kChunk;
+    typename L::Raw zr = {}, tr = {};
+    if (wave_on && rv) {
+      if (resid) L::load_mt(zr, zrow, v0, V, lane, mt);
+      L::load_mt(tr, trow, v0, V, lane, mt);
+    }
+    f32x16_t acc = {};
+    if (wave_on) frag.mma(lds, mt, acc, lane);
+    float x0 = 0.f, x1 = 0.f;
+    if (wave_on && rv) {
+      if (resid) {
+        ResidSums sums;
+        sums.clear();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = i >> 2;  // the M-tile's groups sit in groups 0..3
+          const int v = v0 + mt * 32 + (i >> 2) * 8 + 4 * (lane >> 5) + (i & 3);
+          const bool in = v < V;  // entries past V: target and draft logit -inf, every weight 0
+          sums.add(i, resid_entry(in ? L::get(tr, q, i & 3) : -INFINITY, in ? L::get(zr, q, i & 3) : -INFINITY,
+                                  acc[i], a.scale2, lsp2, lsq2, dlp));
+        }
+        const float rs = ResidSums::fold(sums.r);
+        Rs += (double)rs;
+        QAs += (double)ResidSums::fold(sums.qa);
+        Zps += (double)ResidSums::fold(sums.p);
+        Zqs += (double)ResidSums::fold(sums.q);
+        x0 = halves32_sum(rs);
+      } else {
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = i >> 2;
+          const int v = v0 + mt * 32 + (i >> 2) * 8 + 4 * (lane >> 5) + (i & 3);
+          const float x = v < V ? L::get(tr, q, i & 3) * a.scale2 : -INFINITY;
+          acc[i] = x;
+          m = fmaxf(m, x);
+        }
+        m = fmaxf(m, __shfl_xor(m, 32));
+        float sm = 0.f;
+        if (m != -INFINITY) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sm += exp2f(acc[i] - m);
+        }
+        sm += __shfl_xor(sm, 32);
+        x0 = m;
+        x1 = sm;
+      }
+    }
+    if (lane < 32) {
+      s_x[rg][mt][0][lane] = x0;
+      s_x[rg][mt][1][lane] = x1;
+    }
+    __syncthreads();
+    if (wave_on && rv && mt == 0) {
+      if (c >> 2 != quad_id) {
+        quad = draw_quad(a.key, (uint32_t)c, (uint32_t)b, (uint32_t)kpos, purpose);
+        quad_id = c >> 2;
+      }
+      const float gum = gumbel_from_word(quad_word(quad, c & 3));
+      const int r = lane & 31;
+      float score = -INFINITY;
+      if (resid) {
+        const float rs = (s_x[rg][0][0][r] + s_x[rg][1][0][r]) + (s_x[rg][2][0][r] + s_x[rg][3][0][r]);
+        score = rs > 0.f ? logf(rs) + gum : -INFINITY;
+      } else {
+        float m = s_x[rg][0][0][r], sm = s_x[rg][0][1][r];
+#pragma unroll
+        for (int j = 1; j < 4; ++j) lse2_merge(m, sm, s_x[rg][j][0][r], s_x[rg][j][1][r]);
+        score = sm > 0.f ? (m + log2f(sm)) * kLn2 + gum : -INFINITY;
+      }
+      if (score > best) {
+        best = score;
+        best_c = c;
+      }
+    }
+  }
+  // the row's fp64 sums over the four M-tile waves
+  const double R_w = halves32_sum_d(Rs), QA_w = halves32_sum_d(QAs);
+  const double Zp_w = halves32_sum_d(Zps), Zq_w = halves32_sum_d(Zqs);
+  if (lane < 32) {
+    s_d[rg][mt][0][lane] = R_w;
+    s_d[rg][mt][1][lane] = QA_w;
+    s_d[rg][mt][2][lane] = Zp_w;
+    s_d[rg][mt][3][lane] = Zq_w;
+  }
+  __syncthreads();
+  if (mt == 0 && rv && lane < 32) {
+    double t[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t[q] = (s_d[rg][0][q][lane] + s_d[rg][1][q][lane]) + (s_d[rg][2][q][lane] + s_d[rg][3][q][lane]);
+    a.part[(size_t)b * G + g] = make_float4((float)t[0], (float)t[1], best, __int_as_float(best_c));
+    a.zpart[(size_t)b * G + g] = make_float2((float)t[2], (float)t[3]);
   }
 }
 
@@ -1732,6 +1911,22 @@ __global__ __launch_bounds__(256) void k_select_b16(SelectArgs a) {
     default: return hipErrorInvalidValue;                                                        \
   }
 
+#define DSPARK_R_CASES_SMALLB(ZT, WT)                                                            \
+  switch (P.r) {                                                                                 \
+    case 16: hipLaunchKernelGGL((k_verify_smallb<ZT, WT, 16>), G, kThreads, 0, s, a); break;     \
+    case 32: hipLaunchKernelGGL((k_verify_smallb<ZT, WT, 32>), G, kThreads, 0, s, a); break;     \
+    case 64: hipLaunchKernelGGL((k_verify_smallb<ZT, WT, 64>), G, kThreads, 0, s, a); break;     \
+    case 128: hipLaunchKernelGGL((k_verify_smallb<ZT, WT, 128>), G, kThreads, 0, s, a); break;   \
+    case 256: hipLaunchKernelGGL((k_verify_smallb<ZT, WT, 256>), G, kThreads, 0, s, a); break;   \
+    default: return hipErrorInvalidValue;                                                        \
+  }
+#define DSPARK_R_CASES_SMALLB_F32W(ZT)                                                             \
+  switch (P.r) {                                                                                   \
+    case 16: hipLaunchKernelGGL((k_verify_smallb<ZT, float, 16>), G, kThreads, 0, s, a); break;    \
+    case 32: hipLaunchKernelGGL((k_verify_smallb<ZT, float, 32>), G, kThreads, 0, s, a); break;    \
+    case 64: hipLaunchKernelGGL((k_verify_smallb<ZT, float, 64>), G, kThreads, 0, s, a); break;    \
+    default: return hipErrorInvalidValue;                                                          \
+  }
 #define DSPARK_R_CASES_F32W(ZT, MODE)                                                                \
   switch (P.r) {                                                                                     \
     case 16: hipLaunchKernelGGL((k_stream_generic<ZT, float, 16, MODE>), G, kThreads, 0, s, a); break; \
@@ -1742,6 +1937,8 @@ __global__ __launch_bounds__(256) void k_select_b16(SelectArgs a) {
 
 // bf16 factors: the LDS-pipelined kernel (fp32 logits in verify mode would need
 // 160 KB of LDS per two stages and use the generic kernel); fp32 factors: generic.
+// The generic kernel's verify mode at B <= kSmallVerifyB: k_verify_smallb.
+constexpr int kSmallVerifyB = 64;
 template <int MODE>
 static hipError_t launch_stream(const dspark_problem& P, const StreamArgs& a, int G, hipStream_t s) {
   const bool zb = P.logits_dtype == DSPARK_BF16, wb = P.weight_dtype == DSPARK_BF16;
@@ -1758,8 +1955,16 @@ static hipError_t launch_stream(const dspark_problem& P, const StreamArgs& a, in
       DSPARK_R_CASES_VERIFY16
     } else if (zb) {
       DSPARK_R_CASES_BF16(uint16_t, MODE_VERIFY)
+    } else if (P.B <= kSmallVerifyB) {
+      DSPARK_R_CASES_SMALLB(float, uint16_t)
     } else {
       DSPARK_R_CASES_GENERIC(float, uint16_t, MODE_VERIFY)
+    }
+  } else if (MODE == MODE_VERIFY && P.B <= kSmallVerifyB) {
+    if (zb) {
+      DSPARK_R_CASES_SMALLB_F32W(uint16_t)
+    } else {
+      DSPARK_R_CASES_SMALLB_F32W(float)
     }
   } else {
     if (zb) {
