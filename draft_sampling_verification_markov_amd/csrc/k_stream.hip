@@ -1435,8 +1435,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_verify64(StreamArgs a) {
 
     // z: this unit's draft logits on entry, the next unit's requested into the same registers at the end
     auto step = [&](int u, unsigned char* cur, unsigned char* nxt, u32x4_t (&z)[4]) {
-      wait_vmem();          // unit u's tiles and draft logits have landed
-      barrier_lds_only();   // everyone's have; unit u - 1's stage is free
+      // unit u's tiles have landed (the four draft-logit loads requested after
+      // them may still be in flight: they are first read in the epilogue, after
+      // the MFMAs, where the compiler waits for them)
+      wait_vmem_n<4>();
+      barrier_lds_only();   // everyone's tiles have; unit u - 1's stage is free
       // the next unit's requests in two bursts: its target tile now, its Wt
       // tile and draft logits after this unit's MFMA, so the waves do not all
       // block in issue before computing
