@@ -69,47 +69,6 @@ __device__ __forceinline__ void persist_chunk_range(int g, int G, int nchunks, i
   c_end = c_begin + (int)q + (ug < rem ? 1 : 0);
 }
 
-__device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(unsigned* p, unsigned v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// 8-byte words past the L2 (an XCD's L2 is not kept coherent with another's):
-// a 32-bit value in the low half and its tag in the high half, so that one
-// single-copy-atomic load returns the value together with the proof of which
-// position (and launch) wrote it
-__device__ __forceinline__ void st_tagged(unsigned long long* p, uint32_t v, uint32_t tag) {
-  __hip_atomic_store(p, ((unsigned long long)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned long long ld_tagged(const unsigned long long* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Poll N consecutive tagged words of this lane until every tag is `expect`;
-// bounded: past `limit` polls (at once if the flag is already set) the
-// time-out flag is set and the words are returned as they are.  Lanes poll
-// independently; the wave leaves when every lane is done.
-template <int N>
-__device__ __forceinline__ void poll_tagged(const unsigned long long* p, uint32_t expect, unsigned* flag,
-                                            uint32_t limit, uint32_t (&v)[N]) {
-  unsigned spins = ld_agent(flag) ? limit : 0u;
-  for (;;) {
-    bool ok = true;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const unsigned long long w = ld_tagged(p + i);
-      v[i] = (uint32_t)w;
-      ok = ok && (uint32_t)(w >> 32) == expect;
-    }
-    if (ok) break;
-    if (++spins > limit) {
-      st_agent(flag, 1u);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
-
 // Word i (0..3) of a Philox quad without indexing (an indexed pick can become a scratch access).
 __device__ __forceinline__ uint32_t quad_pick(const Words4& q, int i) {
   const uint32_t lo = (i & 1) ? q.w[1] : q.w[0], hi = (i & 1) ? q.w[3] : q.w[2];
