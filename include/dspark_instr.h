@@ -28,8 +28,8 @@ extern "C" {
  *                              device that launches cooperatively; not under
  *                              stream capture, not for the RNN head).
  * dspark_draft takes DSPARK_DRAFT_AUTO: the persistent schedule where it applies
- * and B <= 48 (bf16 logits) or B <= 96 (fp32 logits), else the per-position one
- * (the measured crossovers). */
+ * and B <= 192 (bf16 logits) or B <= 256 (fp32 logits), else the per-position
+ * one (the measured crossovers). */
 enum {
   DSPARK_DRAFT_AUTO = 0,
   DSPARK_DRAFT_PER_POSITION = 1,
